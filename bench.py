@@ -1,0 +1,250 @@
+"""Benchmark of the denoising-step hot path on one MI355X.
+
+One step = one denoising step of the stack workload: 30 MoE FFN layers (256-token canvas,
+d_model 2816, expert ffn 704, 128 experts top-8, W4A16 group 64, Zipf(1.2) routing), each
+as route -> gate/up (GeGLU) -> down -> fixed-order combine, followed by the sampler
+(entropy + gumbel-max over fp32 logits [256, 262144], temperature 1, then the entropy-bound
+acceptance at bound 2.0).  Accepted positions stay frozen; the canvas is reset every 48
+steps.  All inputs are seeded synthetic tensors resident in HBM before timing starts.
+
+value = algorithmic bytes of the step (touched expert weights with their scales and
+zero-points, activations in and out, router logits, the unfrozen logits rows) / time,
+in GB/s; ms_per_step is the latency of one step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=None, help="MoE layers per step (default 30)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "block_diffusion_lm_router_amd", "csrc", "moe_w4a16.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(per_launch_alg_bytes):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, "gate_up_w4a16_stack_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, layer_inputs, logits, sampler_shape):
+    """The oracle, untuned, on a bounded sample of the same workload: one MoE layer over 48
+    tokens (all their routed experts) and the sampler over 24 rows."""
+    from threadpoolctl import threadpool_limits
+    from oracle import moe as omoe, sampler as osamp
+    from block_diffusion_lm_router_amd import workloads
+    threads = min(os.cpu_count() or 1, 16)
+    x, router, w = layer_inputs
+    tokens = np.arange(48)
+    rows = list(range(24))
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        ids, tw = omoe.route_topk(router, shape.top_k)
+        o = omoe.moe_expert_outputs(x, ids, w, tokens=tokens)
+        omoe.combine(o[tokens], tw[tokens])
+        t1 = time.perf_counter()
+        osamp.sample_rows(logits[:24], sampler_shape.temperature, sampler_shape.seed, 0, rows=rows)
+        t2 = time.perf_counter()
+    gu, dn = workloads.expert_bytes(shape)
+    touched = len(np.unique(ids[tokens]))
+    ffn_bytes = touched * (gu + dn) + 48 * shape.d_model * 2 * 2 + 48 * shape.experts * 4
+    samp_bytes = 24 * sampler_shape.vocab * 4
+    secs = t2 - t0
+    return {
+        "value": round((ffn_bytes + samp_bytes) / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"numpy fp64 oracle: one MoE layer of the stack over 48 tokens "
+                   f"({touched} experts touched, {ffn_bytes / 1e6:.1f} MB) in {t1 - t0:.2f} s, "
+                   f"sampler entropy + two-level gumbel draw over 24 of 256 rows "
+                   f"({samp_bytes / 1e6:.1f} MB) in {t2 - t1:.2f} s; "
+                   f"rate = algorithmic bytes / wall time"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_diffusion_lm_router_amd import _binding as bd, workloads
+
+    torch.cuda.set_device(0)
+    shape = workloads.STACK_LAYER
+    n_layers = args.layers or workloads.STACK_LAYERS
+    sshape = workloads.SAMPLER
+    T, d, f, E, k = shape.tokens, shape.d_model, shape.d_ff, shape.experts, shape.top_k
+    P, V = sshape.positions, sshape.vocab
+    gu_bytes, dn_bytes = workloads.expert_bytes(shape)
+
+    log(f"generating {n_layers} layers of packed weights")
+    t0 = time.time()
+    x_np = workloads.make_activations(shape)
+    x = torch.from_numpy(x_np).cuda()
+    layers = []
+    layer0 = None
+    for l in range(n_layers):
+        w_np = workloads.make_weights(shape, l)
+        r_np = workloads.make_router_logits(shape, l)
+        layers.append((bd.MoeWeights.from_numpy(w_np, k), torch.from_numpy(r_np).cuda()))
+        if l == 0:
+            layer0 = (x_np, r_np, w_np)
+        del w_np
+    logits_np = workloads.make_logits(sshape)
+    logits = torch.from_numpy(logits_np).cuda()
+    log(f"inputs resident in HBM ({time.time() - t0:.1f} s)")
+
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    o = torch.empty((T, k, d), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    ws = bd.moe_workspace(T, layers[0][0])
+    # Experts each layer touches, from the device's own routing (for the byte accounting).
+    touched = []
+    for w, router in layers:
+        bd.moe_route_topk(w, router, ids, tw, ws)
+        touched.append(int(torch.unique(ids).numel()))
+    sws = bd.sample_workspace(P, V)
+    frozen = torch.zeros(P, dtype=torch.uint8, device="cuda")
+    canvas = torch.zeros(P, dtype=torch.int32, device="cuda")
+    tok = torch.empty(P, dtype=torch.int32, device="cuda")
+    H = torch.empty(P, dtype=torch.float32, device="cuda")
+    acc = torch.empty(P, dtype=torch.uint8, device="cuda")
+    total = args.warmup + args.steps
+    n_acc = torch.zeros(total, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    gu_events = []
+
+    def step(i, timed):
+        if i % workloads.STACK_STEPS == 0:
+            frozen.zero_()
+        for w, router in layers:
+            bd.moe_route_topk(w, router, ids, tw, ws)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            bd.moe_w4a16_gate_up(w, x, ws)
+            if timed:
+                e1.record(stream)
+                gu_events.append((e0, e1))
+            bd.moe_w4a16_down(w, T, o, ws)
+            bd.moe_combine_fixed_order(o, tw, y)
+        bd.diffusion_sample_step(logits, sshape.temperature, sshape.bound, sshape.seed,
+                                 i % workloads.STACK_STEPS, frozen, canvas, tok, H, acc,
+                                 n_acc[i:i + 1], sws)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"warmup done; timing {args.steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.warmup, total):
+        step(i, True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # Unfrozen rows seen by each timed step's sampler, from the device's acceptance counts.
+    counts = n_acc.cpu().numpy()
+    unfrozen = []
+    fr = 0
+    for i in range(total):
+        if i % workloads.STACK_STEPS == 0:
+            fr = 0
+        if i >= args.warmup:
+            unfrozen.append(P - fr)
+        fr += int(counts[i])
+    sampler_bytes = np.array(unfrozen, dtype=np.float64) * V * 4 + P * 4 * 4
+    ffn_bytes = sum(t * (gu_bytes + dn_bytes) for t in touched) + n_layers * (
+        2 * T * d * 2 + T * E * 4 + 2 * T * k * 4)
+    step_bytes = ffn_bytes + float(sampler_bytes.mean())
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    gu_ms = np.array([a.elapsed_time(b) for a, b in gu_events])
+    gu_alg = np.array([t * gu_bytes + T * d * 2 + T * k * f * 2 for t in touched] * args.steps,
+                      dtype=np.float64)
+    gu_gbs = gu_alg.sum() / (gu_ms.sum() * 1e-3) / 1e9
+    traffic = measured_traffic(float(gu_alg.mean()))
+
+    result = {
+        "metric": "denoising-step MoE+sampler latency (ms) and achieved HBM GB/s vs peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma/f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"stack: {n_layers} MoE layers (canvas {T}, d_model {d}, expert ffn {f}, "
+                         f"{E} experts top-{k}, W4A16 asym g64, Zipf(1.2) routing) + sampler "
+                         f"fp32 [{P}, {V}] T=1 bound 2.0, 48-step frozen canvas"),
+            "steps_per_block": workloads.STACK_STEPS,
+            "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+            "step_algorithmic_bytes": int(step_bytes),
+        },
+        "roofline": {
+            "kernel": "w4a16_gemm_kernel<gate_up> (moe_w4a16_gate_up)",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(float(gu_ms.mean()) * 1e3, 2),
+            "alg_bytes_per_launch": int(gu_alg.mean()),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(shape, layer0, logits_np, sshape)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

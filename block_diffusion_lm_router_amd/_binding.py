@@ -1,0 +1,242 @@
+"""ctypes binding of libbdstep (see include/bdstep.h).  Argument marshalling only.
+
+Every function takes torch tensors that live on the GPU, checks dtype, shape and
+contiguity, and passes raw device pointers plus the current torch stream to the C
+ABI.  No step of the hot path runs here: if the shared library is missing the
+import of any entry point raises, there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbdstep.so")
+
+BD_SAMPLE_CHUNK = 1024
+
+_STATUS = {0: "ok", 1: "BD_ERR_NULL", 2: "BD_ERR_SHAPE", 3: "BD_ERR_ALIGN",
+           4: "BD_ERR_WORKSPACE", 5: "BD_ERR_UNSUPPORTED", 6: "BD_ERR_HIP"}
+
+# Every symbol the header declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+_U64 = ctypes.c_uint64
+_U32 = ctypes.c_uint32
+
+
+class MoeWeightsC(ctypes.Structure):
+    """Mirror of bd_moe_weights."""
+    _fields_ = [
+        ("num_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("d_model", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("gate_up_q", _P),
+        ("gate_up_scale", _P),
+        ("gate_up_zero", _P),
+        ("down_q", _P),
+        ("down_scale", _P),
+        ("down_zero", _P),
+    ]
+
+
+_W = ctypes.POINTER(MoeWeightsC)
+
+SIGNATURES = {
+    "bd_abi_version": (_I, []),
+    "bd_status_string": (ctypes.c_char_p, [_I]),
+    "bd_moe_workspace_size": (_SZ, [_I, _W]),
+    "moe_route_topk": (_I, [_W, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_w4a16_gate_up": (_I, [_W, _I, _P, _P, _SZ, _P]),
+    "moe_w4a16_down": (_I, [_W, _I, _P, _P, _SZ, _P]),
+    "moe_w4a16_ffn": (_I, [_W, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_combine_fixed_order": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "bd_sample_workspace_size": (_SZ, [_I, _I]),
+    "diffusion_sample_entropy": (_I, [_P, _I, _I, _F, _U64, _U32, _P, _P, _P, _P, _SZ, _P]),
+    "diffusion_accept_entropy_bound": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
+    "diffusion_sample_step": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P, _P, _P,
+                                   _SZ, _P]),
+    "bd_hbm_copy": (_I, [_P, _P, _SZ, _P]),
+}
+
+_lib = None
+
+
+class BdError(RuntimeError):
+    pass
+
+
+def load():
+    """Load libbdstep.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m block_diffusion_lm_router_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = load().bd_status_string(status).decode()
+        raise BdError(f"{what}: {_STATUS.get(status, status)} ({msg})")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class MoeWeights:
+    """Device tensors of one layer's packed expert weights plus the C struct over them."""
+
+    KEYS = ("gate_up_q", "gate_up_scale", "gate_up_zero", "down_q", "down_scale", "down_zero")
+
+    def __init__(self, tensors, top_k, group_size=64):
+        self.tensors = tensors
+        gq = tensors["gate_up_q"]
+        E, two_f, half_d = gq.shape
+        self.num_experts, self.d_ff, self.d_model = E, two_f // 2, half_d * 2
+        self.top_k, self.group_size = top_k, group_size
+        dtypes = {"gate_up_q": torch.uint8, "down_q": torch.uint8}
+        ptrs = {k: _ptr(tensors[k], dtypes.get(k, torch.float16), k) for k in self.KEYS}
+        self.c = MoeWeightsC(E, top_k, self.d_model, self.d_ff, group_size,
+                             *[ptrs[k] for k in self.KEYS])
+
+    @classmethod
+    def from_numpy(cls, arrays, top_k, device="cuda", group_size=64):
+        t = {k: torch.from_numpy(arrays[k]).to(device) for k in cls.KEYS}
+        return cls(t, top_k, group_size)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def abi_version():
+    return load().bd_abi_version()
+
+
+def moe_workspace_size(T, w: MoeWeights):
+    n = load().bd_moe_workspace_size(T, w.ref())
+    if n == 0:
+        raise BdError("bd_moe_workspace_size: invalid shape")
+    return n
+
+
+def moe_workspace(T, w: MoeWeights, device="cuda"):
+    return torch.zeros(moe_workspace_size(T, w), dtype=torch.uint8, device=device)
+
+
+def moe_route_topk(w, router_logits, topk_ids, topk_weights, workspace):
+    T = router_logits.shape[0]
+    _check(load().moe_route_topk(w.ref(), T, _ptr(router_logits, torch.float32, "router_logits"),
+                                 _ptr(topk_ids, torch.int32, "topk_ids"),
+                                 _ptr(topk_weights, torch.float32, "topk_weights"),
+                                 _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                 _stream()), "moe_route_topk")
+
+
+def moe_w4a16_gate_up(w, x, workspace):
+    _check(load().moe_w4a16_gate_up(w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
+                                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                    _stream()), "moe_w4a16_gate_up")
+
+
+def moe_w4a16_down(w, T, expert_out, workspace):
+    _check(load().moe_w4a16_down(w.ref(), T, _ptr(expert_out, torch.float32, "expert_out"),
+                                 _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                 _stream()), "moe_w4a16_down")
+
+
+def moe_w4a16_ffn(w, x, router_logits, topk_ids, topk_weights, expert_out, workspace):
+    _check(load().moe_w4a16_ffn(w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
+                                _ptr(router_logits, torch.float32, "router_logits"),
+                                _ptr(topk_ids, torch.int32, "topk_ids"),
+                                _ptr(topk_weights, torch.float32, "topk_weights"),
+                                _ptr(expert_out, torch.float32, "expert_out"),
+                                _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                _stream()), "moe_w4a16_ffn")
+
+
+def moe_combine_fixed_order(expert_out, topk_weights, y):
+    T, k, d = expert_out.shape
+    _check(load().moe_combine_fixed_order(_ptr(expert_out, torch.float32, "expert_out"),
+                                          _ptr(topk_weights, torch.float32, "topk_weights"),
+                                          T, k, d, _ptr(y, torch.float16, "y"), _stream()),
+           "moe_combine_fixed_order")
+
+
+def sample_workspace_size(P, V):
+    n = load().bd_sample_workspace_size(P, V)
+    if n == 0:
+        raise BdError("bd_sample_workspace_size: invalid shape")
+    return n
+
+
+def sample_workspace(P, V, device="cuda"):
+    return torch.zeros(sample_workspace_size(P, V), dtype=torch.uint8, device=device)
+
+
+def diffusion_sample_entropy(logits, temperature, seed, step, frozen, tokens_out, entropy_out,
+                             workspace):
+    P, V = logits.shape
+    _check(load().diffusion_sample_entropy(
+        _ptr(logits, torch.float32, "logits"), P, V, float(temperature), int(seed), int(step),
+        _ptr(frozen, torch.uint8, "frozen"), _ptr(tokens_out, torch.int32, "tokens_out"),
+        _ptr(entropy_out, torch.float32, "entropy_out"), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream()), "diffusion_sample_entropy")
+
+
+def diffusion_accept_entropy_bound(entropy, tokens, bound, frozen, canvas, accept_out,
+                                   num_accepted):
+    P = entropy.shape[0]
+    _check(load().diffusion_accept_entropy_bound(
+        _ptr(entropy, torch.float32, "entropy"), _ptr(tokens, torch.int32, "tokens"), P,
+        float(bound), _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
+        _ptr(accept_out, torch.uint8, "accept_out"),
+        _ptr(num_accepted, torch.int32, "num_accepted"), _stream()),
+        "diffusion_accept_entropy_bound")
+
+
+def diffusion_sample_step(logits, temperature, entropy_bound, seed, step, frozen, canvas,
+                          tokens_out, entropy_out, accept_out, num_accepted, workspace):
+    P, V = logits.shape
+    _check(load().diffusion_sample_step(
+        _ptr(logits, torch.float32, "logits"), P, V, float(temperature), float(entropy_bound),
+        int(seed), int(step), _ptr(frozen, torch.uint8, "frozen"),
+        _ptr(canvas, torch.int32, "canvas"), _ptr(tokens_out, torch.int32, "tokens_out"),
+        _ptr(entropy_out, torch.float32, "entropy_out"),
+        _ptr(accept_out, torch.uint8, "accept_out"),
+        _ptr(num_accepted, torch.int32, "num_accepted"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream()),
+        "diffusion_sample_step")
+
+
+def hbm_copy(src, dst):
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    _check(load().bd_hbm_copy(_ptr(src, None, "src"), _ptr(dst, None, "dst"), n, _stream()),
+           "bd_hbm_copy")

@@ -1,0 +1,232 @@
+// C ABI of libbdstep: host-side validation, workspace carving and kernel launches.
+// Every check runs before the first launch, so a failing call enqueues nothing.
+
+#include <math.h>
+
+#include "../../include/bdstep.h"
+#include "bd_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int to_status(hipError_t err) { return err == hipSuccess ? BD_OK : BD_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_moe_shape(const bd_moe_weights* w, int T) {
+  if (w == nullptr) return BD_ERR_NULL;
+  if (T < 1 || T > BD_MAX_TOKENS) return BD_ERR_SHAPE;
+  if (w->num_experts < 1 || w->num_experts > BD_MAX_EXPERTS) return BD_ERR_SHAPE;
+  if (w->top_k < 1 || w->top_k > BD_MAX_TOPK || w->top_k > w->num_experts) return BD_ERR_SHAPE;
+  if (w->d_model < 1 || w->d_ff < 1) return BD_ERR_SHAPE;
+  if (w->group_size != 64) return BD_ERR_UNSUPPORTED;
+  if (w->d_model % 128 != 0 || w->d_ff % 64 != 0) return BD_ERR_UNSUPPORTED;
+  if ((int64_t)T * w->top_k > (int64_t)BD_MAX_TOKENS * BD_MAX_TOPK) return BD_ERR_SHAPE;
+  return BD_OK;
+}
+
+int check_workspace(const void* ws, size_t have, size_t need) {
+  if (ws == nullptr) return BD_ERR_NULL;
+  if (!aligned16(ws)) return BD_ERR_ALIGN;
+  if (have < need) return BD_ERR_WORKSPACE;
+  return BD_OK;
+}
+
+int check_gate_up_weights(const bd_moe_weights* w) {
+  if (!w->gate_up_q || !w->gate_up_scale || !w->gate_up_zero) return BD_ERR_NULL;
+  if (!aligned16(w->gate_up_q) || !aligned16(w->gate_up_scale) || !aligned16(w->gate_up_zero))
+    return BD_ERR_ALIGN;
+  return BD_OK;
+}
+
+int check_down_weights(const bd_moe_weights* w) {
+  if (!w->down_q || !w->down_scale || !w->down_zero) return BD_ERR_NULL;
+  if (!aligned16(w->down_q) || !aligned16(w->down_scale) || !aligned16(w->down_zero))
+    return BD_ERR_ALIGN;
+  return BD_OK;
+}
+
+bd::W4A16Matrix gate_up_of(const bd_moe_weights* w) {
+  return bd::W4A16Matrix{w->gate_up_q, w->gate_up_scale, w->gate_up_zero};
+}
+bd::W4A16Matrix down_of(const bd_moe_weights* w) {
+  return bd::W4A16Matrix{w->down_q, w->down_scale, w->down_zero};
+}
+
+int check_sample_shape(int P, int V, float temperature) {
+  if (P < 1 || P > BD_MAX_POSITIONS) return BD_ERR_SHAPE;
+  if (V < 1 || V > BD_MAX_VOCAB) return BD_ERR_SHAPE;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return BD_ERR_SHAPE;
+  return BD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bd_abi_version(void) { return BD_ABI_VERSION; }
+
+const char* bd_status_string(int status) {
+  switch (status) {
+    case BD_OK: return "ok";
+    case BD_ERR_NULL: return "a required pointer is NULL";
+    case BD_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case BD_ERR_ALIGN: return "a pointer is not aligned as the ABI requires";
+    case BD_ERR_WORKSPACE: return "workspace missing or smaller than required";
+    case BD_ERR_UNSUPPORTED: return "shape or format not supported by this build";
+    case BD_ERR_HIP: return "a HIP launch or runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+size_t bd_moe_workspace_size(int T, const bd_moe_weights* w) {
+  if (check_moe_shape(w, T) != BD_OK) return 0;
+  return bd::moe_workspace_bytes(T, w->num_experts, w->top_k, w->d_ff);
+}
+
+int moe_route_topk(const bd_moe_weights* w, int T, const float* router_logits, int32_t* topk_ids,
+                   float* topk_weights, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_moe_shape(w, T);
+  if (st != BD_OK) return st;
+  if (!router_logits || !topk_ids || !topk_weights) return BD_ERR_NULL;
+  if (!aligned4(router_logits) || !aligned4(topk_ids) || !aligned4(topk_weights))
+    return BD_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, bd_moe_workspace_size(T, w));
+  if (st != BD_OK) return st;
+  const bd::MoeWorkspace ws =
+      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_ff);
+  return to_status(bd::launch_route(router_logits, T, w->num_experts, w->top_k, topk_ids,
+                                    topk_weights, ws, as_stream(stream)));
+}
+
+int moe_w4a16_gate_up(const bd_moe_weights* w, int T, const uint16_t* x, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_moe_shape(w, T);
+  if (st != BD_OK) return st;
+  if ((st = check_gate_up_weights(w)) != BD_OK) return st;
+  if (!x) return BD_ERR_NULL;
+  if (!aligned16(x)) return BD_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, bd_moe_workspace_size(T, w));
+  if (st != BD_OK) return st;
+  const bd::MoeWorkspace ws =
+      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_ff);
+  return to_status(bd::launch_gate_up(gate_up_of(w), w->num_experts, w->d_model, w->d_ff,
+                                      w->top_k, T, x, ws, as_stream(stream)));
+}
+
+int moe_w4a16_down(const bd_moe_weights* w, int T, float* expert_out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_moe_shape(w, T);
+  if (st != BD_OK) return st;
+  if ((st = check_down_weights(w)) != BD_OK) return st;
+  if (!expert_out) return BD_ERR_NULL;
+  if (!aligned16(expert_out)) return BD_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, bd_moe_workspace_size(T, w));
+  if (st != BD_OK) return st;
+  const bd::MoeWorkspace ws =
+      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_ff);
+  return to_status(bd::launch_down(down_of(w), w->num_experts, w->d_model, w->d_ff, w->top_k, T,
+                                   expert_out, ws, as_stream(stream)));
+}
+
+int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x, const float* router_logits,
+                  int32_t* topk_ids, float* topk_weights, float* expert_out, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = check_moe_shape(w, T);
+  if (st != BD_OK) return st;
+  if ((st = check_gate_up_weights(w)) != BD_OK) return st;
+  if ((st = check_down_weights(w)) != BD_OK) return st;
+  if (!x || !router_logits || !topk_ids || !topk_weights || !expert_out) return BD_ERR_NULL;
+  if (!aligned16(x) || !aligned4(router_logits) || !aligned4(topk_ids) ||
+      !aligned4(topk_weights) || !aligned16(expert_out))
+    return BD_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, bd_moe_workspace_size(T, w));
+  if (st != BD_OK) return st;
+  const bd::MoeWorkspace ws =
+      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_ff);
+  hipStream_t s = as_stream(stream);
+  hipError_t err = bd::launch_route(router_logits, T, w->num_experts, w->top_k, topk_ids,
+                                    topk_weights, ws, s);
+  if (err == hipSuccess)
+    err = bd::launch_gate_up(gate_up_of(w), w->num_experts, w->d_model, w->d_ff, w->top_k, T, x,
+                             ws, s);
+  if (err == hipSuccess)
+    err = bd::launch_down(down_of(w), w->num_experts, w->d_model, w->d_ff, w->top_k, T,
+                          expert_out, ws, s);
+  return to_status(err);
+}
+
+int moe_combine_fixed_order(const float* expert_out, const float* topk_weights, int T, int k,
+                            int d, uint16_t* y, void* stream) {
+  if (!expert_out || !topk_weights || !y) return BD_ERR_NULL;
+  if (T < 1 || T > BD_MAX_TOKENS || k < 1 || k > BD_MAX_TOPK || d < 4 || d % 4 != 0)
+    return BD_ERR_SHAPE;
+  if (!aligned16(expert_out) || !aligned4(topk_weights) || !aligned16(y)) return BD_ERR_ALIGN;
+  return to_status(bd::launch_combine(expert_out, topk_weights, T, k, d, y, as_stream(stream)));
+}
+
+size_t bd_sample_workspace_size(int P, int V) {
+  if (check_sample_shape(P, V, 0.f) != BD_OK) return 0;
+  return bd::sample_workspace_bytes(P, V);
+}
+
+int diffusion_sample_entropy(const float* logits, int P, int V, float temperature, uint64_t seed,
+                             uint32_t step, const uint8_t* frozen, int32_t* tokens_out,
+                             float* entropy_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  int st = check_sample_shape(P, V, temperature);
+  if (st != BD_OK) return st;
+  if (!logits || !tokens_out || !entropy_out) return BD_ERR_NULL;
+  if (!aligned16(logits) || !aligned4(tokens_out) || !aligned4(entropy_out)) return BD_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, bd::sample_workspace_bytes(P, V));
+  if (st != BD_OK) return st;
+  return to_status(bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
+                                             tokens_out, entropy_out, workspace,
+                                             as_stream(stream)));
+}
+
+int diffusion_accept_entropy_bound(const float* entropy, const int32_t* tokens, int P, float bound,
+                                   uint8_t* frozen, int32_t* canvas, uint8_t* accept_out,
+                                   int32_t* num_accepted, void* stream) {
+  if (P < 1 || P > BD_MAX_POSITIONS || !isfinite(bound)) return BD_ERR_SHAPE;
+  if (!entropy || !tokens || !accept_out || !num_accepted) return BD_ERR_NULL;
+  if (!aligned4(entropy) || !aligned4(tokens) || !aligned4(num_accepted) ||
+      (canvas && !aligned4(canvas)))
+    return BD_ERR_ALIGN;
+  return to_status(bd::launch_accept(entropy, tokens, P, bound, frozen, canvas, accept_out,
+                                     num_accepted, as_stream(stream)));
+}
+
+int diffusion_sample_step(const float* logits, int P, int V, float temperature,
+                          float entropy_bound, uint64_t seed, uint32_t step, uint8_t* frozen,
+                          int32_t* canvas, int32_t* tokens_out, float* entropy_out,
+                          uint8_t* accept_out, int32_t* num_accepted, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = check_sample_shape(P, V, temperature);
+  if (st != BD_OK) return st;
+  if (!isfinite(entropy_bound)) return BD_ERR_SHAPE;
+  if (!logits || !tokens_out || !entropy_out || !accept_out || !num_accepted) return BD_ERR_NULL;
+  if (!aligned16(logits) || !aligned4(tokens_out) || !aligned4(entropy_out) ||
+      !aligned4(num_accepted) || (canvas && !aligned4(canvas)))
+    return BD_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, bd::sample_workspace_bytes(P, V));
+  if (st != BD_OK) return st;
+  hipStream_t s = as_stream(stream);
+  hipError_t err = bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
+                                             tokens_out, entropy_out, workspace, s);
+  if (err == hipSuccess)
+    err = bd::launch_accept(entropy_out, tokens_out, P, entropy_bound, frozen, canvas, accept_out,
+                            num_accepted, s);
+  return to_status(err);
+}
+
+int bd_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return BD_ERR_NULL;
+  if (bytes % 16 != 0) return BD_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return BD_ERR_ALIGN;
+  return to_status(bd::launch_copy(src, dst, bytes, as_stream(stream)));
+}
+
+}  // extern "C"

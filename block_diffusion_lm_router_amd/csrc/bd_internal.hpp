@@ -1,0 +1,69 @@
+// Host/device declarations shared between the kernels' translation units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bd {
+
+inline size_t align_up(size_t n, size_t a = 256) { return (n + a - 1) / a * a; }
+
+// Partial entropy / argmax state of one V-split of one row (32 bytes).
+struct PartState {
+  float m;       // reference maximum (-inf: empty)
+  float n;       // entries equal to m
+  float s;       // sum of exp(x - m) over the other entries
+  float t;       // sum of exp(x - m) (x - m)
+  float best_v;  // temperature-0 argmax value
+  int best_i;    // and its lowest index
+  int nan;       // a NaN was seen where no finite entry could carry it
+  int pad;
+};
+
+// ---------------------------------------------------------------- MoE
+constexpr int kItemTokens = 32;  // tokens per work item of the grouped GEMMs
+
+struct MoeWorkspace {
+  int32_t* offsets;  // [E + 1] bucket starts
+  int32_t* items;    // [0] = count, then (expert, first bucket position, tokens) triples
+  int32_t* perm;     // [T * k] assignment index t*k + j at each bucket position
+  uint16_t* h;       // [T * k][d_ff] fp16 GeGLU activations, bucket order
+  int max_items;
+};
+
+int moe_max_items(int T, int E, int k);
+size_t moe_workspace_bytes(int T, int E, int k, int d_ff);
+MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_ff);
+
+hipError_t launch_route(const float* router_logits, int T, int E, int k, int32_t* topk_ids,
+                        float* topk_weights, const MoeWorkspace& ws, hipStream_t stream);
+
+struct W4A16Matrix {
+  const uint8_t* q;
+  const uint16_t* scale;
+  const uint16_t* zero;
+};
+
+hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, int top_k, int T,
+                          const uint16_t* x, const MoeWorkspace& ws, hipStream_t stream);
+hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int top_k, int T,
+                       float* expert_out, const MoeWorkspace& ws, hipStream_t stream);
+hipError_t launch_combine(const float* expert_out, const float* topk_weights, int T, int k, int d,
+                          uint16_t* y, hipStream_t stream);
+
+// ---------------------------------------------------------------- sampler
+int sample_split_count(int P, int V);
+size_t sample_workspace_bytes(int P, int V);
+hipError_t launch_sample_entropy(const float* logits, int P, int V, float temperature,
+                                 uint64_t seed, uint32_t step, const uint8_t* frozen,
+                                 int32_t* tokens_out, float* entropy_out, void* workspace,
+                                 hipStream_t stream);
+hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, float bound,
+                         uint8_t* frozen, int32_t* canvas, uint8_t* accept_out,
+                         int32_t* num_accepted, hipStream_t stream);
+
+// ---------------------------------------------------------------- measurement
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+}  // namespace bd

@@ -1,0 +1,491 @@
+// Per-step sampler kernels: streaming entropy + token pass, per-row finish, and the
+// entropy-bound acceptance (sort + scan).
+//
+// Sources: axe-diffusion-ksl-xe model card, "the kernels we built" (entropy once per
+// step in one streaming pass over the fp32 logits; gumbel-max instead of softmax +
+// multinomial); DiffusionGemma block-diffusion page, "Samplers" (entropy-bound rule).
+//
+// Streaming pass.  The logits are read exactly once.  A wave takes one chunk of 1024
+// consecutive entries at a time (16 per lane, four coalesced 16-byte loads), finds the
+// chunk maximum m_c with DPP, and folds exp(x - m_c) into per-lane running sums kept
+// against a wave-uniform running maximum:
+//     n  = count of entries equal to the running maximum,
+//     s  = sum of exp(x - m) over the other entries,
+//     t  = sum of exp(x - m) (x - m).
+// With Z = n + s the entropy is H = ln Z - t / Z = log1p((n - 1) + s) - t / Z; keeping
+// the maximal entries out of s keeps H accurate when it is near zero.  The temperature-0
+// argmax needs only the chunk maxima.  For T > 0 the pass also stores each chunk's
+// log-mass L_c = ln sum exp(x / T), the input of the level-1 gumbel-max.  Partial states
+// of the V-splits of a row are merged in split order by the finish kernel, which also
+// draws the level-1 and level-2 gumbel noise (Philox, fp64) and re-reads the one winning
+// chunk (1024 entries) of the row.
+
+#include "bd_device.hpp"
+#include "bd_internal.hpp"
+
+namespace bd {
+
+namespace {
+
+constexpr int kChunk = 1024;
+constexpr int kStreamThreads = 256;
+constexpr int kStreamWaves = kStreamThreads / kWave;
+
+// Loads chunk c of a row: entry e(j, q) = c*1024 + (j*64 + lane)*4 + q lands in x[4j + q].
+// Entries past V read as -inf (they carry no probability mass).
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int V, int c, bool vec,
+                                           float (&x)[16]) {
+  const int lane = lane_id();
+  const int base = c * kChunk;
+  if (vec) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = base + (j * kWave + lane) * 4;
+      if (idx < V) {
+        const float4_t v = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(row + idx));
+        x[4 * j + 0] = v[0];
+        x[4 * j + 1] = v[1];
+        x[4 * j + 2] = v[2];
+        x[4 * j + 3] = v[3];
+      } else {
+        x[4 * j + 0] = x[4 * j + 1] = x[4 * j + 2] = x[4 * j + 3] = -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = base + ((i >> 2) * kWave + lane) * 4 + (i & 3);
+      x[i] = idx < V ? row[idx] : -INFINITY;
+    }
+  }
+}
+
+struct LaneState {
+  float m;  // wave-uniform running maximum
+  float n, s, t;
+  float best_v;  // temperature-0 argmax (wave-uniform)
+  int best_i;
+  bool nan;      // NaN seen in a chunk with no finite entry (wave-uniform)
+};
+
+// MODE 0: temperature 0 (argmax); 1: temperature 1; 2: any other temperature.
+template <int MODE>
+__device__ __forceinline__ void process_chunk(const float (&x)[16], int c, float invT,
+                                              LaneState& st, float* __restrict__ lmass_row) {
+  const int lane = lane_id();
+  float lm = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) lm = fmaxf(lm, x[i]);
+  const float mc = wave_max(lm);
+  if (mc == -INFINITY) {  // no finite entry: only NaN can hide here
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bad |= (x[i] != x[i]);
+    if (wave_any(bad)) st.nan = true;
+    if (MODE != 0 && lane == 0) lmass_row[c] = -INFINITY;
+    return;
+  }
+  float nc = 0.f, sc = 0.f, tc = 0.f, zt = 0.f;
+  const float scaleT = kLog2e * invT;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float d = x[i] - mc;
+    const float e = __builtin_amdgcn_exp2f(d * kLog2e);
+    const bool off_max = d != 0.f;  // true for NaN as well, which then poisons s
+    sc += off_max ? e : 0.f;
+    nc += off_max ? 0.f : 1.f;
+    tc = fmaf(e, fmaxf(d, -200.f), tc);
+    if (MODE == 2) zt += __builtin_amdgcn_exp2f(d * scaleT);
+  }
+  // Fold the chunk into the running per-lane state (branches are wave-uniform).
+  if (mc > st.m) {
+    if (st.m == -INFINITY) {
+      st.n = nc;
+      st.s = sc;
+      st.t = tc;
+    } else {
+      const float delta = st.m - mc;
+      const float r = __builtin_amdgcn_exp2f(delta * kLog2e);
+      st.t = fmaf(r, fmaf(delta, st.n + st.s, st.t), tc);
+      st.s = fmaf(r, st.s + st.n, sc);
+      st.n = nc;
+    }
+    st.m = mc;
+  } else if (mc == st.m) {
+    st.n += nc;
+    st.s += sc;
+    st.t += tc;
+  } else {
+    const float delta = mc - st.m;
+    const float r = __builtin_amdgcn_exp2f(delta * kLog2e);
+    const float zc = nc + sc;
+    st.t = fmaf(r, fmaf(delta, zc, tc), st.t);
+    st.s = fmaf(r, zc, st.s);
+  }
+  if (MODE == 0) {
+    if (mc > st.best_v) {
+      const int base = c * kChunk;
+      int idx = 0x7fffffff;
+#pragma unroll
+      for (int i = 15; i >= 0; --i)
+        if (x[i] == mc) idx = base + ((i >> 2) * kWave + lane) * 4 + (i & 3);
+      st.best_i = wave_min_i32(idx);
+      st.best_v = mc;
+    }
+  } else {
+    const float z = wave_sum(MODE == 1 ? nc + sc : zt);
+    const float L = (MODE == 1 ? mc : mc * invT) + __builtin_amdgcn_logf(z) * kLn2;
+    if (lane == 0) lmass_row[c] = L;
+  }
+}
+
+// Merge entropy state b into a (a's maximum is the reference when larger).
+__device__ __forceinline__ void merge_state(PartState& a, const PartState& b) {
+  a.nan |= b.nan;
+  if (b.best_v > a.best_v || (b.best_v == a.best_v && b.best_i < a.best_i)) {
+    a.best_v = b.best_v;
+    a.best_i = b.best_i;
+  }
+  if (b.m == -INFINITY) return;
+  if (a.m == -INFINITY) {
+    a.m = b.m;
+    a.n = b.n;
+    a.s = b.s;
+    a.t = b.t;
+    return;
+  }
+  if (b.m > a.m) {
+    const float delta = a.m - b.m;
+    const float r = __builtin_amdgcn_exp2f(delta * kLog2e);
+    a.t = fmaf(r, fmaf(delta, a.n + a.s, a.t), b.t);
+    a.s = fmaf(r, a.s + a.n, b.s);
+    a.n = b.n;
+    a.m = b.m;
+  } else if (b.m == a.m) {
+    a.n += b.n;
+    a.s += b.s;
+    a.t += b.t;
+  } else {
+    const float delta = b.m - a.m;
+    const float r = __builtin_amdgcn_exp2f(delta * kLog2e);
+    const float zb = b.n + b.s;
+    a.t = fmaf(r, fmaf(delta, zb, b.t), a.t);
+    a.s = fmaf(r, zb, a.s);
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
+    const float* __restrict__ logits, int V, int nC, int S, float invT,
+    const uint8_t* __restrict__ frozen, PartState* __restrict__ part, float* __restrict__ lmass) {
+  const int p = blockIdx.y;
+  const int s = blockIdx.x;
+  if (frozen != nullptr && frozen[p]) return;
+  const int wave = threadIdx.x / kWave;
+  const int c_begin = (int)((int64_t)s * nC / S);
+  const int c_end = (int)((int64_t)(s + 1) * nC / S);
+  const float* __restrict__ row = logits + (size_t)p * V;
+  float* __restrict__ lmass_row = lmass + (size_t)p * nC;
+  const bool vec = (V & 3) == 0;
+
+  LaneState st;
+  st.m = -INFINITY;
+  st.n = st.s = st.t = 0.f;
+  st.best_v = -INFINITY;
+  st.best_i = 0x7fffffff;
+  st.nan = false;
+
+  float xa[16], xb[16];
+  int c = c_begin + wave;
+  if (c < c_end) load_chunk(row, V, c, vec, xa);
+  while (c < c_end) {
+    const int c2 = c + kStreamWaves;
+    if (c2 < c_end) load_chunk(row, V, c2, vec, xb);
+    process_chunk<MODE>(xa, c, invT, st, lmass_row);
+    if (c2 >= c_end) break;
+    const int c3 = c2 + kStreamWaves;
+    if (c3 < c_end) load_chunk(row, V, c3, vec, xa);
+    process_chunk<MODE>(xb, c2, invT, st, lmass_row);
+    c = c3;
+  }
+
+  // Lanes share the reference maximum: the wave state is a plain sum.
+  PartState ws;
+  ws.m = st.m;
+  ws.n = wave_sum(st.n);
+  ws.s = wave_sum(st.s);
+  ws.t = wave_sum(st.t);
+  ws.best_v = st.best_v;
+  ws.best_i = st.best_i;
+  ws.nan = st.nan ? 1 : 0;
+
+  __shared__ PartState wstate[kStreamWaves];
+  if (lane_id() == 0) wstate[wave] = ws;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    PartState acc = wstate[0];
+    for (int w = 1; w < kStreamWaves; ++w) merge_state(acc, wstate[w]);
+    part[(size_t)p * S + s] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- finish (one block per row)
+
+constexpr int kFinishThreads = 256;
+
+__device__ __forceinline__ bool better_key(double ka, int ia, double kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+__device__ void block_argmax(double& key, int& idx, double* skey, int* sidx) {
+  const int tid = threadIdx.x;
+  skey[tid] = key;
+  sidx[tid] = idx;
+  __syncthreads();
+  for (int off = kFinishThreads / 2; off > 0; off >>= 1) {
+    if (tid < off && better_key(skey[tid + off], sidx[tid + off], skey[tid], sidx[tid])) {
+      skey[tid] = skey[tid + off];
+      sidx[tid] = sidx[tid + off];
+    }
+    __syncthreads();
+  }
+  key = skey[0];
+  idx = sidx[0];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
+    const float* __restrict__ logits, int V, int nC, int S, float temperature, uint32_t k0,
+    uint32_t k1, uint32_t step, const uint8_t* __restrict__ frozen,
+    const PartState* __restrict__ part, const float* __restrict__ lmass,
+    int32_t* __restrict__ tokens_out, float* __restrict__ entropy_out) {
+  const int p = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (frozen != nullptr && frozen[p]) {
+    if (tid == 0) {
+      tokens_out[p] = -1;
+      entropy_out[p] = INFINITY;
+    }
+    return;
+  }
+  __shared__ float sH;
+  __shared__ int sValid, sArg;
+  __shared__ double skey[kFinishThreads];
+  __shared__ int sidx[kFinishThreads];
+  if (tid == 0) {
+    PartState acc = part[(size_t)p * S];
+    for (int s = 1; s < S; ++s) merge_state(acc, part[(size_t)p * S + s]);
+    float H = NAN;
+    bool valid = !acc.nan && acc.m != -INFINITY;
+    if (valid) {
+      const float Z = acc.n + acc.s;
+      H = log1pf((acc.n - 1.f) + acc.s) - acc.t / Z;
+      valid = !(H != H);
+    }
+    sH = valid ? H : NAN;
+    sValid = valid ? 1 : 0;
+    sArg = acc.best_i;
+  }
+  __syncthreads();
+  if (!sValid) {
+    if (tid == 0) {
+      tokens_out[p] = -1;
+      entropy_out[p] = NAN;
+    }
+    return;
+  }
+  if (temperature == 0.f) {
+    if (tid == 0) {
+      tokens_out[p] = sArg;
+      entropy_out[p] = sH;
+    }
+    return;
+  }
+  // Level 1: chunk keys K_c = L_c + G_c, G_c from counter (c, p, step, 1) word 0.
+  double best = -INFINITY;
+  int bestc = 0x7fffffff;
+  for (int c = tid; c < nC; c += kFinishThreads) {
+    const float L = lmass[(size_t)p * nC + c];
+    if (L == -INFINITY) continue;
+    const Philox4 r = philox4x32_10((uint32_t)c, (uint32_t)p, step, 1u, k0, k1);
+    const double key = (double)L + gumbel_from_word(r.w[0]);
+    if (better_key(key, c, best, bestc)) {
+      best = key;
+      bestc = c;
+    }
+  }
+  block_argmax(best, bestc, skey, sidx);
+  // Level 2: inside chunk bestc, maximise x_v / T + g_v, g_v from (v >> 2, p, step, 0).
+  const int v0 = bestc * kChunk + 4 * tid;
+  const int vend = min(V, (bestc + 1) * kChunk);
+  double sbest = -INFINITY;
+  int sv = 0x7fffffff;
+  if (v0 < vend) {
+    const Philox4 r = philox4x32_10((uint32_t)(v0 >> 2), (uint32_t)p, step, 0u, k0, k1);
+    const float* row = logits + (size_t)p * V;
+    const double T = (double)temperature;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = v0 + q;
+      if (v < vend) {
+        const double sc = (double)row[v] / T + gumbel_from_word(r.w[q]);
+        if (better_key(sc, v, sbest, sv)) {
+          sbest = sc;
+          sv = v;
+        }
+      }
+    }
+  }
+  block_argmax(sbest, sv, skey, sidx);
+  if (tid == 0) {
+    tokens_out[p] = sv;
+    entropy_out[p] = sH;
+  }
+}
+
+// ---------------------------------------------------------------- acceptance (one block)
+
+constexpr int kAcceptThreads = 1024;
+
+// Order-preserving map of a float to uint32 (-0 is folded onto +0).
+__device__ __forceinline__ uint32_t float_order_key(float h) {
+  uint32_t u = __builtin_bit_cast(uint32_t, h);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float float_from_order_key(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __builtin_bit_cast(float, u);
+}
+
+__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
+    const float* __restrict__ entropy, const int32_t* __restrict__ tokens, int P, float bound,
+    uint8_t* __restrict__ frozen, int32_t* __restrict__ canvas, uint8_t* __restrict__ accept_out,
+    int32_t* __restrict__ num_accepted) {
+  __shared__ uint64_t keys[kAcceptThreads];
+  __shared__ int sCount;
+  const int tid = threadIdx.x;
+  int n = 1;
+  while (n < P) n <<= 1;
+  if (tid < n) {
+    uint64_t key = ~0ull;  // non-candidates sort last
+    if (tid < P) {
+      const float h = entropy[tid];
+      const bool is_frozen = frozen != nullptr && frozen[tid];
+      if (!is_frozen && !(h != h)) key = ((uint64_t)float_order_key(h) << 32) | (uint32_t)tid;
+      accept_out[tid] = 0;
+    }
+    keys[tid] = key;
+  }
+  __syncthreads();
+  // Bitonic sort, ascending, of n keys (n a power of two, n <= 1024).
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (tid < n) {
+        const int partner = tid ^ j;
+        if (partner > tid) {
+          const uint64_t a = keys[tid], b = keys[partner];
+          const bool up = (tid & k) == 0;
+          if ((a > b) == up) {
+            keys[tid] = b;
+            keys[partner] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // One lane: the sequential fp32 scan in sorted order.
+  if (tid == 0) {
+    float S = 0.f;
+    int cnt = 0;
+    bool stop = false;
+    for (int base = 0; base < n && !stop; base += 8) {
+      uint64_t kk[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) kk[q] = (base + q < n) ? keys[base + q] : ~0ull;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (stop) break;
+        if (kk[q] == ~0ull) {
+          stop = true;
+          break;
+        }
+        const float h = float_from_order_key((uint32_t)(kk[q] >> 32));
+        S = __fadd_rn(S, h);
+        const float c = __fsub_rn(S, h);
+        if (!(c <= bound)) {
+          stop = true;
+          break;
+        }
+        ++cnt;
+      }
+    }
+    if (cnt == 0 && keys[0] != ~0ull) cnt = 1;
+    sCount = cnt;
+    *num_accepted = cnt;
+  }
+  __syncthreads();
+  if (tid < sCount) {
+    const int pos = (int)(uint32_t)keys[tid];
+    accept_out[pos] = 1;
+    if (canvas != nullptr) canvas[pos] = tokens[pos];
+    if (frozen != nullptr) frozen[pos] = 1;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- host-side launchers
+
+int sample_split_count(int P, int V) {
+  const int nC = (V + kChunk - 1) / kChunk;
+  int S = (2048 + P - 1) / P;
+  S = min(S, nC / 8);
+  return S < 1 ? 1 : S;
+}
+
+hipError_t launch_sample_entropy(const float* logits, int P, int V, float temperature,
+                                 uint64_t seed, uint32_t step, const uint8_t* frozen,
+                                 int32_t* tokens_out, float* entropy_out, void* workspace,
+                                 hipStream_t stream) {
+  const int nC = (V + kChunk - 1) / kChunk;
+  const int S = sample_split_count(P, V);
+  PartState* part = reinterpret_cast<PartState*>(workspace);
+  float* lmass = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                          align_up((size_t)P * S * sizeof(PartState)));
+  const dim3 grid(S, P);
+  const float invT = temperature > 0.f ? 1.f / temperature : 0.f;
+  if (temperature == 0.f)
+    hipLaunchKernelGGL(sample_stream_kernel<0>, grid, dim3(kStreamThreads), 0, stream, logits, V,
+                       nC, S, invT, frozen, part, lmass);
+  else if (temperature == 1.f)
+    hipLaunchKernelGGL(sample_stream_kernel<1>, grid, dim3(kStreamThreads), 0, stream, logits, V,
+                       nC, S, invT, frozen, part, lmass);
+  else
+    hipLaunchKernelGGL(sample_stream_kernel<2>, grid, dim3(kStreamThreads), 0, stream, logits, V,
+                       nC, S, invT, frozen, part, lmass);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(sample_finish_kernel, dim3(P), dim3(kFinishThreads), 0, stream, logits, V, nC,
+                     S, temperature, (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32), step,
+                     frozen, part, lmass, tokens_out, entropy_out);
+  return hipGetLastError();
+}
+
+size_t sample_workspace_bytes(int P, int V) {
+  const int nC = (V + kChunk - 1) / kChunk;
+  const int S = sample_split_count(P, V);
+  return align_up((size_t)P * S * sizeof(PartState)) + align_up((size_t)P * nC * sizeof(float));
+}
+
+hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, float bound,
+                         uint8_t* frozen, int32_t* canvas, uint8_t* accept_out,
+                         int32_t* num_accepted, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kAcceptThreads), 0, stream, entropy, tokens, P,
+                     bound, frozen, canvas, accept_out, num_accepted);
+  return hipGetLastError();
+}
+
+}  // namespace bd

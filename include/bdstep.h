@@ -1,0 +1,256 @@
+/*
+ * bdstep.h -- C ABI of the block-diffusion denoising-step hot path on MI355X (gfx950).
+ *
+ * Two parts, as on the pages this library implements:
+ *
+ *  1. The mixture-of-experts FFN of one layer over a canvas of T tokens: top-k routing
+ *     over E experts, the W4A16 expert GEMMs (asymmetric uint4 weights with an fp16
+ *     scale and fp16 zero-point per 64-element group along the contraction dim,
+ *     dequantised inline), the gated GELU folded into the gate/up epilogue, and a
+ *     fixed-order weighted combine.  Source: axe-diffusion-ksl-xe model card,
+ *     sections "what the model is", "the kernels we built" and "requirements".
+ *
+ *  2. The per-step sampler: per-position entropy and a gumbel-max (or argmax) token in
+ *     one streaming pass over fp32 logits, then the entropy-bound acceptance rule
+ *     (sort by ascending entropy, accept while (cumsum - cummax) <= bound, at least
+ *     one).  Sources: axe-diffusion-ksl-xe model card, "the kernels we built";
+ *     DiffusionGemma block-diffusion page, "Samplers".
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument except `workspace` sizes and host structs is a DEVICE
+ *    pointer into memory the caller owns.  The library allocates nothing, frees
+ *    nothing and keeps no pointer after the call's work completes on the stream.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
+ *    All work is enqueued on it asynchronously; no call synchronises the host.
+ *  - fp16 values travel as uint16_t bit patterns.  Arrays are dense and row-major.
+ *    The arrays read or written with vector accesses -- logits, x, expert_out, y, the
+ *    packed weights with their scales and zero-points, and workspaces -- must be
+ *    16-byte aligned (BD_ERR_ALIGN otherwise); every other array needs only the
+ *    alignment of its element type.
+ *  - Every argument is validated on the host BEFORE anything is enqueued; on any
+ *    error the call returns a nonzero bd_status and enqueues nothing.  A launch
+ *    failure returns BD_ERR_HIP.  Device faults surface at the caller's next sync.
+ *  - Calls are reentrant and the library holds no mutable global state.  Calls that
+ *    share a workspace must be ordered on one stream.
+ */
+#ifndef BDSTEP_H
+#define BDSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BD_ABI_VERSION 1
+/* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
+#define BD_SAMPLE_CHUNK 1024
+/* Limits checked on the host. */
+#define BD_MAX_EXPERTS 256
+#define BD_MAX_TOPK 16
+#define BD_MAX_TOKENS 65536
+#define BD_MAX_POSITIONS 1024
+#define BD_MAX_VOCAB (1 << 24)
+
+typedef enum {
+  BD_OK = 0,
+  BD_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  BD_ERR_SHAPE = 2,       /* a size is out of range or inconsistent             */
+  BD_ERR_ALIGN = 3,       /* a pointer lacks the alignment the ABI requires     */
+  BD_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the queried size */
+  BD_ERR_UNSUPPORTED = 5, /* valid in principle, not implemented (e.g. g != 64) */
+  BD_ERR_HIP = 6          /* a HIP launch or runtime call failed                */
+} bd_status;
+
+/*
+ * Packed W4A16 expert weights of one layer (all device pointers).
+ * Source: axe-diffusion-ksl-xe model card, "the kernels we built" and "requirements":
+ * asymmetric uint4, fp16 scale and zero-point per group, two nibbles per byte,
+ * groups along the contraction dimension.
+ *
+ *   gate_up_q      uint8 [E][2*d_ff][d_model/2]   rows 0..d_ff-1 = gate, d_ff..2*d_ff-1 = up
+ *   gate_up_scale  fp16  [E][2*d_ff][d_model/g]
+ *   gate_up_zero   fp16  [E][2*d_ff][d_model/g]
+ *   down_q         uint8 [E][d_model][d_ff/2]
+ *   down_scale     fp16  [E][d_model][d_ff/g]
+ *   down_zero      fp16  [E][d_model][d_ff/g]
+ *
+ * Byte i of a packed row holds element 2i in its low nibble and element 2i+1 in its
+ * high nibble.  The dequantised weight is w[n][k] = (q[n][k] - zero[n][k/g]) *
+ * scale[n][k/g].  Zero-points are the uint4 code of the zero (an integer 0..15 held
+ * in fp16); the GEMM subtracts them exactly in fp16, a non-integer zero-point is
+ * rounded to the nearest integer first.
+ * Supported: group_size == 64, d_model % 128 == 0, d_ff % 64 == 0.
+ */
+typedef struct bd_moe_weights {
+  int32_t num_experts; /* E, 1..256          */
+  int32_t top_k;       /* k, 1..min(E, 16)   */
+  int32_t d_model;     /* d                  */
+  int32_t d_ff;        /* f                  */
+  int32_t group_size;  /* g, must be 64      */
+  const uint8_t* gate_up_q;
+  const uint16_t* gate_up_scale;
+  const uint16_t* gate_up_zero;
+  const uint8_t* down_q;
+  const uint16_t* down_scale;
+  const uint16_t* down_zero;
+} bd_moe_weights;
+
+/* Library ABI version (BD_ABI_VERSION of the build). */
+int bd_abi_version(void);
+
+/* Static, never-NULL text for a bd_status value. */
+const char* bd_status_string(int status);
+
+/* ------------------------------------------------------------------ MoE FFN */
+
+/*
+ * Device workspace bytes needed by the MoE entry points for T tokens.  The same
+ * workspace carries the routing state from moe_route_topk to moe_w4a16_gate_up and
+ * moe_w4a16_down (the expert buckets, the work list and the fp16 GeGLU activations
+ * h [T*k][d_ff]).  Returns 0 if the shape is invalid.
+ */
+size_t bd_moe_workspace_size(int T, const bd_moe_weights* w);
+
+/*
+ * Routing: per token, the top_k experts by descending router logit (the lower expert
+ * id first on equal logits) and their weights = softmax over the k selected logits;
+ * then a stable bucketing of the T*k assignments by expert (ordered by token, then
+ * slot) and the work list of touched experts.
+ * Source: axe-diffusion-ksl-xe model card, "what the model is" (128 experts, top-8)
+ * and "the kernels we built" (one launch over all experts, not a per-expert loop).
+ *
+ *   router_logits  fp32  [T][E]   finite values
+ *   topk_ids       int32 [T][k]   out
+ *   topk_weights   fp32  [T][k]   out
+ *   workspace      device, >= bd_moe_workspace_size(T, w) bytes (routing state written)
+ */
+int moe_route_topk(const bd_moe_weights* w, int T, const float* router_logits,
+                   int32_t* topk_ids, float* topk_weights,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gate/up grouped W4A16 GEMM with the GeGLU epilogue, over every touched expert in
+ * one launch: for each assignment (t, j) routed to expert e,
+ *   h = gelu_tanh(W_gate[e] x_t) * (W_up[e] x_t),
+ * gelu_tanh(a) = a/2 (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))).  Packed nibbles are
+ * streamed once per expert tile, dequantised in registers, contracted on MFMA with
+ * fp32 accumulation per 64-group, scaled per group; h is kept in the workspace as fp16.
+ * Source: axe-diffusion-ksl-xe model card, "the kernels we built" (inline dequant of
+ * packed nibbles, activation folded into the first GEMM's epilogue).
+ * Requires a preceding moe_route_topk on the same workspace and stream.
+ *
+ *   x   fp16 [T][d_model]
+ */
+int moe_w4a16_gate_up(const bd_moe_weights* w, int T, const uint16_t* x,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Down grouped W4A16 GEMM: o[t][j] = W_down[e] h_(t,j) for every assignment, written
+ * in slot order with exactly one writer per row (no atomics).
+ * Requires a preceding moe_w4a16_gate_up on the same workspace and stream.
+ *
+ *   expert_out  fp32 [T][k][d_model]   out
+ */
+int moe_w4a16_down(const bd_moe_weights* w, int T, float* expert_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_route_topk, moe_w4a16_gate_up and moe_w4a16_down in one call. */
+int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x,
+                  const float* router_logits, int32_t* topk_ids, float* topk_weights,
+                  float* expert_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fixed-order weighted combine: y[t] = fp16( sum_{j=0}^{k-1} w[t][j] * o[t][j] ), the
+ * sum taken in fp32 as acc = fma(w[t][j], o[t][j], acc) for j = 0, 1, ..., k-1 from
+ * acc = 0, then rounded once to fp16 (round to nearest even).  No atomics: results are
+ * bit-identical from run to run.
+ * Source: axe-diffusion-ksl-xe model card, "the kernels we built" (fixed-order
+ * reduction instead of index_add_, since a 1-ulp change can flip an acceptance).
+ *
+ *   expert_out    fp32 [T][k][d]
+ *   topk_weights  fp32 [T][k]
+ *   y             fp16 [T][d]   out;  d % 4 == 0
+ */
+int moe_combine_fixed_order(const float* expert_out, const float* topk_weights,
+                            int T, int k, int d, uint16_t* y, void* stream);
+
+/* ------------------------------------------------------------------ sampler */
+
+/* Device workspace bytes needed by diffusion_sample_entropy for P rows of V logits. */
+size_t bd_sample_workspace_size(int P, int V);
+
+/*
+ * One streaming pass over fp32 logits [P][V] (row-major): for every position p that
+ * is not frozen,
+ *   entropy_out[p] = H_p = -sum_v softmax(x_p)_v * ln softmax(x_p)_v   (temperature 1)
+ *   tokens_out[p]  = argmax_v x_pv (lowest v on ties)                  if temperature == 0
+ *                  = a draw from softmax(x_p / temperature)             otherwise.
+ * The draw is gumbel-max on two levels: the row is cut into chunks of BD_SAMPLE_CHUNK
+ * entries; level 1 takes the chunk c maximising L_c + G_c with L_c = ln sum_{v in c}
+ * exp(x_v / temperature); level 2 takes, inside that chunk, the v maximising
+ * x_v / temperature + g_v (exact in distribution; identical to flat gumbel-max when
+ * V <= BD_SAMPLE_CHUNK).  Noise is Philox4x32-10 (Salmon et al., SC'11) keyed by
+ * (seed & 0xffffffff, seed >> 32): g_v from counter (v >> 2, p, step, 0) word v & 3,
+ * G_c from counter (c, p, step, 1) word 0; u = ((r >> 8) + 0.5) * 2^-24 and
+ * g = -ln(-ln u), both evaluated in fp64, as is the level-2 score.
+ * Sources: axe-diffusion-ksl-xe model card, "the kernels we built" (entropy once per
+ * step in a single streaming pass; one gumbel-max kernel instead of softmax +
+ * multinomial); configuration text "Philox, seed per step".
+ *
+ *   frozen       uint8 [P] or NULL (none frozen).  Frozen rows are not read; they get
+ *                tokens_out = -1 and entropy_out = +inf.
+ *   A row containing NaN or +inf, or only -inf, gets entropy NaN and token -1.
+ *   temperature  >= 0 and finite
+ *   P in 1..BD_MAX_POSITIONS, V in 1..BD_MAX_VOCAB.  V % 4 == 0 takes the vector path;
+ *   other V are handled, more slowly.
+ */
+int diffusion_sample_entropy(const float* logits, int P, int V, float temperature,
+                             uint64_t seed, uint32_t step, const uint8_t* frozen,
+                             int32_t* tokens_out, float* entropy_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Entropy-bound acceptance on one workgroup.  Candidates are the positions that are
+ * not frozen and whose entropy is not NaN; they are sorted by (entropy ascending,
+ * position ascending) and scanned in that order in fp32: S = S + H_i; c = S - H_i
+ * (cumsum - cummax, cummax being H_i in ascending order); position i is accepted
+ * while c <= bound, and the scan stops at the first failure.  If candidates exist and
+ * none passed, the first one is accepted.  Each accepted p gets accept_out[p] = 1,
+ * canvas[p] = tokens[p] and frozen[p] = 1; every other accept_out entry is 0.
+ * Source: DiffusionGemma block-diffusion page, "Samplers" (entropy-bound).
+ *
+ *   entropy       fp32  [P]      (the device's own entropies, e.g. from above)
+ *   tokens        int32 [P]
+ *   frozen        uint8 [P] in/out, or NULL (none frozen, nothing recorded)
+ *   canvas        int32 [P] in/out, or NULL (not updated)
+ *   accept_out    uint8 [P] out
+ *   num_accepted  int32 [1] out
+ *   bound         finite
+ */
+int diffusion_accept_entropy_bound(const float* entropy, const int32_t* tokens, int P,
+                                   float bound, uint8_t* frozen, int32_t* canvas,
+                                   uint8_t* accept_out, int32_t* num_accepted, void* stream);
+
+/* diffusion_sample_entropy then diffusion_accept_entropy_bound on the same stream. */
+int diffusion_sample_step(const float* logits, int P, int V, float temperature,
+                          float entropy_bound, uint64_t seed, uint32_t step,
+                          uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                          float* entropy_out, uint8_t* accept_out, int32_t* num_accepted,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ measurement */
+
+/*
+ * Plain device-to-device copy of `bytes` bytes (bytes % 16 == 0, both pointers 16-byte
+ * aligned) with a streaming kernel: the calibration for HBM traffic counters and the
+ * achievable-bandwidth figure beside the 8 TB/s specification.
+ */
+int bd_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDSTEP_H */

@@ -1,0 +1,130 @@
+"""Host-side checks of libbdstep (no GPU needed): the shared library loads, exports every
+function include/bdstep.h declares, and its argument validation rejects bad calls before
+anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "bdstep.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_diffusion_lm_router_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from block_diffusion_lm_router_amd import build
+        build.build()
+    return _binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "sizeof")))
+
+
+def test_header_declares_the_hot_path():
+    names = declared_functions()
+    for required in ("moe_w4a16_ffn", "moe_combine_fixed_order", "diffusion_sample_step",
+                     "moe_route_topk", "moe_w4a16_gate_up", "moe_w4a16_down",
+                     "diffusion_sample_entropy", "diffusion_accept_entropy_bound"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    from block_diffusion_lm_router_amd import _binding
+    names = declared_functions()
+    assert len(names) >= 13
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared but not exported"
+        assert name in _binding.SIGNATURES, f"{name} has no binding signature"
+    assert set(_binding.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bd_abi_version() == 1
+    for s in range(7):
+        assert len(lib.bd_status_string(s)) > 0
+    assert lib.bd_status_string(99) == b"unknown status"
+
+
+def _weights(E=128, k=8, d=2816, f=704, g=64, ptr=0x1000):
+    from block_diffusion_lm_router_amd._binding import MoeWeightsC
+    p = ctypes.c_void_p(ptr)
+    return MoeWeightsC(E, k, d, f, g, p, p, p, p, p, p)
+
+
+def test_moe_workspace_size(lib):
+    w = _weights()
+    n = lib.bd_moe_workspace_size(256, ctypes.byref(w))
+    A = 256 * 8
+    assert n >= A * 704 * 2 + A * 4 + 129 * 4
+    assert lib.bd_moe_workspace_size(0, ctypes.byref(w)) == 0
+    bad = _weights(g=128)
+    assert lib.bd_moe_workspace_size(256, ctypes.byref(bad)) == 0
+    assert lib.bd_moe_workspace_size(256, None) == 0
+
+
+@pytest.mark.parametrize("kw,T,code", [
+    (dict(), 0, 2), (dict(), 65537, 2), (dict(E=0), 4, 2), (dict(E=257), 4, 2),
+    (dict(k=0), 4, 2), (dict(k=17), 4, 2), (dict(E=4, k=5), 4, 2),
+    (dict(g=128), 4, 5), (dict(d=2880), 4, 5), (dict(f=700), 4, 5),
+])
+def test_moe_shape_validation(lib, kw, T, code):
+    w = _weights(**kw)
+    P = ctypes.c_void_p(0x1000)
+    assert lib.moe_route_topk(ctypes.byref(w), T, P, P, P, P, 1 << 40, None) == code
+
+
+def test_moe_pointer_and_workspace_validation(lib):
+    w = _weights()
+    P = ctypes.c_void_p(0x1000)
+    need = lib.bd_moe_workspace_size(256, ctypes.byref(w))
+    assert lib.moe_route_topk(ctypes.byref(w), 256, None, P, P, P, need, None) == 1
+    assert lib.moe_route_topk(ctypes.byref(w), 256, P, P, P, None, need, None) == 1
+    assert lib.moe_route_topk(ctypes.byref(w), 256, P, P, P, P, need - 1, None) == 4
+    assert lib.moe_route_topk(ctypes.byref(w), 256, ctypes.c_void_p(0x1002), P, P, P, need, None) == 3
+    assert lib.moe_w4a16_gate_up(ctypes.byref(w), 256, ctypes.c_void_p(0x1008), P, need, None) == 3
+    assert lib.moe_w4a16_down(ctypes.byref(w), 256, P, ctypes.c_void_p(0x1004), need, None) == 3
+    nulls = _weights(ptr=0)
+    assert lib.moe_w4a16_gate_up(ctypes.byref(nulls), 256, P, P, need, None) == 1
+    assert lib.moe_w4a16_ffn(ctypes.byref(w), 256, P, P, P, P, P, P, 16, None) == 4
+
+
+def test_combine_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    assert lib.moe_combine_fixed_order(P, P, 4, 8, 2818, P, None) == 2
+    assert lib.moe_combine_fixed_order(P, P, 4, 17, 2816, P, None) == 2
+    assert lib.moe_combine_fixed_order(None, P, 4, 8, 2816, P, None) == 1
+    assert lib.moe_combine_fixed_order(P, P, 4, 8, 2816, ctypes.c_void_p(0x1008), None) == 3
+
+
+def test_sampler_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    n = lib.bd_sample_workspace_size(256, 262144)
+    assert n >= 256 * 256 * 4
+    assert lib.bd_sample_workspace_size(0, 10) == 0
+    assert lib.bd_sample_workspace_size(1025, 10) == 0
+    assert lib.bd_sample_workspace_size(10, (1 << 24) + 1) == 0
+    call = lib.diffusion_sample_entropy
+    assert call(P, 256, 262144, -1.0, 0, 0, None, P, P, P, n, None) == 2
+    assert call(P, 256, 262144, float("nan"), 0, 0, None, P, P, P, n, None) == 2
+    assert call(P, 256, 262144, float("inf"), 0, 0, None, P, P, P, n, None) == 2
+    assert call(P, 256, 262144, 1.0, 0, 0, None, P, P, P, n - 1, None) == 4
+    assert call(None, 256, 262144, 1.0, 0, 0, None, P, P, P, n, None) == 1
+    assert call(ctypes.c_void_p(0x1004), 256, 262144, 1.0, 0, 0, None, P, P, P, n, None) == 3
+    acc = lib.diffusion_accept_entropy_bound
+    assert acc(P, P, 0, 1.0, None, None, P, P, None) == 2
+    assert acc(P, P, 1025, 1.0, None, None, P, P, None) == 2
+    assert acc(P, P, 8, float("nan"), None, None, P, P, None) == 2
+    assert acc(P, P, 8, 1.0, None, None, None, P, None) == 1
+    step = lib.diffusion_sample_step
+    assert step(P, 8, 100, 1.0, float("inf"), 0, 0, None, None, P, P, P, P, P, 1 << 20, None) == 2
+    assert lib.bd_hbm_copy(P, P, 17, None) == 2
+    assert lib.bd_hbm_copy(None, P, 16, None) == 1

@@ -1,0 +1,181 @@
+"""GPU parity of the MoE FFN (moe_route_topk / moe_w4a16_gate_up / moe_w4a16_down /
+moe_w4a16_ffn / moe_combine_fixed_order) against the CPU oracle, through the C ABI.
+
+Bars: top-k ids bit-exact; routing weights within fp32 rounding; per-assignment expert
+outputs and combined outputs within 2e-2 abs + 1e-2 rel of the fp64 oracle; the combine
+bit-identical across repeated runs.
+"""
+
+import numpy as np
+import pytest
+
+from block_diffusion_lm_router_amd import workloads
+from oracle import moe as omoe
+from gpu_common import check_ffn_close, requires_gpu, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+@pytest.fixture(scope="module")
+def bd():
+    import torch  # noqa: F401
+    from block_diffusion_lm_router_amd import _binding
+    _binding.load()
+    return _binding
+
+
+class Layer:
+    """One layer's inputs on the host and on the device."""
+
+    def __init__(self, bd, shape, x=None, logits=None, weights=None, layer=0):
+        import torch
+        self.shape = shape
+        self.x = workloads.make_activations(shape) if x is None else x
+        self.logits = workloads.make_router_logits(shape, layer) if logits is None else logits
+        self.w_np = workloads.make_weights(shape, layer) if weights is None else weights
+        self.w = bd.MoeWeights.from_numpy(self.w_np, shape.top_k)
+        self.x_d = torch.from_numpy(self.x).cuda()
+        self.logits_d = torch.from_numpy(self.logits).cuda()
+
+    def run(self, bd, fused=True):
+        import torch
+        T, k, d = self.shape.tokens, self.shape.top_k, self.shape.d_model
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        o = torch.full((T, k, d), float("nan"), dtype=torch.float32, device="cuda")
+        y = torch.empty((T, d), dtype=torch.float16, device="cuda")
+        ws = bd.moe_workspace(T, self.w)
+        if fused:
+            bd.moe_w4a16_ffn(self.w, self.x_d, self.logits_d, ids, tw, o, ws)
+        else:
+            bd.moe_route_topk(self.w, self.logits_d, ids, tw, ws)
+            bd.moe_w4a16_gate_up(self.w, self.x_d, ws)
+            bd.moe_w4a16_down(self.w, T, o, ws)
+        bd.moe_combine_fixed_order(o, tw, y)
+        torch.cuda.synchronize()
+        return ids.cpu().numpy(), tw.cpu().numpy(), o.cpu().numpy(), y.cpu().numpy()
+
+
+def outputs_and_h_rounding_bound(layer, ids, rows):
+    """Oracle expert outputs o[t, j] and the worst-case effect on them of storing the
+    GeGLU activations h in fp16 (the MFMA operand precision): |W_down| @ |h| * 2^-11."""
+    T, k = ids.shape
+    d = layer.shape.d_model
+    o = np.full((T, k, d), np.nan)
+    bound = np.full((T, k, d), np.nan)
+    mask = np.zeros(T, dtype=bool)
+    mask[rows] = True
+    x64 = layer.x.astype(np.float64)
+    for e in np.unique(ids[rows]):
+        tt, jj = np.nonzero((ids == e) & mask[:, None])
+        wg, wu, wd = omoe.expert_matrices(layer.w_np, int(e))
+        o[tt, jj] = omoe.expert_ffn(x64[tt], wg, wu, wd)
+        h = omoe.gelu_tanh(x64[tt] @ wg.T) * (x64[tt] @ wu.T)
+        bound[tt, jj] = (np.abs(h) @ np.abs(wd.T)) * 2.0 ** -11
+    return o, bound
+
+
+def check_layer(layer, got, tokens=None):
+    """ids bit-exact; y (the fp16 FFN output) within 2e-2 + 1e-2|ref|; the fp32 per-assignment
+    outputs within that plus the fp16 rounding bound of h, and rel-L2 <= 1e-3."""
+    ids, tw, o, y = got
+    ref_ids, ref_w = omoe.route_topk(layer.logits, layer.shape.top_k)
+    assert np.array_equal(ids, ref_ids), "top-k ids differ"
+    np.testing.assert_allclose(tw, ref_w, rtol=2e-6, atol=1e-7)
+    rows = np.arange(layer.shape.tokens) if tokens is None else np.asarray(tokens)
+    o_ref, o_bound = outputs_and_h_rounding_bound(layer, ref_ids, rows)
+    err = np.abs(o[rows] - o_ref[rows])
+    lim = 2e-2 + 1e-2 * np.abs(o_ref[rows]) + o_bound[rows]
+    assert np.all(err <= lim), f"expert_out: {int((err > lim).sum())} outside; worst {(err / lim).max():.3g}"
+    rel_l2 = np.sqrt(np.sum(err ** 2) / np.sum(o_ref[rows] ** 2))
+    assert rel_l2 < 1e-3, f"expert_out rel-L2 {rel_l2:.3g}"
+    y_ref = omoe.combine(o_ref[rows], ref_w[rows])
+    return check_ffn_close(y[rows].astype(np.float64), y_ref, "y")
+
+
+def test_tiny_layer(bd):
+    say("tiny layer")
+    layer = Layer(bd, workloads.TINY_LAYER)
+    got = layer.run(bd)
+    rel = check_layer(layer, got)
+    assert rel < 2e-3
+    got2 = layer.run(bd, fused=False)
+    for a, b in zip(got, got2):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("T,E,k,d,f", [(1, 4, 1, 128, 64), (3, 8, 3, 256, 192),
+                                       (100, 4, 2, 128, 64), (77, 16, 4, 384, 128),
+                                       (250, 2, 2, 128, 64)])
+def test_ragged_buckets(bd, T, E, k, d, f):
+    """Buckets of 1..T tokens: partial 16-row tiles, several 32-token items per expert."""
+    shape = workloads.LayerShape(T, d, f, E, k)
+    say("ragged buckets", T, E, k, d, f)
+    layer = Layer(bd, shape, layer=T + E)
+    check_layer(layer, layer.run(bd))
+
+
+def test_single_expert_and_zero_input(bd):
+    shape = workloads.LayerShape(40, 256, 128, 1, 1)
+    say("single expert / zero input")
+    layer = Layer(bd, shape, logits=np.zeros((40, 1), dtype=np.float32), layer=3)
+    check_layer(layer, layer.run(bd))
+    zero = Layer(bd, shape, x=np.zeros((40, 256), dtype=np.float16),
+                 logits=np.zeros((40, 1), dtype=np.float32), layer=3)
+    _, _, o, y = zero.run(bd)
+    assert np.all(o == 0) and np.all(y == 0)
+
+
+def test_router_ties_take_lower_expert(bd):
+    shape = workloads.LayerShape(16, 128, 64, 8, 3)
+    logits = np.zeros((16, 8), dtype=np.float32)
+    logits[:, 5] = 1.0
+    logits[3, [1, 6]] = 1.0
+    logits[7, :] = -0.0
+    say("router ties")
+    layer = Layer(bd, shape, logits=logits, layer=1)
+    check_layer(layer, layer.run(bd))
+
+
+def test_combine_bit_identical_and_within_fp16_rounding(bd):
+    import torch
+    rng = np.random.default_rng(4)
+    T, k, d = 200, 8, 2816
+    o = torch.from_numpy(rng.standard_normal((T, k, d)).astype(np.float32) * 30).cuda()
+    w = torch.from_numpy(rng.random((T, k)).astype(np.float32)).cuda()
+    say("combine repeat")
+    outs = []
+    for _ in range(5):
+        y = torch.empty((T, d), dtype=torch.float16, device="cuda")
+        bd.moe_combine_fixed_order(o, w, y)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    for y in outs[1:]:
+        assert np.array_equal(y.view(np.uint16), outs[0].view(np.uint16))
+    o_np, w_np = o.cpu().numpy().astype(np.float64), w.cpu().numpy().astype(np.float64)
+    ref = omoe.combine(o_np, w_np)
+    y = outs[0].astype(np.float64)
+    # one fp16 rounding (half an ulp of the result) plus k fp32 roundings of the running sum
+    half_ulp = 0.5 * np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    fp32_sum = 2.0 ** -24 * k * np.einsum("tj,tjd->td", np.abs(w_np), np.abs(o_np))
+    assert np.all(np.abs(y - ref) <= half_ulp * 1.0001 + fp32_sum)
+
+
+def test_full_layer_sampled_tokens(bd):
+    """Full shape (256 tokens, 128 experts, top-8): ids for all, outputs on sampled tokens."""
+    say("full layer")
+    layer = Layer(bd, workloads.LAYER)
+    got = layer.run(bd)
+    tokens = np.random.default_rng(0).choice(layer.shape.tokens, 6, replace=False)
+    check_layer(layer, got, tokens=tokens)
+
+
+def test_short_zipf_layer(bd):
+    """64 tokens with Zipf-skewed routing: small and large buckets in one launch."""
+    say("short zipf layer")
+    layer = Layer(bd, workloads.SHORT_LAYER)
+    got = layer.run(bd)
+    counts = np.bincount(got[0].ravel(), minlength=128)
+    assert counts.max() > 32      # the hottest expert needs several 32-token items
+    tokens = np.random.default_rng(1).choice(layer.shape.tokens, 6, replace=False)
+    check_layer(layer, got, tokens=tokens)

@@ -1,0 +1,237 @@
+"""GPU parity of the sampler (diffusion_sample_entropy / _accept_entropy_bound / _step)
+against the CPU oracle, through the C ABI.
+
+Bars: tokens at temperature 0 and acceptance masks bit-exact (the mask fed the GPU's
+entropies); entropies within 1e-4 relative; tokens at T > 0 bit-exact except where the
+oracle's own decision margin is below the rounding of the chunk log-masses.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from block_diffusion_lm_router_amd import workloads
+from oracle import sampler as osamp
+from gpu_common import (H_REL, L1_MARGIN, L2_MARGIN, requires_gpu, say, top2_margin)
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+@pytest.fixture(scope="module")
+def bd():
+    import torch  # noqa: F401
+    from block_diffusion_lm_router_amd import _binding
+    _binding.load()
+    return _binding
+
+
+def run_entropy(bd, logits_np, temperature, seed=0, step=0, frozen_np=None):
+    import torch
+    P, V = logits_np.shape
+    logits = torch.from_numpy(np.ascontiguousarray(logits_np)).cuda()
+    frozen = None if frozen_np is None else torch.from_numpy(frozen_np.astype(np.uint8)).cuda()
+    tok = torch.empty(P, dtype=torch.int32, device="cuda")
+    H = torch.empty(P, dtype=torch.float32, device="cuda")
+    ws = bd.sample_workspace(P, V)
+    bd.diffusion_sample_entropy(logits, temperature, seed, step, frozen, tok, H, ws)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), H.cpu().numpy()
+
+
+def check_entropy(H_gpu, H_ref, rows=None):
+    rows = range(len(H_ref)) if rows is None else rows
+    for p in rows:
+        r = H_ref[p]
+        g = float(H_gpu[p])
+        if math.isnan(r):
+            assert math.isnan(g), f"row {p}: expected NaN, got {g}"
+        elif math.isinf(r):
+            assert g == r, f"row {p}: expected {r}, got {g}"
+        else:
+            assert abs(g - r) <= H_REL * r + 1e-30, f"row {p}: H {g} vs {r} (rel {abs(g - r) / r:.3g})"
+
+
+def check_tokens_sampled(logits_np, tok_gpu, temperature, seed, step, rows=None, frozen=None):
+    """Bit-exact tokens, excusing only near-ties; returns the number of excused rows."""
+    excused = 0
+    P = logits_np.shape[0]
+    for p in (range(P) if rows is None else rows):
+        if frozen is not None and frozen[p]:
+            assert tok_gpu[p] == -1
+            continue
+        x = logits_np[p]
+        if not osamp.row_is_valid(x):
+            assert tok_gpu[p] == -1, f"row {p}: invalid row must give -1"
+            continue
+        ref, keys, scores = osamp.draw_token(x, temperature, seed, step, p)
+        if int(tok_gpu[p]) == ref:
+            continue
+        assert temperature > 0, f"row {p}: argmax {tok_gpu[p]} vs {ref}"
+        kmax = np.max(keys[np.isfinite(keys)])
+        near1 = top2_margin(keys) < L1_MARGIN * max(1.0, abs(kmax))
+        near2 = top2_margin(scores) < L2_MARGIN * max(1.0, np.max(np.abs(scores[np.isfinite(scores)])))
+        assert near1 or near2, (f"row {p}: token {tok_gpu[p]} vs oracle {ref} with margins "
+                                f"{top2_margin(keys):.3g} / {top2_margin(scores):.3g}")
+        excused += 1
+    return excused
+
+
+# ---------------------------------------------------------------- tiny workload
+
+
+@pytest.mark.parametrize("temperature", [0.0, 1.0, 0.7])
+def test_tiny_workload(bd, temperature):
+    shape = workloads.TINY_SAMPLER
+    x = workloads.make_logits(shape)
+    say("tiny sampler", x.shape, "T", temperature)
+    tok, H = run_entropy(bd, x, temperature, seed=shape.seed, step=3)
+    H_ref = np.array([osamp.entropy(r) for r in x])
+    check_entropy(H, H_ref)
+    assert check_tokens_sampled(x, tok, temperature, shape.seed, 3) <= 1
+
+
+@pytest.mark.parametrize("P,V", [(1, 1), (3, 7), (5, 1023), (4, 1025), (7, 4100), (6, 5003),
+                                 (2, 3 * 1024), (1024, 64)])
+@pytest.mark.parametrize("temperature", [0.0, 1.0])
+def test_ragged_shapes(bd, P, V, temperature):
+    rng = np.random.default_rng(P * 7919 + V)
+    x = (rng.standard_normal((P, V)) * 3).astype(np.float32)
+    say("ragged", P, V, temperature)
+    tok, H = run_entropy(bd, x, temperature, seed=11, step=5)
+    check_entropy(H, np.array([osamp.entropy(r) for r in x]))
+    assert check_tokens_sampled(x, tok, temperature, 11, 5) <= max(1, P // 50)
+
+
+def special_rows(V=3000):
+    rows = []
+    rng = np.random.default_rng(99)
+    base = rng.standard_normal(V).astype(np.float32)
+    r = base.copy(); r[17] = np.nan; rows.append(r)                      # NaN
+    r = base.copy(); r[2999] = np.inf; rows.append(r)                    # +inf
+    rows.append(np.full(V, -np.inf, dtype=np.float32))                   # all -inf
+    r = np.full(V, -np.inf, dtype=np.float32); r[2050] = 1.5; rows.append(r)   # one live entry
+    r = base.copy(); r[:2048] = -np.inf; rows.append(r)                  # first chunks dead
+    r = base.copy(); r[1500] += 40.0; rows.append(r)                     # near-zero entropy
+    r = base.copy(); r[[5, 1100, 2900]] = 9.0; rows.append(r)            # ties at the maximum
+    rows.append(np.zeros(V, dtype=np.float32))                           # uniform: ln V
+    r = np.full(V, -np.inf, dtype=np.float32); r[10] = np.nan; rows.append(r)  # NaN among -inf
+    r = base.copy(); r[700] = -np.inf; r[701] = np.float32(-3e38); rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("temperature", [0.0, 1.0])
+def test_special_rows(bd, temperature):
+    x = special_rows()
+    say("special rows", x.shape, temperature)
+    tok, H = run_entropy(bd, x, temperature, seed=3, step=1)
+    H_ref = np.array([osamp.entropy(r) for r in x])
+    check_entropy(H, H_ref)
+    assert check_tokens_sampled(x, tok, temperature, 3, 1) == 0
+    if temperature == 0.0:
+        assert tok[6] == 5                       # lowest index among tied maxima
+    assert abs(H[7] - math.log(x.shape[1])) < 1e-4 * math.log(x.shape[1])
+
+
+def test_frozen_rows_are_skipped(bd):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((9, 2048)).astype(np.float32)
+    frozen = np.array([1, 0, 0, 1, 1, 0, 1, 0, 1], dtype=np.uint8)
+    x[frozen == 1] = np.nan                      # must not be read
+    say("frozen rows")
+    tok, H = run_entropy(bd, x, 1.0, seed=2, step=0, frozen_np=frozen)
+    assert np.all(tok[frozen == 1] == -1) and np.all(np.isposinf(H[frozen == 1]))
+    H_ref = np.array([osamp.entropy(r) if not f else np.inf for r, f in zip(x, frozen)])
+    check_entropy(H, H_ref)
+    assert check_tokens_sampled(x, tok, 1.0, 2, 0, frozen=frozen) == 0
+
+
+def test_repeat_runs_bit_identical(bd):
+    x = workloads.make_logits(workloads.TINY_SAMPLER)
+    say("repeat bit-identity")
+    a = run_entropy(bd, x, 1.0, seed=5, step=9)
+    for _ in range(3):
+        b = run_entropy(bd, x, 1.0, seed=5, step=9)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+# ---------------------------------------------------------------- acceptance
+
+
+def run_accept(bd, H_np, tokens_np, bound, frozen_np=None, canvas_np=None):
+    import torch
+    P = H_np.shape[0]
+    H = torch.from_numpy(H_np.astype(np.float32)).cuda()
+    tok = torch.from_numpy(tokens_np.astype(np.int32)).cuda()
+    frozen = None if frozen_np is None else torch.from_numpy(frozen_np.astype(np.uint8)).cuda()
+    canvas = None if canvas_np is None else torch.from_numpy(canvas_np.astype(np.int32)).cuda()
+    acc = torch.full((P,), 7, dtype=torch.uint8, device="cuda")
+    cnt = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    bd.diffusion_accept_entropy_bound(H, tok, bound, frozen, canvas, acc, cnt)
+    torch.cuda.synchronize()
+    return (acc.cpu().numpy(), int(cnt.item()),
+            None if frozen is None else frozen.cpu().numpy(),
+            None if canvas is None else canvas.cpu().numpy())
+
+
+@pytest.mark.parametrize("P", [1, 2, 5, 64, 256, 1000, 1024])
+def test_accept_matches_oracle(bd, P):
+    rng = np.random.default_rng(P)
+    for trial in range(6):
+        H = (rng.exponential(0.4, P) * (rng.random(P) < 0.8)).astype(np.float32)
+        H[rng.random(P) < 0.05] = np.nan
+        if trial == 1:
+            H[:] = 0.25                              # all tied: position order decides
+        frozen = (rng.random(P) < 0.3).astype(np.uint8)
+        tokens = rng.integers(0, 1000, P).astype(np.int32)
+        canvas = rng.integers(0, 1000, P).astype(np.int32)
+        bound = [2.0, 0.0, -1.0, 1e30, 0.5, 5.0][trial]
+        say("accept", P, trial, bound)
+        acc, cnt, fr, cv = run_accept(bd, H, tokens, bound, frozen, canvas)
+        ref_mask, ref_n = osamp.accept(H, bound, frozen)
+        assert cnt == ref_n and np.array_equal(acc, ref_mask), f"P={P} trial={trial}"
+        assert np.array_equal(fr, np.maximum(frozen, ref_mask))
+        assert np.array_equal(cv, np.where(ref_mask == 1, tokens, canvas))
+
+
+def test_accept_without_frozen_or_canvas(bd):
+    H = np.array([0.5, 0.1, 0.2, 3.0], dtype=np.float32)
+    acc, cnt, _, _ = run_accept(bd, H, np.arange(4), 0.25)
+    ref_mask, ref_n = osamp.accept(H, 0.25)   # exclusive sums 0, .1, .3 -> two pass
+    assert cnt == ref_n == 2 and np.array_equal(acc, ref_mask)
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+
+@pytest.mark.parametrize("which", ["sampler", "sampler_wide"])
+def test_full_size_step(bd, which):
+    import torch
+    shape = workloads.SAMPLER if which == "sampler" else workloads.SAMPLER_WIDE
+    x = workloads.make_logits(shape)
+    P, V = x.shape
+    say("full-size", which, x.shape)
+    H_ref = np.array([osamp.entropy(r) for r in x])
+    for temperature, step in ((0.0, 0), (1.0, 4)):
+        logits = torch.from_numpy(x).cuda()
+        frozen = torch.zeros(P, dtype=torch.uint8, device="cuda")
+        canvas = torch.full((P,), -7, dtype=torch.int32, device="cuda")
+        tok = torch.empty(P, dtype=torch.int32, device="cuda")
+        H = torch.empty(P, dtype=torch.float32, device="cuda")
+        acc = torch.empty(P, dtype=torch.uint8, device="cuda")
+        cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+        ws = bd.sample_workspace(P, V)
+        bd.diffusion_sample_step(logits, temperature, shape.bound, shape.seed, step, frozen,
+                                 canvas, tok, H, acc, cnt, ws)
+        torch.cuda.synchronize()
+        tok_np, H_np = tok.cpu().numpy(), H.cpu().numpy()
+        check_entropy(H_np, H_ref)
+        ex = check_tokens_sampled(x, tok_np, temperature, shape.seed, step)
+        assert ex <= 3, f"{ex} near-tie rows excused"
+        ref_mask, ref_n = osamp.accept(H_np, shape.bound)
+        assert int(cnt.item()) == ref_n
+        assert np.array_equal(acc.cpu().numpy(), ref_mask)
+        assert np.array_equal(frozen.cpu().numpy(), ref_mask)
+        assert np.array_equal(canvas.cpu().numpy(), np.where(ref_mask == 1, tok_np, -7))
+        if which == "sampler_wide":
+            assert ref_n > 1        # the wide-boost variant exercises multi-accept
