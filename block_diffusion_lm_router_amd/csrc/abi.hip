@@ -23,6 +23,7 @@ int check_moe_shape(const bd_moe_weights* w, int T) {
   if (w->d_model < 1 || w->d_ff < 1) return BD_ERR_SHAPE;
   if (w->group_size != 64) return BD_ERR_UNSUPPORTED;
   if (w->d_model % 128 != 0 || w->d_ff % 64 != 0) return BD_ERR_UNSUPPORTED;
+  if (w->d_model > 4096 || w->d_ff > 4096) return BD_ERR_UNSUPPORTED;  // per-block scale table
   if ((int64_t)T * w->top_k > (int64_t)BD_MAX_TOKENS * BD_MAX_TOPK) return BD_ERR_SHAPE;
   return BD_OK;
 }

@@ -22,7 +22,10 @@ struct PartState {
 };
 
 // ---------------------------------------------------------------- MoE
-constexpr int kItemTokens = 32;  // tokens per work item of the grouped GEMMs
+#ifndef BD_ITEM_TOKENS
+#define BD_ITEM_TOKENS 32
+#endif
+constexpr int kItemTokens = BD_ITEM_TOKENS;  // tokens per work item of the grouped GEMMs (16 or 32)
 
 struct MoeWorkspace {
   int32_t* offsets;  // [E + 1] bucket starts

@@ -8,9 +8,22 @@
 // Work decomposition.  A block owns one work item (an expert and up to 32 of its routed
 // tokens) and one tile of 128 weight rows: gate/up takes 64 gate rows and the 64 up rows
 // that pair with them, so the GeGLU product is formed in registers; down takes 128
-// consecutive output rows.  Each wave owns two 16-row sets.  The block streams every
-// packed byte of its rows exactly once (8 bytes per lane per 64-group: one group of one
-// row for four lanes), so the expert's weights cross HBM once per 32 tokens.
+// consecutive output rows.  Each wave owns two 16-row sets.  Every packed byte of the
+// block's rows crosses HBM once per item.
+//
+// Block order.  Consecutive block ids are dispatched round-robin over the 8 XCDs.  Block b
+// maps to XCD b % 8, and the blocks an XCD receives walk through all row tiles of one item
+// before the next, so the item's activation rows are fetched into that XCD's L2 once.
+//
+// Data movement.  The contraction dim is walked in stages of kSG 64-groups.  Packed weight
+// rows and activation rows go from HBM straight into a ring of LDS stage buffers with
+// global_load_lds_dwordx4 (no VGPRs held while in flight); each wave fetches its own
+// weight rows (whole 16-byte chunks of kSG*32 contiguous bytes per row) and a share of
+// the block's activation rows, kDepth stages ahead.  The compiler does not order LDS reads
+// after these loads, so each stage starts with an explicit s_waitcnt vmcnt for the wave's
+// own loads followed by a block barrier.  Scales and zero-points (two halves per row and
+// group) are fetched through registers and written to the stage buffer before the barrier.
+// Both LDS layouts are XOR-swizzled by row so that MFMA fragment reads are conflict-free.
 //
 // MFMA layout (v_mfma_f32_16x16x32_f16).  A = activations (16 tokens x 32 k), B =
 // dequantised weights (32 k x 16 rows), D = 16 tokens x 16 rows in fp32.  Lane (n, kb) =
@@ -22,14 +35,10 @@
 // masks 0x000F000F and 0x00F000F0 (and the same after >> 8) yield the pairs (k0,k4),
 // (16k1,16k5), (k2,k6), (16k3,16k7).  One packed add of -(1024 + z) or one packed fma
 // by 1/16 then -(64 + z) turns each pair into the exact fp16 values q - z.  The k-order
-// of a lane's 8 weights is therefore (0,4,1,5,2,6,3,7); the activation tile in LDS is
-// stored in the same order, so the contraction is unchanged.  The 64-group partial sums
-// come out of MFMA in fp32 and are scaled by that group's fp16 scale in fp32.
-//
-// Pipeline.  The contraction dim is walked in stages of 4 groups (256 k).  While stage
-// c is contracted, the packed bytes of stage c+1 are in flight in registers and the
-// activations and scales/zero-points of stage c+1 are fetched into registers, then
-// written to the other LDS buffer.  One barrier per stage.
+// of a lane's 8 weights is therefore (0,4,1,5,2,6,3,7); activation fragments are put in
+// the same order (gate/up permutes x after the LDS read; down's h is stored permuted by
+// the gate/up epilogue), so the contraction is unchanged.  The 64-group partial sums come
+// out of MFMA in fp32 and are scaled by that group's fp16 scale in fp32.
 
 #include "bd_device.hpp"
 #include "bd_internal.hpp"
@@ -38,11 +47,44 @@ namespace bd {
 
 namespace {
 
+#ifndef BD_STAGE_GROUPS
+#define BD_STAGE_GROUPS 2
+#endif
+#ifndef BD_DEPTH
+#define BD_DEPTH 2
+#endif
+
 constexpr int kThreads = 256;
-constexpr int kStageK = 256;                 // contraction entries per stage
-constexpr int kStageGroups = kStageK / 64;   // 64-groups per stage
-constexpr int kXStride = kStageK + 8;        // halves; 16-byte pad against bank aliasing
 constexpr int kRowsPerBlock = 128;
+constexpr int kXcds = 8;
+constexpr int kSG = BD_STAGE_GROUPS;                 // 64-groups per stage (2 or 4)
+constexpr int kDepth = BD_DEPTH;                     // stages in flight ahead of compute
+constexpr int kRing = kDepth + 1;                    // stage buffers
+constexpr int kStageK = kSG * 64;
+constexpr int kWRowBytes = kSG * 32;                 // packed bytes of one row per stage
+constexpr int kWChunks = kWRowBytes / 16;            // 16-byte chunks per row per stage
+constexpr int kWRowsPerLoad = 1024 / kWRowBytes;     // rows covered by one wave-wide load
+constexpr int kWLoads = 32 / kWRowsPerLoad;          // loads per wave per stage (32 rows)
+constexpr int kWWaveBytes = 32 * kWRowBytes;
+constexpr int kWBytes = 4 * kWWaveBytes;
+constexpr int kXRows = kItemTokens;                  // activation rows per item (<= 32)
+constexpr int kXRowBytes = kStageK * 2;
+constexpr int kXChunks = kXRowBytes / 16;
+constexpr int kXRowsPerLoad = 1024 / kXRowBytes;
+constexpr int kXBytes = kXRows * kXRowBytes;
+constexpr int kStageBytes = kWBytes + kXBytes;
+constexpr int kRingBytes = kRing * kStageBytes;
+// Scale and zero-point tables of the block's 128 rows for the whole contraction dim, loaded
+// once per block: [2 arrays][128 rows][G] halves.  G is at most kMaxGroups.
+constexpr int kMaxGroups = 64;
+constexpr int kSZTableBytes = 2 * kRowsPerBlock * kMaxGroups * 2;
+constexpr int kLdsBytes = kRingBytes + kSZTableBytes;
+static_assert(kItemTokens == 16 || kItemTokens == 32, "work items hold at most 32 tokens");
+static_assert(kWChunks * 16 == kWRowBytes && kXChunks >= 16, "stage geometry");
+
+// Row swizzles: rows that alias in the 64 LDS banks get different chunk rotations.
+__device__ __forceinline__ int wswz(int r) { return (r / (64 / (kWRowBytes / 4))) & (kWChunks - 1); }
+__device__ __forceinline__ int xswz(int m) { return m & 15; }
 
 struct GemmArgs {
   const uint8_t* q;        // [E][R][K/2]
@@ -52,6 +94,7 @@ struct GemmArgs {
   int R;                   // rows per expert
   int d_ff;                // gate/up: first up row
   int top_k;
+  int tiles;               // row tiles per item
   const uint16_t* act;     // gate/up: x [T][K]; down: h [T*k][K] (bucket order, permuted k)
   const int32_t* perm;     // bucket position -> assignment t*k + j
   const int32_t* items;    // [0] = count, then (expert, first position, tokens)
@@ -86,13 +129,16 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 zc1, _Float16 z
   return r;
 }
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 // Reorder 8 halves (h0..h7) to (h0,h4,h1,h5,h2,h6,h3,h7).
-__device__ __forceinline__ uint4 permute8(uint4 v) {
-  uint4 r;
-  r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-  r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-  r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-  r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+__device__ __forceinline__ u32x4_t permute8(u32x4_t v) {
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
   return r;
 }
 
@@ -102,168 +148,188 @@ __device__ __forceinline__ float gelu_tanh(float a) {
   return 0.5f * a * (1.f + th);
 }
 
-template <bool GATED>
-__global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(GemmArgs a) {
-  const int item = blockIdx.y;
-  if (item >= a.items[0]) return;
-  const int e = a.items[1 + 3 * item];
-  const int pos0 = a.items[2 + 3 * item];
-  const int mcount = a.items[3 + 3 * item];
-  const int tile = blockIdx.x;
+// Wait until at most N of this wave's vector-memory operations are outstanding.  Written as
+// asm with a memory clobber so that no LDS read is scheduled above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Block barrier for LDS data only: this wave's LDS writes complete, then s_barrier.  Unlike
+// __syncthreads() it does not drain outstanding global loads (the stage prefetches).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <bool GATED, int NMT>
+__device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, int pos0,
+                                          int mcount, int tile) {
+  constexpr int kXLoads = (NMT * 16) / kXRowsPerLoad / 4;   // activation loads per wave per stage
+  constexpr int kLoads = kWLoads + kXLoads;                  // loads per wave per stage
+  static_assert(kXLoads >= 1 && kLoads * kDepth < 64, "load count");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n = lane & 15;
   const int kb = lane >> 4;
   const int G = a.K >> 6;
-  const int NS = (G + kStageGroups - 1) / kStageGroups;
-  const int nMT = (mcount + 15) >> 4;
-
-  const int rA = GATED ? tile * 64 + wave * 16 + n : tile * kRowsPerBlock + wave * 32 + n;
-  const int rB = GATED ? a.d_ff + rA : rA + 16;
+  const int NS = (G + kSG - 1) / kSG;
   const size_t rowbytes = (size_t)(a.K >> 1);
-  const uint8_t* __restrict__ qA = a.q + ((size_t)e * a.R + rA) * rowbytes + kb * 8;
-  const uint8_t* __restrict__ qB = a.q + ((size_t)e * a.R + rB) * rowbytes + kb * 8;
 
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2][kItemTokens][kXStride];
-  __shared__ __attribute__((aligned(16))) _Float16 szs[2][2][kRowsPerBlock][kStageGroups];
-
-  // Staging roles: activations (row m, 32-half segment) and scale/zero (row slot, group pair).
-  const int st_m = tid >> 3;
-  const int st_seg = tid & 7;
-  const uint16_t* xsrc = nullptr;
-  if (st_m < mcount) {
-    if (GATED) {
-      const int tok = a.perm[pos0 + st_m] / a.top_k;
-      xsrc = a.act + (size_t)tok * a.K + st_seg * 32;
-    } else {
-      xsrc = a.act + (size_t)(pos0 + st_m) * a.K + st_seg * 32;
-    }
+  // Weight rows of this wave: set A = rows rA0.., set B = rows rB0.. (16 each).
+  const int rA0 = GATED ? tile * 64 + wave * 16 : tile * kRowsPerBlock + wave * 32;
+  const int rB0 = GATED ? a.d_ff + rA0 : rA0 + 16;
+  // Their slots in the scale/zero table.
+  const int slotA = GATED ? wave * 16 + n : wave * 32 + n;
+  const int slotB = GATED ? 64 + wave * 16 + n : wave * 32 + 16 + n;
+  // Weight loads: load i covers wave rows i*kWRowsPerLoad..; lane -> (row, chunk slot), the
+  // slot holding global chunk slot ^ wswz(row).
+  const uint8_t* wsrc[kWLoads];
+  int wchunk[kWLoads];
+#pragma unroll
+  for (int i = 0; i < kWLoads; ++i) {
+    const int r = i * kWRowsPerLoad + lane / kWChunks;
+    const int grow = r < 16 ? rA0 + r : rB0 + (r - 16);
+    wsrc[i] = a.q + ((size_t)e * a.R + grow) * rowbytes;
+    wchunk[i] = (lane % kWChunks) ^ wswz(r & 15);
   }
-  const int sz_r = tid >> 1;
-  const int sz_gp = (tid & 1) * 2;
-  int sz_row;
+  // Activation loads: load i of this wave covers rows (wave*kXLoads + i)*kXRowsPerLoad..
+  const uint16_t* xsrc[kXLoads];
+  int xchunk[kXLoads];
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    const int m = (wave * kXLoads + i) * kXRowsPerLoad + lane / kXChunks;
+    const int mm = m < mcount ? m : mcount - 1;              // padding rows re-read a valid row
+    const int row = GATED ? a.perm[pos0 + mm] / a.top_k : pos0 + mm;
+    xsrc[i] = a.act + (size_t)row * a.K;
+    xchunk[i] = (lane % kXChunks) ^ xswz(m);
+  }
+
+  // Scale / zero-point table, copied once: the block's rows form contiguous 16-byte aligned
+  // ranges of each array (gate/up: 64 gate rows and 64 up rows; down: 128 rows), laid out in
+  // LDS back to back as [array][row slot][group].  Chunk q (16 bytes) of the concatenated
+  // ranges goes to table byte 16q; a wave-wide copy covers 64 consecutive chunks, and lanes
+  // past the end re-read the last chunk into the table's padding.
+  char* sztab = lds + kRingBytes;
   {
-    const int w = sz_r >> 5, b = (sz_r >> 4) & 1, nn = sz_r & 15;
-    sz_row = GATED ? (b ? a.d_ff : 0) + tile * 64 + w * 16 + nn : tile * kRowsPerBlock + w * 32 + b * 16 + nn;
+    const int rows = GATED ? 64 : kRowsPerBlock;
+    const int rchunks = rows * G * 2 / 16;
+    const int ranges = GATED ? 4 : 2;
+    const int total = ranges * rchunks;
+    for (int q0 = wave * 64; q0 < total; q0 += 4 * 64) {
+      const int q = min(q0 + lane, total - 1);
+      const int rng = q / rchunks;
+      const int arr = GATED ? (rng >> 1) : rng;
+      const int row0 = GATED ? ((rng & 1) ? a.d_ff : 0) + tile * 64 : tile * kRowsPerBlock;
+      const char* src = reinterpret_cast<const char*>((arr ? a.zero : a.scale) +
+                                                      ((size_t)e * a.R + row0) * G) +
+                        (q % rchunks) * 16;
+      __builtin_amdgcn_global_load_lds(src, sztab + q0 * 16, 16, 0, 0);
+    }
   }
-  const uint16_t* __restrict__ ssrc = a.scale + ((size_t)e * a.R + sz_row) * G;
-  const uint16_t* __restrict__ zsrc = a.zero + ((size_t)e * a.R + sz_row) * G;
+  const _Float16* stab = reinterpret_cast<const _Float16*>(sztab);
+  const _Float16* ztab = stab + kRowsPerBlock * G;
 
-  uint4 xr[4];
-  uint32_t sr = 0, zr = 0;
-  auto stage_load = [&](int c) {
-    const int k0 = c * kStageK + st_seg * 32;
-    if (xsrc != nullptr && k0 < a.K) {
+  // Issue the loads of stage c into ring slot `slot`.  Chunks past the last group (odd G)
+  // re-read group 0 of their row; compute never uses them.
+  auto dma = [&](int c, int slot) {
+    char* st = lds + slot * kStageBytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xr[i] = *reinterpret_cast<const uint4*>(xsrc + c * kStageK + 8 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xr[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kWLoads; ++i) {
+      int byte = c * kWRowBytes + wchunk[i] * 16;
+      if ((byte >> 5) >= G) byte &= 31;
+      __builtin_amdgcn_global_load_lds(wsrc[i] + byte, st + wave * kWWaveBytes + i * 1024, 16, 0, 0);
     }
-    const int g0 = c * kStageGroups + sz_gp;
-    const uint32_t s0 = g0 < G ? ssrc[g0] : 0u, s1 = g0 + 1 < G ? ssrc[g0 + 1] : 0u;
-    const uint32_t z0 = g0 < G ? zsrc[g0] : 0u, z1 = g0 + 1 < G ? zsrc[g0 + 1] : 0u;
-    sr = s0 | (s1 << 16);
-    zr = z0 | (z1 << 16);
-  };
-  auto stage_store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = GATED ? permute8(xr[i]) : xr[i];
-      *reinterpret_cast<uint4*>(&xs[buf][st_m][st_seg * 32 + 8 * i]) = v;
-    }
-    *reinterpret_cast<uint32_t*>(&szs[buf][0][sz_r][sz_gp]) = sr;
-    *reinterpret_cast<uint32_t*>(&szs[buf][1][sz_r][sz_gp]) = zr;
-  };
-
-  uint2 nA0[kStageGroups], nB0[kStageGroups], nA1[kStageGroups], nB1[kStageGroups];
-  auto nib_load = [&](int c, uint2 (&na)[kStageGroups], uint2 (&nb)[kStageGroups]) {
-#pragma unroll
-    for (int gl = 0; gl < kStageGroups; ++gl) {
-      const int g = c * kStageGroups + gl;
-      if (g < G) {
-        na[gl] = *reinterpret_cast<const uint2*>(qA + g * 32);
-        nb[gl] = *reinterpret_cast<const uint2*>(qB + g * 32);
-      } else {
-        na[gl] = make_uint2(0, 0);
-        nb[gl] = make_uint2(0, 0);
-      }
+    for (int i = 0; i < kXLoads; ++i) {
+      int col = c * kStageK + xchunk[i] * 8;
+      if (col >= a.K) col &= 63;
+      __builtin_amdgcn_global_load_lds(xsrc[i] + col, st + kWBytes + (wave * kXLoads + i) * 1024, 16,
+                                       0, 0);
     }
   };
 
-  float4_t totA[2], totB[2];
+  float4_t totA[NMT], totB[NMT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < NMT; ++mt) {
     totA[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
     totB[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
   const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int c, int buf, const uint2 (&na)[kStageGroups], const uint2 (&nb)[kStageGroups]) {
-    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-    const half4_t sA = *reinterpret_cast<const half4_t*>(&szs[buf][0][wave * 32 + n][0]);
-    const half4_t zA = *reinterpret_cast<const half4_t*>(&szs[buf][1][wave * 32 + n][0]);
-    const half4_t sB = *reinterpret_cast<const half4_t*>(&szs[buf][0][wave * 32 + 16 + n][0]);
-    const half4_t zB = *reinterpret_cast<const half4_t*>(&szs[buf][1][wave * 32 + 16 + n][0]);
+  auto compute = [&](int c, int slot) {
+    const char* st = lds + slot * kStageBytes;
+    const char* wbase = st + wave * kWWaveBytes;
+    const char* xbase = st + kWBytes;
 #pragma unroll
-    for (int gl = 0; gl < kStageGroups; ++gl) {
-      if (c * kStageGroups + gl >= G) break;
-      const _Float16 za = zA[gl], zb = zB[gl];
-      const half8_t bA0 = dequant8(na[gl].x, -((_Float16)1024.f + za), -((_Float16)64.f + za));
-      const half8_t bA1 = dequant8(na[gl].y, -((_Float16)1024.f + za), -((_Float16)64.f + za));
-      const half8_t bB0 = dequant8(nb[gl].x, -((_Float16)1024.f + zb), -((_Float16)64.f + zb));
-      const half8_t bB1 = dequant8(nb[gl].y, -((_Float16)1024.f + zb), -((_Float16)64.f + zb));
-      const float fsA = (float)sA[gl], fsB = (float)sB[gl];
+    for (int gl = 0; gl < kSG; ++gl) {
+      const int g = c * kSG + gl;
+      if (g >= G) break;
+      const int chunk = 2 * gl + (kb >> 1);
+      const int sw = wswz(n);
+      const u32x2_t wa = *reinterpret_cast<const u32x2_t*>(
+          wbase + n * kWRowBytes + ((chunk ^ sw) << 4) + ((kb & 1) << 3));
+      const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(
+          wbase + (16 + n) * kWRowBytes + ((chunk ^ sw) << 4) + ((kb & 1) << 3));
+      const _Float16 za = ztab[slotA * G + g], zb = ztab[slotB * G + g];
+      const float fsA = (float)stab[slotA * G + g], fsB = (float)stab[slotB * G + g];
+      const _Float16 za1 = -((_Float16)1024.f + za), za2 = -((_Float16)64.f + za);
+      const _Float16 zb1 = -((_Float16)1024.f + zb), zb2 = -((_Float16)64.f + zb);
+      const half8_t bA0 = dequant8(wa[0], za1, za2);
+      const half8_t bA1 = dequant8(wa[1], za1, za2);
+      const half8_t bB0 = dequant8(wb[0], zb1, zb2);
+      const half8_t bB1 = dequant8(wb[1], zb1, zb2);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        if (mt < nMT) {
-          const _Float16* xrow = &xs[buf][mt * 16 + n][gl * 64 + kb * 16];
-          const half8_t a0 = *reinterpret_cast<const half8_t*>(xrow);
-          const half8_t a1 = *reinterpret_cast<const half8_t*>(xrow + 8);
-          float4_t accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bA0, zero4, 0, 0, 0);
-          accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bA1, accA, 0, 0, 0);
-          float4_t accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bB0, zero4, 0, 0, 0);
-          accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bB1, accB, 0, 0, 0);
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int m = mt * 16 + n;
+        const char* xrow = xbase + m * kXRowBytes;
+        const int c8 = gl * 8 + kb * 2;                      // 8-half chunk of step 0
+        u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 0) ^ xswz(m)) << 4));
+        u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 1) ^ xswz(m)) << 4));
+        if (GATED) {
+          v0 = permute8(v0);
+          v1 = permute8(v1);
+        }
+        const half8_t a0 = __builtin_bit_cast(half8_t, v0);
+        const half8_t a1 = __builtin_bit_cast(half8_t, v1);
+        float4_t accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bA0, zero4, 0, 0, 0);
+        accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bA1, accA, 0, 0, 0);
+        float4_t accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bB0, zero4, 0, 0, 0);
+        accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bB1, accB, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            totA[mt][r] = fmaf(fsA, accA[r], totA[mt][r]);
-            totB[mt][r] = fmaf(fsB, accB[r], totB[mt][r]);
-          }
+        for (int r = 0; r < 4; ++r) {
+          totA[mt][r] = fmaf(fsA, accA[r], totA[mt][r]);
+          totB[mt][r] = fmaf(fsB, accB[r], totB[mt][r]);
         }
       }
     }
   };
 
-  // Prologue: stage 0 into LDS buffer 0, its packed bytes into registers set 0.
-  stage_load(0);
-  nib_load(0, nA0, nB0);
-  stage_store(0);
-  __syncthreads();
-  for (int c = 0; c < NS; c += 2) {
-    // even stage: registers set 0, LDS buffer 0
-    if (c + 1 < NS) {
-      stage_load(c + 1);
-      nib_load(c + 1, nA1, nB1);
+  // Prologue: the first kDepth stages in flight (stages past the end re-read the last one).
+#pragma unroll
+  for (int s = 0; s < kDepth; ++s) dma(min(s, NS - 1), s);
+  // Every stage issues the loads of stage cc + kDepth, also past the end (re-reading the last
+  // stage, an L2 hit, into a ring slot nobody reads), so the number of loads issued after a
+  // stage's own is always kLoads * (kDepth - 1).  Loads complete in order, so waiting down to
+  // that many outstanding completes the stage's loads (and the table copy issued before them);
+  // the barrier then publishes every wave's loads to the block.
+  for (int c = 0; c < NS; c += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {   // unrolled so every ring slot is a constant
+      const int cc = c + u;
+      if (cc >= NS) break;
+      wait_vmcnt<kLoads * (kDepth - 1)>();
+      lds_barrier();
+      dma(min(cc + kDepth, NS - 1), (u + kDepth) % kRing);
+      compute(cc, u);
     }
-    compute(c, 0, nA0, nB0);
-    if (c + 1 < NS) stage_store(1);
-    __syncthreads();
-    if (c + 1 >= NS) break;
-    // odd stage: registers set 1, LDS buffer 1
-    if (c + 2 < NS) {
-      stage_load(c + 2);
-      nib_load(c + 2, nA0, nB0);
-    }
-    compute(c + 1, 1, nA1, nB1);
-    if (c + 2 < NS) stage_store(0);
-    __syncthreads();
   }
+  wait_vmcnt<0>();   // no LDS write may still be in flight when the block ends
 
   // Epilogue: D lane layout = tokens 4kb..4kb+3 of weight row n.
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    if (mt >= nMT) break;
+  for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mt * 16 + kb * 4 + r;
@@ -284,6 +350,27 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(GemmArgs a) {
   }
 }
 
+template <bool GATED>
+__global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int b = blockIdx.x;
+  const int local = b / kXcds;
+  const int item = (local / a.tiles) * kXcds + (b % kXcds);
+  const int tile = local % a.tiles;
+  if (item >= a.items[0]) return;
+  const int e = a.items[1 + 3 * item];
+  const int pos0 = a.items[2 + 3 * item];
+  const int mcount = a.items[3 + 3 * item];
+  if (kItemTokens > 16 && mcount > 16)
+    gemm_item<GATED, (kItemTokens > 16 ? 2 : 1)>(a, lds, e, pos0, mcount, tile);
+  else
+    gemm_item<GATED, 1>(a, lds, e, pos0, mcount, tile);
+}
+
+int grid_blocks(int max_items, int tiles) {
+  return ((max_items + kXcds - 1) / kXcds) * kXcds * tiles;
+}
+
 }  // namespace
 
 hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, int top_k, int T,
@@ -296,6 +383,7 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.R = 2 * d_ff;
   a.d_ff = d_ff;
   a.top_k = top_k;
+  a.tiles = d_ff / 64;
   a.act = x;
   a.perm = ws.perm;
   a.items = ws.items;
@@ -304,8 +392,8 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.out_ld = d_ff;
   (void)E;
   (void)T;
-  hipLaunchKernelGGL(w4a16_gemm_kernel<true>, dim3(d_ff / 64, ws.max_items), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL(w4a16_gemm_kernel<true>, dim3(grid_blocks(ws.max_items, a.tiles)),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -319,6 +407,7 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
   a.R = d_model;
   a.d_ff = d_ff;
   a.top_k = top_k;
+  a.tiles = d_model / kRowsPerBlock;
   a.act = ws.h;
   a.perm = ws.perm;
   a.items = ws.items;
@@ -327,7 +416,7 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
   a.out_ld = d_model;
   (void)E;
   (void)T;
-  hipLaunchKernelGGL(w4a16_gemm_kernel<false>, dim3(d_model / kRowsPerBlock, ws.max_items),
+  hipLaunchKernelGGL(w4a16_gemm_kernel<false>, dim3(grid_blocks(ws.max_items, a.tiles)),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -81,7 +81,7 @@ typedef enum {
  * scale[n][k/g].  Zero-points are the uint4 code of the zero (an integer 0..15 held
  * in fp16); the GEMM subtracts them exactly in fp16, a non-integer zero-point is
  * rounded to the nearest integer first.
- * Supported: group_size == 64, d_model % 128 == 0, d_ff % 64 == 0.
+ * Supported: group_size == 64, d_model % 128 == 0, d_ff % 64 == 0, d_model and d_ff <= 4096.
  */
 typedef struct bd_moe_weights {
   int32_t num_experts; /* E, 1..256          */
