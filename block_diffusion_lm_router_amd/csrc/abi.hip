@@ -84,7 +84,7 @@ const char* bd_status_string(int status) {
 
 size_t bd_moe_workspace_size(int T, const bd_moe_weights* w) {
   if (check_moe_shape(w, T) != BD_OK) return 0;
-  return bd::moe_workspace_bytes(T, w->num_experts, w->top_k, w->d_ff);
+  return bd::moe_workspace_bytes(T, w->num_experts, w->top_k, w->d_model, w->d_ff);
 }
 
 int moe_route_topk(const bd_moe_weights* w, int T, const float* router_logits, int32_t* topk_ids,
@@ -97,7 +97,7 @@ int moe_route_topk(const bd_moe_weights* w, int T, const float* router_logits, i
   st = check_workspace(workspace, workspace_bytes, bd_moe_workspace_size(T, w));
   if (st != BD_OK) return st;
   const bd::MoeWorkspace ws =
-      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_ff);
+      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_model, w->d_ff);
   return to_status(bd::launch_route(router_logits, T, w->num_experts, w->top_k, topk_ids,
                                     topk_weights, ws, as_stream(stream)));
 }
@@ -112,7 +112,7 @@ int moe_w4a16_gate_up(const bd_moe_weights* w, int T, const uint16_t* x, void* w
   st = check_workspace(workspace, workspace_bytes, bd_moe_workspace_size(T, w));
   if (st != BD_OK) return st;
   const bd::MoeWorkspace ws =
-      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_ff);
+      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_model, w->d_ff);
   return to_status(bd::launch_gate_up(gate_up_of(w), w->num_experts, w->d_model, w->d_ff,
                                       w->top_k, T, x, ws, as_stream(stream)));
 }
@@ -127,7 +127,7 @@ int moe_w4a16_down(const bd_moe_weights* w, int T, float* expert_out, void* work
   st = check_workspace(workspace, workspace_bytes, bd_moe_workspace_size(T, w));
   if (st != BD_OK) return st;
   const bd::MoeWorkspace ws =
-      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_ff);
+      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_model, w->d_ff);
   return to_status(bd::launch_down(down_of(w), w->num_experts, w->d_model, w->d_ff, w->top_k, T,
                                    expert_out, ws, as_stream(stream)));
 }
@@ -146,7 +146,7 @@ int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x, const float
   st = check_workspace(workspace, workspace_bytes, bd_moe_workspace_size(T, w));
   if (st != BD_OK) return st;
   const bd::MoeWorkspace ws =
-      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_ff);
+      bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_model, w->d_ff);
   hipStream_t s = as_stream(stream);
   hipError_t err = bd::launch_route(router_logits, T, w->num_experts, w->top_k, topk_ids,
                                     topk_weights, ws, s);

@@ -31,13 +31,14 @@ struct MoeWorkspace {
   int32_t* offsets;  // [E + 1] bucket starts
   int32_t* items;    // [0] = count, then (expert, first bucket position, tokens) triples
   int32_t* perm;     // [T * k] assignment index t*k + j at each bucket position
-  uint16_t* h;       // [T * k][d_ff] fp16 GeGLU activations, bucket order
+  uint16_t* h;       // [T * k][d_ff] fp16 GeGLU activations, bucket order, k-permuted
+  uint16_t* xp;      // [T][d_model] fp16 activations with k permuted within blocks of 8
   int max_items;
 };
 
 int moe_max_items(int T, int E, int k);
-size_t moe_workspace_bytes(int T, int E, int k, int d_ff);
-MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_ff);
+size_t moe_workspace_bytes(int T, int E, int k, int d_model, int d_ff);
+MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_model, int d_ff);
 
 hipError_t launch_route(const float* router_logits, int T, int E, int k, int32_t* topk_ids,
                         float* topk_weights, const MoeWorkspace& ws, hipStream_t stream);

@@ -178,13 +178,13 @@ int moe_max_items(int T, int E, int k) {
   return A / kItemTokens + (E < A ? E : A);
 }
 
-size_t moe_workspace_bytes(int T, int E, int k, int d_ff) {
+size_t moe_workspace_bytes(int T, int E, int k, int d_model, int d_ff) {
   const size_t A = (size_t)T * k;
   return align_up((size_t)(E + 1) * 4) + align_up((size_t)(1 + 3 * moe_max_items(T, E, k)) * 4) +
-         align_up(A * 4) + align_up(A * (size_t)d_ff * 2);
+         align_up(A * 4) + align_up(A * (size_t)d_ff * 2) + align_up((size_t)T * d_model * 2);
 }
 
-MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_ff) {
+MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_model, int d_ff) {
   const size_t A = (size_t)T * k;
   char* p = reinterpret_cast<char*>(base);
   MoeWorkspace ws;
@@ -196,7 +196,9 @@ MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_ff) {
   ws.perm = reinterpret_cast<int32_t*>(p);
   p += align_up(A * 4);
   ws.h = reinterpret_cast<uint16_t*>(p);
-  (void)d_ff;
+  p += align_up(A * (size_t)d_ff * 2);
+  ws.xp = reinterpret_cast<uint16_t*>(p);
+  (void)d_model;
   return ws;
 }
 

@@ -8,8 +8,10 @@
 // Work decomposition.  A block owns one work item (an expert and up to 32 of its routed
 // tokens) and one tile of 128 weight rows: gate/up takes 64 gate rows and the 64 up rows
 // that pair with them, so the GeGLU product is formed in registers; down takes 128
-// consecutive output rows.  Each wave owns two 16-row sets.  Every packed byte of the
-// block's rows crosses HBM once per item.
+// consecutive output rows.  The 8 waves form 4 row groups of 32 rows (two 16-row sets) times
+// 2 parities: wave (g, p) contracts the 64-groups of parity p of every stage for row group g,
+// and the two parities' fp32 sums are added in a fixed order at the end.  Every packed byte of
+// the block's rows crosses HBM once per item.
 //
 // Block order.  Consecutive block ids are dispatched round-robin over the 8 XCDs.  Block b
 // maps to XCD b % 8, and the blocks an XCD receives walk through all row tiles of one item
@@ -35,9 +37,9 @@
 // masks 0x000F000F and 0x00F000F0 (and the same after >> 8) yield the pairs (k0,k4),
 // (16k1,16k5), (k2,k6), (16k3,16k7).  One packed add of -(1024 + z) or one packed fma
 // by 1/16 then -(64 + z) turns each pair into the exact fp16 values q - z.  The k-order
-// of a lane's 8 weights is therefore (0,4,1,5,2,6,3,7); activation fragments are put in
-// the same order (gate/up permutes x after the LDS read; down's h is stored permuted by
-// the gate/up epilogue), so the contraction is unchanged.  The 64-group partial sums come
+// of a lane's 8 weights is therefore (0,4,1,5,2,6,3,7); the activations are stored in the same
+// order (x by a small permutation pass before gate/up, h by the gate/up epilogue), so the
+// contraction is unchanged.  The 64-group partial sums come
 // out of MFMA in fp32 and are scaled by that group's fp16 scale in fp32.
 
 #include "bd_device.hpp"
@@ -54,26 +56,32 @@ namespace {
 #define BD_DEPTH 2
 #endif
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                        // 8 waves: 4 row groups x 2 group parities
+constexpr int kRowGroups = 4;                        // 32 weight rows each
 constexpr int kRowsPerBlock = 128;
 constexpr int kXcds = 8;
 constexpr int kSG = BD_STAGE_GROUPS;                 // 64-groups per stage (2 or 4)
-constexpr int kDepth = BD_DEPTH;                     // stages in flight ahead of compute
-constexpr int kRing = kDepth + 1;                    // stage buffers
+constexpr int kRing = BD_DEPTH + 1;                 // stage buffers at the largest item size
 constexpr int kStageK = kSG * 64;
 constexpr int kWRowBytes = kSG * 32;                 // packed bytes of one row per stage
 constexpr int kWChunks = kWRowBytes / 16;            // 16-byte chunks per row per stage
 constexpr int kWRowsPerLoad = 1024 / kWRowBytes;     // rows covered by one wave-wide load
 constexpr int kWLoads = 32 / kWRowsPerLoad;          // loads per wave per stage (32 rows)
 constexpr int kWWaveBytes = 32 * kWRowBytes;
-constexpr int kWBytes = 4 * kWWaveBytes;
-constexpr int kXRows = kItemTokens;                  // activation rows per item (<= 32)
+constexpr int kWBytes = kRowGroups * kWWaveBytes;
 constexpr int kXRowBytes = kStageK * 2;
 constexpr int kXChunks = kXRowBytes / 16;
 constexpr int kXRowsPerLoad = 1024 / kXRowBytes;
-constexpr int kXBytes = kXRows * kXRowBytes;
-constexpr int kStageBytes = kWBytes + kXBytes;
-constexpr int kRingBytes = kRing * kStageBytes;
+// The ring holds kRingBytes.  A stage is the weight tile plus NMT*16 activation rows, so items
+// of at most 16 tokens fit one more stage in flight than items of up to 32.
+constexpr int kRingBytes = kRing * (kWBytes + kItemTokens * kXRowBytes);
+template <int NMT>
+struct Ring {
+  static constexpr int kXBytes = NMT * 16 * kXRowBytes;
+  static constexpr int kStageBytes = kWBytes + kXBytes;
+  static constexpr int kSlots = kRingBytes / kStageBytes;
+  static constexpr int kDepth = kSlots - 1;          // stages in flight ahead of compute
+};
 // Scale and zero-point tables of the block's 128 rows for the whole contraction dim, loaded
 // once per block: [2 arrays][128 rows][G] halves.  G is at most kMaxGroups.
 constexpr int kMaxGroups = 64;
@@ -81,6 +89,7 @@ constexpr int kSZTableBytes = 2 * kRowsPerBlock * kMaxGroups * 2;
 constexpr int kLdsBytes = kRingBytes + kSZTableBytes;
 static_assert(kItemTokens == 16 || kItemTokens == 32, "work items hold at most 32 tokens");
 static_assert(kWChunks * 16 == kWRowBytes && kXChunks >= 16, "stage geometry");
+static_assert(kWLoads == 2 && kSG % 2 == 0, "one weight load per wave per stage");
 
 // Row swizzles: rows that alias in the 64 LDS banks get different chunk rotations.
 __device__ __forceinline__ int wswz(int r) { return (r / (64 / (kWRowBytes / 4))) & (kWChunks - 1); }
@@ -95,7 +104,7 @@ struct GemmArgs {
   int d_ff;                // gate/up: first up row
   int top_k;
   int tiles;               // row tiles per item
-  const uint16_t* act;     // gate/up: x [T][K]; down: h [T*k][K] (bucket order, permuted k)
+  const uint16_t* act;     // gate/up: x [T][K]; down: h [T*k][K] (bucket order); both k-permuted
   const int32_t* perm;     // bucket position -> assignment t*k + j
   const int32_t* items;    // [0] = count, then (expert, first position, tokens)
   uint16_t* h_out;         // gate/up output [T*k][d_ff]
@@ -103,8 +112,22 @@ struct GemmArgs {
   int out_ld;
 };
 
-__device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 zc1, _Float16 zc2) {
-  const uint32_t kLo = 0x000F000Fu, kHi = 0x00F000F0u, kMagic = 0x64006400u;
+// The masks and the magic exponent are passed in registers (see DequantConsts) so that each
+// (w & mask) | magic is one v_and_or_b32.
+struct DequantConsts {
+  uint32_t lo, hi, magic;
+};
+__device__ __forceinline__ DequantConsts dequant_consts() {
+  DequantConsts k;
+  asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(k.lo));
+  asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(k.hi));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.magic));
+  return k;
+}
+
+__device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 zc1, _Float16 zc2,
+                                            const DequantConsts& k) {
+  const uint32_t kLo = k.lo, kHi = k.hi, kMagic = k.magic;
   const uint32_t a = (w & kLo) | kMagic;
   const uint32_t b = (w & kHi) | kMagic;
   const uint32_t w8 = w >> 8;
@@ -165,46 +188,47 @@ __device__ __forceinline__ void lds_barrier() {
 template <bool GATED, int NMT>
 __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, int pos0,
                                           int mcount, int tile) {
-  constexpr int kXLoads = (NMT * 16) / kXRowsPerLoad / 4;   // activation loads per wave per stage
-  constexpr int kLoads = kWLoads + kXLoads;                  // loads per wave per stage
-  static_assert(kXLoads >= 1 && kLoads * kDepth < 64, "load count");
+  // Per stage the block issues 2 weight loads per row group and 4*NMT activation loads (4 rows
+  // each).  Wave (rg, par) issues the weight load of set par of row group rg and activation
+  // load rg + 4*par if that one exists.
+  constexpr int kXLoadsBlock = (NMT * 16) / kXRowsPerLoad;
+  static_assert(kXLoadsBlock == 4 || kXLoadsBlock == 8, "activation loads per stage");
+  constexpr int kStageBytes = Ring<NMT>::kStageBytes;
+  constexpr int kSlots = Ring<NMT>::kSlots;
+  constexpr int kDepth = Ring<NMT>::kDepth;
+  static_assert(kDepth >= 1 && 2 * kDepth < 64, "ring depth");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+  const int rg = wave & 3;                 // row group: 32 weight rows
+  const int par = wave >> 2;               // which 64-groups of each stage this wave contracts
+  const bool xload = rg + 4 * par < kXLoadsBlock;
   const int n = lane & 15;
   const int kb = lane >> 4;
   const int G = a.K >> 6;
   const int NS = (G + kSG - 1) / kSG;
   const size_t rowbytes = (size_t)(a.K >> 1);
+  const DequantConsts dq = dequant_consts();
 
-  // Weight rows of this wave: set A = rows rA0.., set B = rows rB0.. (16 each).
-  const int rA0 = GATED ? tile * 64 + wave * 16 : tile * kRowsPerBlock + wave * 32;
+  // Weight rows of this row group: set A = rows rA0.., set B = rows rB0.. (16 each).
+  const int rA0 = GATED ? tile * 64 + rg * 16 : tile * kRowsPerBlock + rg * 32;
   const int rB0 = GATED ? a.d_ff + rA0 : rA0 + 16;
-  // Their slots in the scale/zero table.
-  const int slotA = GATED ? wave * 16 + n : wave * 32 + n;
-  const int slotB = GATED ? 64 + wave * 16 + n : wave * 32 + 16 + n;
-  // Weight loads: load i covers wave rows i*kWRowsPerLoad..; lane -> (row, chunk slot), the
-  // slot holding global chunk slot ^ wswz(row).
-  const uint8_t* wsrc[kWLoads];
-  int wchunk[kWLoads];
-#pragma unroll
-  for (int i = 0; i < kWLoads; ++i) {
-    const int r = i * kWRowsPerLoad + lane / kWChunks;
-    const int grow = r < 16 ? rA0 + r : rB0 + (r - 16);
-    wsrc[i] = a.q + ((size_t)e * a.R + grow) * rowbytes;
-    wchunk[i] = (lane % kWChunks) ^ wswz(r & 15);
-  }
-  // Activation loads: load i of this wave covers rows (wave*kXLoads + i)*kXRowsPerLoad..
-  const uint16_t* xsrc[kXLoads];
-  int xchunk[kXLoads];
-#pragma unroll
-  for (int i = 0; i < kXLoads; ++i) {
-    const int m = (wave * kXLoads + i) * kXRowsPerLoad + lane / kXChunks;
-    const int mm = m < mcount ? m : mcount - 1;              // padding rows re-read a valid row
+  const int slotA = GATED ? rg * 16 + n : rg * 32 + n;         // rows in the scale table
+  const int slotB = GATED ? 64 + rg * 16 + n : rg * 32 + 16 + n;
+  // Weight load: rows of set `par`; lane -> (row, chunk slot), the slot holding global chunk
+  // slot ^ wswz(row).
+  const int wr = lane / kWChunks;                               // 0..15
+  const uint8_t* wsrc = a.q + ((size_t)e * a.R + (par ? rB0 : rA0) + wr) * rowbytes;
+  const int wchunk = (lane % kWChunks) ^ wswz(wr);
+  // Activation load rg + 4*par: rows (rg + 4*par)*4 + lane/16.
+  const int xm = (rg + 4 * par) * kXRowsPerLoad + lane / kXChunks;
+  const uint16_t* xsrc;
+  {
+    const int mm = min(xm, mcount - 1);                         // padding rows re-read a valid row
     const int row = GATED ? a.perm[pos0 + mm] / a.top_k : pos0 + mm;
-    xsrc[i] = a.act + (size_t)row * a.K;
-    xchunk[i] = (lane % kXChunks) ^ xswz(m);
+    xsrc = a.act + (size_t)row * a.K;   // both activations are stored k-permuted
   }
+  const int xchunk = (lane % kXChunks) ^ xswz(xm);
 
   // Scale / zero-point table, copied once: the block's rows form contiguous 16-byte aligned
   // ranges of each array (gate/up: 64 gate rows and 64 up rows; down: 128 rows), laid out in
@@ -217,7 +241,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, i
     const int rchunks = rows * G * 2 / 16;
     const int ranges = GATED ? 4 : 2;
     const int total = ranges * rchunks;
-    for (int q0 = wave * 64; q0 < total; q0 += 4 * 64) {
+    for (int q0 = wave * 64; q0 < total; q0 += kThreads) {
       const int q = min(q0 + lane, total - 1);
       const int rng = q / rchunks;
       const int arr = GATED ? (rng >> 1) : rng;
@@ -231,22 +255,17 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, i
   const _Float16* stab = reinterpret_cast<const _Float16*>(sztab);
   const _Float16* ztab = stab + kRowsPerBlock * G;
 
-  // Issue the loads of stage c into ring slot `slot`.  Chunks past the last group (odd G)
-  // re-read group 0 of their row; compute never uses them.
+  // Issue this wave's loads of stage c into ring slot `slot`.  Chunks past the last group
+  // (odd G) re-read group 0 of their row; compute never uses them.
   auto dma = [&](int c, int slot) {
     char* st = lds + slot * kStageBytes;
-#pragma unroll
-    for (int i = 0; i < kWLoads; ++i) {
-      int byte = c * kWRowBytes + wchunk[i] * 16;
-      if ((byte >> 5) >= G) byte &= 31;
-      __builtin_amdgcn_global_load_lds(wsrc[i] + byte, st + wave * kWWaveBytes + i * 1024, 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < kXLoads; ++i) {
-      int col = c * kStageK + xchunk[i] * 8;
+    int byte = c * kWRowBytes + wchunk * 16;
+    if ((byte >> 5) >= G) byte &= 31;
+    __builtin_amdgcn_global_load_lds(wsrc + byte, st + rg * kWWaveBytes + par * 1024, 16, 0, 0);
+    if (xload) {
+      int col = c * kStageK + xchunk * 8;
       if (col >= a.K) col &= 63;
-      __builtin_amdgcn_global_load_lds(xsrc[i] + col, st + kWBytes + (wave * kXLoads + i) * 1024, 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(xsrc + col, st + kWBytes + (rg + 4 * par) * 1024, 16, 0, 0);
     }
   };
 
@@ -260,10 +279,11 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, i
 
   auto compute = [&](int c, int slot) {
     const char* st = lds + slot * kStageBytes;
-    const char* wbase = st + wave * kWWaveBytes;
+    const char* wbase = st + rg * kWWaveBytes;
     const char* xbase = st + kWBytes;
 #pragma unroll
-    for (int gl = 0; gl < kSG; ++gl) {
+    for (int gq = 0; gq < kSG / 2; ++gq) {
+      const int gl = 2 * gq + par;
       const int g = c * kSG + gl;
       if (g >= G) break;
       const int chunk = 2 * gl + (kb >> 1);
@@ -276,21 +296,17 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, i
       const float fsA = (float)stab[slotA * G + g], fsB = (float)stab[slotB * G + g];
       const _Float16 za1 = -((_Float16)1024.f + za), za2 = -((_Float16)64.f + za);
       const _Float16 zb1 = -((_Float16)1024.f + zb), zb2 = -((_Float16)64.f + zb);
-      const half8_t bA0 = dequant8(wa[0], za1, za2);
-      const half8_t bA1 = dequant8(wa[1], za1, za2);
-      const half8_t bB0 = dequant8(wb[0], zb1, zb2);
-      const half8_t bB1 = dequant8(wb[1], zb1, zb2);
+      const half8_t bA0 = dequant8(wa[0], za1, za2, dq);
+      const half8_t bA1 = dequant8(wa[1], za1, za2, dq);
+      const half8_t bB0 = dequant8(wb[0], zb1, zb2, dq);
+      const half8_t bB1 = dequant8(wb[1], zb1, zb2, dq);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int m = mt * 16 + n;
         const char* xrow = xbase + m * kXRowBytes;
         const int c8 = gl * 8 + kb * 2;                      // 8-half chunk of step 0
-        u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 0) ^ xswz(m)) << 4));
-        u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 1) ^ xswz(m)) << 4));
-        if (GATED) {
-          v0 = permute8(v0);
-          v1 = permute8(v1);
-        }
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 0) ^ xswz(m)) << 4));
+        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 1) ^ xswz(m)) << 4));
         const half8_t a0 = __builtin_bit_cast(half8_t, v0);
         const half8_t a1 = __builtin_bit_cast(half8_t, v1);
         float4_t accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bA0, zero4, 0, 0, 0);
@@ -310,22 +326,48 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, i
 #pragma unroll
   for (int s = 0; s < kDepth; ++s) dma(min(s, NS - 1), s);
   // Every stage issues the loads of stage cc + kDepth, also past the end (re-reading the last
-  // stage, an L2 hit, into a ring slot nobody reads), so the number of loads issued after a
-  // stage's own is always kLoads * (kDepth - 1).  Loads complete in order, so waiting down to
-  // that many outstanding completes the stage's loads (and the table copy issued before them);
-  // the barrier then publishes every wave's loads to the block.
-  for (int c = 0; c < NS; c += kRing) {
+  // stage, an L2 hit, into a ring slot nobody reads), so the number of loads this wave issued
+  // after a stage's own is always its per-stage count times kDepth - 1.  Loads complete in
+  // order, so waiting down to that many outstanding completes the stage's loads (and the table
+  // copy issued before them); the barrier then publishes every wave's loads to the block.
+  for (int c = 0; c < NS; c += kSlots) {
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) {   // unrolled so every ring slot is a constant
+    for (int u = 0; u < kSlots; ++u) {  // unrolled so every ring slot is a constant
       const int cc = c + u;
       if (cc >= NS) break;
-      wait_vmcnt<kLoads * (kDepth - 1)>();
+      if (xload)
+        wait_vmcnt<2 * (kDepth - 1)>();
+      else
+        wait_vmcnt<1 * (kDepth - 1)>();
       lds_barrier();
-      dma(min(cc + kDepth, NS - 1), (u + kDepth) % kRing);
+      dma(min(cc + kDepth, NS - 1), (u + kDepth) % kSlots);
       compute(cc, u);
     }
   }
   wait_vmcnt<0>();   // no LDS write may still be in flight when the block ends
+
+  // Reduce the two group parities of each row group in a fixed order (par 0 + par 1), in the
+  // ring's LDS, which no load targets any more.
+  lds_barrier();
+  float* red = reinterpret_cast<float*>(lds) + (rg * 64 + lane) * (NMT * 8);
+  if (par == 1) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        red[mt * 8 + r] = totA[mt][r];
+        red[mt * 8 + 4 + r] = totB[mt][r];
+      }
+  }
+  lds_barrier();
+  if (par == 1) return;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      totA[mt][r] += red[mt * 8 + r];
+      totB[mt][r] += red[mt * 8 + 4 + r];
+    }
 
   // Epilogue: D lane layout = tokens 4kb..4kb+3 of weight row n.
 #pragma unroll
@@ -336,13 +378,13 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, i
       if (m >= mcount) continue;
       if (GATED) {
         const float hv = gelu_tanh(totA[mt][r]) * totB[mt][r];
-        const int col = tile * 64 + wave * 16 + n;
+        const int col = tile * 64 + rg * 16 + n;
         const int pcol = (col & ~7) | ((col & 3) << 1) | ((col >> 2) & 1);
         const _Float16 h16 = (_Float16)hv;
         a.h_out[(size_t)(pos0 + m) * a.d_ff + pcol] = __builtin_bit_cast(uint16_t, h16);
       } else {
         const int slot = a.perm[pos0 + m];
-        const int row = tile * kRowsPerBlock + wave * 32 + n;
+        const int row = tile * kRowsPerBlock + rg * 32 + n;
         a.o_out[(size_t)slot * a.out_ld + row] = totA[mt][r];
         a.o_out[(size_t)slot * a.out_ld + row + 16] = totB[mt][r];
       }
@@ -367,6 +409,13 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(GemmArgs a) {
     gemm_item<GATED, 1>(a, lds, e, pos0, mcount, tile);
 }
 
+// x [T][d] -> xp [T][d] with every 8 consecutive halves reordered to (0,4,1,5,2,6,3,7).
+__global__ __launch_bounds__(256) void permute_x_kernel(const u32x4_t* __restrict__ x,
+                                                        u32x4_t* __restrict__ xp, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) xp[i] = permute8(x[i]);
+}
+
 int grid_blocks(int max_items, int tiles) {
   return ((max_items + kXcds - 1) / kXcds) * kXcds * tiles;
 }
@@ -384,14 +433,18 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.d_ff = d_ff;
   a.top_k = top_k;
   a.tiles = d_ff / 64;
-  a.act = x;
+  a.act = ws.xp;
   a.perm = ws.perm;
   a.items = ws.items;
   a.h_out = ws.h;
   a.o_out = nullptr;
   a.out_ld = d_ff;
   (void)E;
-  (void)T;
+  const int n8 = T * d_model / 8;
+  hipLaunchKernelGGL(permute_x_kernel, dim3((n8 + 255) / 256), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4_t*>(x), reinterpret_cast<u32x4_t*>(ws.xp), n8);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(w4a16_gemm_kernel<true>, dim3(grid_blocks(ws.max_items, a.tiles)),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
