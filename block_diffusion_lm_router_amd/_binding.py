@@ -93,6 +93,37 @@ def _check(status, what):
         raise BdError(f"{what}: {_STATUS.get(status, status)} ({msg})")
 
 
+_binding_calls = False
+
+
+def _invoke(name, *cargs):
+    """Call entry point `name` with marshalled arguments and raise on a non-zero status.
+    Under bind() the call is not made: the arguments are handed back instead."""
+    if _binding_calls:
+        return name, cargs
+    _check(getattr(load(), name)(*cargs), name)
+
+
+def bind(fn, *args, **kwargs):
+    """Marshal the arguments of wrapper `fn` once (pointers, sizes, the current stream) and
+    return a zero-argument callable that launches the entry point with them.  Repeated
+    launches of the same call skip the per-call checks and conversions, which keeps the
+    host ahead of the GPU when a loop issues many short launches."""
+    global _binding_calls
+    _binding_calls = True
+    try:
+        name, cargs = fn(*args, **kwargs)
+    finally:
+        _binding_calls = False
+    raw = getattr(load(), name)
+
+    def call():
+        status = raw(*cargs)
+        if status != 0:
+            _check(status, name)
+    return call
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -151,41 +182,37 @@ def moe_workspace(T, w: MoeWeights, device="cuda"):
 
 def moe_route_topk(w, router_logits, topk_ids, topk_weights, workspace):
     T = router_logits.shape[0]
-    _check(load().moe_route_topk(w.ref(), T, _ptr(router_logits, torch.float32, "router_logits"),
-                                 _ptr(topk_ids, torch.int32, "topk_ids"),
-                                 _ptr(topk_weights, torch.float32, "topk_weights"),
-                                 _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-                                 _stream()), "moe_route_topk")
+    return _invoke("moe_route_topk", w.ref(), T,
+                   _ptr(router_logits, torch.float32, "router_logits"),
+                   _ptr(topk_ids, torch.int32, "topk_ids"),
+                   _ptr(topk_weights, torch.float32, "topk_weights"),
+                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
 
 
 def moe_w4a16_gate_up(w, x, workspace):
-    _check(load().moe_w4a16_gate_up(w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
-                                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-                                    _stream()), "moe_w4a16_gate_up")
+    return _invoke("moe_w4a16_gate_up", w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
+                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
 
 
 def moe_w4a16_down(w, T, expert_out, workspace):
-    _check(load().moe_w4a16_down(w.ref(), T, _ptr(expert_out, torch.float32, "expert_out"),
-                                 _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-                                 _stream()), "moe_w4a16_down")
+    return _invoke("moe_w4a16_down", w.ref(), T, _ptr(expert_out, torch.float32, "expert_out"),
+                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
 
 
 def moe_w4a16_ffn(w, x, router_logits, topk_ids, topk_weights, expert_out, workspace):
-    _check(load().moe_w4a16_ffn(w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
-                                _ptr(router_logits, torch.float32, "router_logits"),
-                                _ptr(topk_ids, torch.int32, "topk_ids"),
-                                _ptr(topk_weights, torch.float32, "topk_weights"),
-                                _ptr(expert_out, torch.float32, "expert_out"),
-                                _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-                                _stream()), "moe_w4a16_ffn")
+    return _invoke("moe_w4a16_ffn", w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
+                   _ptr(router_logits, torch.float32, "router_logits"),
+                   _ptr(topk_ids, torch.int32, "topk_ids"),
+                   _ptr(topk_weights, torch.float32, "topk_weights"),
+                   _ptr(expert_out, torch.float32, "expert_out"),
+                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
 
 
 def moe_combine_fixed_order(expert_out, topk_weights, y):
     T, k, d = expert_out.shape
-    _check(load().moe_combine_fixed_order(_ptr(expert_out, torch.float32, "expert_out"),
-                                          _ptr(topk_weights, torch.float32, "topk_weights"),
-                                          T, k, d, _ptr(y, torch.float16, "y"), _stream()),
-           "moe_combine_fixed_order")
+    return _invoke("moe_combine_fixed_order", _ptr(expert_out, torch.float32, "expert_out"),
+                   _ptr(topk_weights, torch.float32, "topk_weights"), T, k, d,
+                   _ptr(y, torch.float16, "y"), _stream())
 
 
 def sample_workspace_size(P, V):
@@ -202,41 +229,38 @@ def sample_workspace(P, V, device="cuda"):
 def diffusion_sample_entropy(logits, temperature, seed, step, frozen, tokens_out, entropy_out,
                              workspace):
     P, V = logits.shape
-    _check(load().diffusion_sample_entropy(
-        _ptr(logits, torch.float32, "logits"), P, V, float(temperature), int(seed), int(step),
-        _ptr(frozen, torch.uint8, "frozen"), _ptr(tokens_out, torch.int32, "tokens_out"),
-        _ptr(entropy_out, torch.float32, "entropy_out"), _ptr(workspace, torch.uint8, "workspace"),
-        workspace.numel(), _stream()), "diffusion_sample_entropy")
+    return _invoke("diffusion_sample_entropy", _ptr(logits, torch.float32, "logits"), P, V,
+                   float(temperature), int(seed), int(step), _ptr(frozen, torch.uint8, "frozen"),
+                   _ptr(tokens_out, torch.int32, "tokens_out"),
+                   _ptr(entropy_out, torch.float32, "entropy_out"),
+                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
 
 
 def diffusion_accept_entropy_bound(entropy, tokens, bound, frozen, canvas, accept_out,
                                    num_accepted):
     P = entropy.shape[0]
-    _check(load().diffusion_accept_entropy_bound(
-        _ptr(entropy, torch.float32, "entropy"), _ptr(tokens, torch.int32, "tokens"), P,
-        float(bound), _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
-        _ptr(accept_out, torch.uint8, "accept_out"),
-        _ptr(num_accepted, torch.int32, "num_accepted"), _stream()),
-        "diffusion_accept_entropy_bound")
+    return _invoke("diffusion_accept_entropy_bound", _ptr(entropy, torch.float32, "entropy"),
+                   _ptr(tokens, torch.int32, "tokens"), P, float(bound),
+                   _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
+                   _ptr(accept_out, torch.uint8, "accept_out"),
+                   _ptr(num_accepted, torch.int32, "num_accepted"), _stream())
 
 
 def diffusion_sample_step(logits, temperature, entropy_bound, seed, step, frozen, canvas,
                           tokens_out, entropy_out, accept_out, num_accepted, workspace):
     P, V = logits.shape
-    _check(load().diffusion_sample_step(
-        _ptr(logits, torch.float32, "logits"), P, V, float(temperature), float(entropy_bound),
-        int(seed), int(step), _ptr(frozen, torch.uint8, "frozen"),
-        _ptr(canvas, torch.int32, "canvas"), _ptr(tokens_out, torch.int32, "tokens_out"),
-        _ptr(entropy_out, torch.float32, "entropy_out"),
-        _ptr(accept_out, torch.uint8, "accept_out"),
-        _ptr(num_accepted, torch.int32, "num_accepted"),
-        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream()),
-        "diffusion_sample_step")
+    return _invoke("diffusion_sample_step", _ptr(logits, torch.float32, "logits"), P, V,
+                   float(temperature), float(entropy_bound), int(seed), int(step),
+                   _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
+                   _ptr(tokens_out, torch.int32, "tokens_out"),
+                   _ptr(entropy_out, torch.float32, "entropy_out"),
+                   _ptr(accept_out, torch.uint8, "accept_out"),
+                   _ptr(num_accepted, torch.int32, "num_accepted"),
+                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
 
 
 def hbm_copy(src, dst):
     n = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst smaller than src")
-    _check(load().bd_hbm_copy(_ptr(src, None, "src"), _ptr(dst, None, "dst"), n, _stream()),
-           "bd_hbm_copy")
+    return _invoke("bd_hbm_copy", _ptr(src, None, "src"), _ptr(dst, None, "dst"), n, _stream())
