@@ -37,23 +37,25 @@ int check_workspace(const void* ws, size_t have, size_t need) {
 
 int check_gate_up_weights(const bd_moe_weights* w) {
   if (!w->gate_up_q || !w->gate_up_scale || !w->gate_up_zero) return BD_ERR_NULL;
-  if (!aligned16(w->gate_up_q) || !aligned16(w->gate_up_scale) || !aligned16(w->gate_up_zero))
+  if (!aligned16(w->gate_up_q) || !aligned16(w->gate_up_scale) || !aligned16(w->gate_up_zero) ||
+      !aligned16(w->gate_up_sz))
     return BD_ERR_ALIGN;
   return BD_OK;
 }
 
 int check_down_weights(const bd_moe_weights* w) {
   if (!w->down_q || !w->down_scale || !w->down_zero) return BD_ERR_NULL;
-  if (!aligned16(w->down_q) || !aligned16(w->down_scale) || !aligned16(w->down_zero))
+  if (!aligned16(w->down_q) || !aligned16(w->down_scale) || !aligned16(w->down_zero) ||
+      !aligned16(w->down_sz))
     return BD_ERR_ALIGN;
   return BD_OK;
 }
 
 bd::W4A16Matrix gate_up_of(const bd_moe_weights* w) {
-  return bd::W4A16Matrix{w->gate_up_q, w->gate_up_scale, w->gate_up_zero};
+  return bd::W4A16Matrix{w->gate_up_q, w->gate_up_scale, w->gate_up_zero, w->gate_up_sz};
 }
 bd::W4A16Matrix down_of(const bd_moe_weights* w) {
-  return bd::W4A16Matrix{w->down_q, w->down_scale, w->down_zero};
+  return bd::W4A16Matrix{w->down_q, w->down_scale, w->down_zero, w->down_sz};
 }
 
 int check_sample_shape(int P, int V, float temperature) {
@@ -80,6 +82,26 @@ const char* bd_status_string(int status) {
     case BD_ERR_HIP: return "a HIP launch or runtime call failed";
     default: return "unknown status";
   }
+}
+
+size_t bd_moe_sz_size(const bd_moe_weights* w, int matrix) {
+  if (check_moe_shape(w, 1) != BD_OK || (matrix != 0 && matrix != 1)) return 0;
+  return bd::sz_prep_bytes(matrix == 0, w->num_experts, w->d_model, w->d_ff);
+}
+
+int moe_w4a16_prepare(const bd_moe_weights* w, uint16_t* gate_up_sz, uint16_t* down_sz,
+                      void* stream) {
+  int st = check_moe_shape(w, 1);
+  if (st != BD_OK) return st;
+  if (!gate_up_sz || !down_sz || !w->gate_up_scale || !w->gate_up_zero || !w->down_scale ||
+      !w->down_zero)
+    return BD_ERR_NULL;
+  if (!aligned16(gate_up_sz) || !aligned16(down_sz)) return BD_ERR_ALIGN;
+  st = to_status(bd::launch_prep_sz(gate_up_of(w), true, w->num_experts, w->d_model, w->d_ff,
+                                    gate_up_sz, as_stream(stream)));
+  if (st != BD_OK) return st;
+  return to_status(bd::launch_prep_sz(down_of(w), false, w->num_experts, w->d_model, w->d_ff,
+                                      down_sz, as_stream(stream)));
 }
 
 size_t bd_moe_workspace_size(int T, const bd_moe_weights* w) {

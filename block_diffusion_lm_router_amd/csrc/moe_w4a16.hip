@@ -107,6 +107,7 @@ struct GemmArgs {
   const uint16_t* act;     // gate/up: x [T][K]; down: h [T*k][K] (bucket order); both k-permuted
   const int32_t* perm;     // bucket position -> assignment t*k + j
   const int32_t* items;    // [0] = count, then (expert, first position, tokens)
+  const uint16_t* sz;      // stage-major scales/zero-points (wide kernel), see prep_sz_kernel
   uint16_t* h_out;         // gate/up output [T*k][d_ff]
   float* o_out;            // down output [T*k][d_model]
   int out_ld;
@@ -153,6 +154,7 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 zc1, _Float16 z
 }
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Reorder 8 halves (h0..h7) to (h0,h4,h1,h5,h2,h6,h3,h7).
@@ -409,6 +411,261 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(GemmArgs a) {
     gemm_item<GATED, 1>(a, lds, e, pos0, mcount, tile);
 }
 
+
+// ------------------------------------------------------------------ wide kernel
+//
+// The same GEMM on 256-row tiles, for weights whose scales and zero-points have been laid
+// out stage-major by prep_sz_kernel.  Per stage a block moves 16 KB of packed weights, at
+// most 8 KB of activation rows and 2 KB of scales/zero-points; the activation rows are shared
+// by twice the weight rows of the 128-row tiles, which halves the bytes the CU's memory
+// pipeline moves per weight byte, and the scales and zero-points stream with the stage
+// instead of filling a per-block table.  Each wave owns 32 whole rows (both groups of every
+// stage), so there is no cross-wave reduction: gate/up wave w holds gate columns 16w..16w+15
+// of the tile and the matching up rows; down wave w holds rows 32w..32w+31.  A tile past the
+// end of the matrix (d_ff % 128 == 64 for gate/up, d_model % 256 == 128 for down) leaves its
+// last four waves without rows: they skip their weight loads and compute and keep their
+// share of the activation and scale loads.
+constexpr int kWdRows = 256;
+constexpr int kWdWBytes = kWdRows * kWRowBytes;                // 16 KB
+constexpr int kWdXBytes = kItemTokens * kXRowBytes;            // 8 KB
+constexpr int kWdSZBytes = kWdRows * 8;                        // 2 KB: [row][s0 s1 z0 z1]
+constexpr int kWdSlot = kWdWBytes + kWdXBytes + kWdSZBytes;
+constexpr int kWdSlots = 3;                                     // two stages in flight
+constexpr int kWdLds = kWdSlots * kWdSlot;
+static_assert(kWdLds <= 80 * 1024, "two wide blocks per CU");
+static_assert(kSG == 2 && kItemTokens == 32 && kXRowBytes == 256, "wide stage geometry");
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vmcnt<N>();
+      return;
+    }
+    wait_vmcnt_upto<N - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+template <bool GATED, int NMT>
+__device__ __forceinline__ void wide_item(const GemmArgs& a, char* lds, int e, int pos0,
+                                          int mcount, int tile) {
+  constexpr int kDepth = kWdSlots - 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int kb = lane >> 4;
+  const int G = a.K >> 6;
+  const int NS = (G + 1) >> 1;
+  const size_t rowbytes = (size_t)(a.K >> 1);
+  const DequantConsts dq = dequant_consts();
+
+  // Rows of this wave (set A, set B) within the tile and whether they exist.
+  const int rows_here = GATED ? min(128, a.d_ff - tile * 128) : min(kWdRows, a.R - tile * kWdRows);
+  const bool valid = GATED ? wave * 16 < rows_here : wave * 32 < rows_here;
+  const int rA = GATED ? wave * 16 + n : wave * 32 + n;           // tile row of set A
+  const int rB = GATED ? 128 + wave * 16 + n : wave * 32 + 16 + n;
+  // Load duties: weights (valid waves, two loads), activation rows 4w..4w+3 (waves below
+  // 4 * NMT), scales/zero-points rows 128(w-6).. (waves 6 and 7).
+  const bool xload = wave < 4 * NMT;
+  const bool szload = wave >= 6;
+  const int my_loads = (valid ? 2 : 0) + (xload ? 1 : 0) + (szload ? 1 : 0);
+
+  // Weight load of set S: tile rows base..base+15, lane -> (row lane/4, chunk slot lane%4)
+  // holding global chunk (lane%4) ^ wswz(row).
+  const int wr = lane >> 2;
+  const int wchunk = (lane & 3) ^ wswz(wr);
+  auto mrow = [&](int tr) -> int {       // matrix row of tile row tr (of this expert)
+    if (GATED) return (tr < 128 ? 0 : a.d_ff) + tile * 128 + (tr & 127);
+    return tile * kWdRows + tr;
+  };
+  const uint8_t* wsrcA = a.q + ((size_t)e * a.R + mrow(rA - n + wr)) * rowbytes;
+  const uint8_t* wsrcB = a.q + ((size_t)e * a.R + mrow(rB - n + wr)) * rowbytes;
+  // Activation load: rows 4w + lane/16.
+  const int xm = wave * 4 + (lane >> 4);
+  const int xchunk = (lane & 15) ^ xswz(xm);
+  const uint16_t* xsrc;
+  {
+    const int mm = min(xm, mcount - 1);
+    const int row = GATED ? a.perm[pos0 + mm] / a.top_k : pos0 + mm;
+    xsrc = a.act + (size_t)row * a.K;
+  }
+  // Scale/zero-point load: stage-major block of this (expert, tile), 2 KB per stage.
+  const char* szsrc = reinterpret_cast<const char*>(a.sz) +
+                      ((size_t)e * a.tiles + tile) * NS * kWdSZBytes + max(wave - 6, 0) * 1024 + lane * 16;
+
+  auto dma = [&](int c, int slot) {
+    char* st = lds + slot * kWdSlot;
+    if (valid) {
+      int byte = c * kWRowBytes + wchunk * 16;
+      if ((byte >> 5) >= G) byte &= 31;
+      __builtin_amdgcn_global_load_lds(wsrcA + byte, st + (wave * 2 + 0) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(wsrcB + byte, st + (wave * 2 + 1) * 1024, 16, 0, 0);
+    }
+    if (xload) {
+      int col = c * kStageK + xchunk * 8;
+      if (col >= a.K) col &= 63;
+      __builtin_amdgcn_global_load_lds(xsrc + col, st + kWdWBytes + wave * 1024, 16, 0, 0);
+    }
+    if (szload)
+      __builtin_amdgcn_global_load_lds(szsrc + (size_t)c * kWdSZBytes,
+                                       st + kWdWBytes + kWdXBytes + (wave - 6) * 1024, 16, 0, 0);
+  };
+
+  float4_t totA[NMT], totB[NMT];
+  const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) totA[mt] = totB[mt] = zero4;
+
+  auto compute = [&](int c, int slot) {
+    const char* st = lds + slot * kWdSlot;
+    const char* wA = st + (wave * 2 + 0) * 1024 + n * kWRowBytes;
+    const char* wB = st + (wave * 2 + 1) * 1024 + n * kWRowBytes;
+    const char* xt = st + kWdWBytes;
+    const char* sz = st + kWdWBytes + kWdXBytes;
+    const half4_t szA = __builtin_bit_cast(half4_t, *reinterpret_cast<const u32x2_t*>(sz + rA * 8));
+    const half4_t szB = __builtin_bit_cast(half4_t, *reinterpret_cast<const u32x2_t*>(sz + rB * 8));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int g = 2 * c + j;
+      if (g >= G) break;
+      const int chunk = 2 * j + (kb >> 1);
+      const u32x2_t wa = *reinterpret_cast<const u32x2_t*>(wA + ((chunk ^ wswz(n)) << 4) + ((kb & 1) << 3));
+      const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(wB + ((chunk ^ wswz(n)) << 4) + ((kb & 1) << 3));
+      const _Float16 sA = szA[j], zA = szA[2 + j];
+      const _Float16 sB = szB[j], zB = szB[2 + j];
+      const _Float16 za1 = -((_Float16)1024.f + zA), za2 = -((_Float16)64.f + zA);
+      const _Float16 zb1 = -((_Float16)1024.f + zB), zb2 = -((_Float16)64.f + zB);
+      const float fsA = (float)sA, fsB = (float)sB;
+      const half8_t bA0 = dequant8(wa[0], za1, za2, dq);
+      const half8_t bA1 = dequant8(wa[1], za1, za2, dq);
+      const half8_t bB0 = dequant8(wb[0], zb1, zb2, dq);
+      const half8_t bB1 = dequant8(wb[1], zb1, zb2, dq);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int m = mt * 16 + n;
+        const char* xrow = xt + m * kXRowBytes;
+        const int c8 = j * 8 + kb * 2;
+        const half8_t a0 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 0) ^ xswz(m)) << 4)));
+        const half8_t a1 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 1) ^ xswz(m)) << 4)));
+        float4_t accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bA0, zero4, 0, 0, 0);
+        accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bA1, accA, 0, 0, 0);
+        float4_t accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bB0, zero4, 0, 0, 0);
+        accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bB1, accB, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          totA[mt][r] = fmaf(fsA, accA[r], totA[mt][r]);
+          totB[mt][r] = fmaf(fsB, accB[r], totB[mt][r]);
+        }
+      }
+    }
+  };
+
+  // Same pipeline as the tile kernel: kDepth stages in flight, every wave issuing its fixed
+  // share of loads every stage (stages past the end re-read the last one into ring slots no
+  // stage reads), so waiting until at most my_loads * (kDepth - 1) of this wave's loads are
+  // outstanding completes the stage's loads; the barrier publishes every wave's.
+#pragma unroll
+  for (int s = 0; s < kDepth; ++s) dma(min(s, NS - 1), s);
+  for (int c = 0; c < NS; c += kWdSlots) {
+#pragma unroll
+    for (int u = 0; u < kWdSlots; ++u) {
+      const int cc = c + u;
+      if (cc >= NS) break;
+      wait_vmcnt_upto<4 * (kDepth - 1)>(my_loads * (kDepth - 1));
+      lds_barrier();
+      dma(min(cc + kDepth, NS - 1), (u + kDepth) % kWdSlots);
+      if (valid) compute(cc, u);
+    }
+  }
+  wait_vmcnt<0>();   // no LDS write may still be in flight when the block ends
+  if (!valid) return;
+
+  // Epilogue: D lane layout = tokens 4kb..4kb+3 of row n.
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mt * 16 + kb * 4 + r;
+      if (m >= mcount) continue;
+      if (GATED) {
+        const float hv = gelu_tanh(totA[mt][r]) * totB[mt][r];
+        const int col = tile * 128 + wave * 16 + n;
+        const int pcol = (col & ~7) | ((col & 3) << 1) | ((col >> 2) & 1);
+        const _Float16 h16 = (_Float16)hv;
+        a.h_out[(size_t)(pos0 + m) * a.d_ff + pcol] = __builtin_bit_cast(uint16_t, h16);
+      } else {
+        const int slot = a.perm[pos0 + m];
+        const int row = tile * kWdRows + wave * 32 + n;
+        a.o_out[(size_t)slot * a.out_ld + row] = totA[mt][r];
+        a.o_out[(size_t)slot * a.out_ld + row + 16] = totB[mt][r];
+      }
+    }
+  }
+}
+
+template <bool GATED>
+__global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kWdLds];
+  const int b = blockIdx.x;
+  const int local = b / kXcds;
+  const int item = (local / a.tiles) * kXcds + (b % kXcds);
+  const int tile = local % a.tiles;
+  if (item >= a.items[0]) return;
+  const int e = a.items[1 + 3 * item];
+  const int pos0 = a.items[2 + 3 * item];
+  const int mcount = a.items[3 + 3 * item];
+  if (mcount > 16)
+    wide_item<GATED, 2>(a, lds, e, pos0, mcount, tile);
+  else
+    wide_item<GATED, 1>(a, lds, e, pos0, mcount, tile);
+}
+
+// Stage-major scales and zero-points for the wide kernel.  Entry (e, tile, stage s, row r)
+// is 4 halves: scale and zero-point of groups 2s and 2s+1 (0 past the last group) of tile
+// row r (gate/up: r < 128 the gate row of column 128 tile + r, else the matching up row;
+// down: row 256 tile + r), 0 for rows past the matrix.  One thread per entry.
+__global__ __launch_bounds__(256) void prep_sz_kernel(const uint16_t* __restrict__ scale,
+                                                      const uint16_t* __restrict__ zero, int R,
+                                                      int G, int tiles, int NS, int gated,
+                                                      int d_ff, size_t entries,
+                                                      u32x2_t* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= entries) return;
+  const int r = (int)(i % kWdRows);
+  const size_t q = i / kWdRows;
+  const int s = (int)(q % NS);
+  const int tile = (int)((q / NS) % tiles);
+  const size_t e = q / ((size_t)NS * tiles);
+  int row;
+  bool ok;
+  if (gated) {
+    const int col = tile * 128 + (r & 127);
+    ok = col < d_ff;
+    row = (r < 128 ? 0 : d_ff) + col;
+  } else {
+    row = tile * kWdRows + r;
+    ok = row < R;
+  }
+  const int g0 = 2 * s, g1 = 2 * s + 1;
+  uint32_t s0 = 0, s1 = 0, z0 = 0, z1 = 0;
+  if (ok) {
+    const size_t base = (e * R + row) * (size_t)G;
+    s0 = scale[base + g0];
+    z0 = zero[base + g0];
+    if (g1 < G) {
+      s1 = scale[base + g1];
+      z1 = zero[base + g1];
+    }
+  }
+  u32x2_t v;
+  v[0] = s0 | (s1 << 16);
+  v[1] = z0 | (z1 << 16);
+  out[i] = v;
+}
+
 // x [T][d] -> xp [T][d] with every 8 consecutive halves reordered to (0,4,1,5,2,6,3,7).
 __global__ __launch_bounds__(256) void permute_x_kernel(const u32x4_t* __restrict__ x,
                                                         u32x4_t* __restrict__ xp, int n) {
@@ -421,6 +678,28 @@ int grid_blocks(int max_items, int tiles) {
 }
 
 }  // namespace
+
+int sz_tiles(bool gated, int d_model, int d_ff) {
+  return gated ? (d_ff + 127) / 128 : (d_model + kWdRows - 1) / kWdRows;
+}
+
+size_t sz_prep_bytes(bool gated, int E, int d_model, int d_ff) {
+  const int K = gated ? d_model : d_ff;
+  const int NS = (K / 64 + 1) / 2;
+  return (size_t)E * sz_tiles(gated, d_model, d_ff) * NS * kWdSZBytes;
+}
+
+hipError_t launch_prep_sz(const W4A16Matrix& m, bool gated, int E, int d_model, int d_ff,
+                          uint16_t* out, hipStream_t stream) {
+  const int K = gated ? d_model : d_ff;
+  const int R = gated ? 2 * d_ff : d_model;
+  const int G = K / 64, NS = (G + 1) / 2, tiles = sz_tiles(gated, d_model, d_ff);
+  const size_t entries = (size_t)E * tiles * NS * kWdRows;
+  hipLaunchKernelGGL(prep_sz_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, stream,
+                     m.scale, m.zero, R, G, tiles, NS, gated ? 1 : 0, d_ff, entries,
+                     reinterpret_cast<u32x2_t*>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, int top_k, int T,
                           const uint16_t* x, const MoeWorkspace& ws, hipStream_t stream) {
@@ -436,6 +715,7 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.act = ws.xp;
   a.perm = ws.perm;
   a.items = ws.items;
+  a.sz = gu.sz;
   a.h_out = ws.h;
   a.o_out = nullptr;
   a.out_ld = d_ff;
@@ -445,8 +725,14 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
                      reinterpret_cast<const u32x4_t*>(x), reinterpret_cast<u32x4_t*>(ws.xp), n8);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(w4a16_gemm_kernel<true>, dim3(grid_blocks(ws.max_items, a.tiles)),
-                     dim3(kThreads), 0, stream, a);
+  if (gu.sz) {
+    a.tiles = sz_tiles(true, d_model, d_ff);
+    hipLaunchKernelGGL(w4a16_wide_kernel<true>, dim3(grid_blocks(ws.max_items, a.tiles)),
+                       dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(w4a16_gemm_kernel<true>, dim3(grid_blocks(ws.max_items, a.tiles)),
+                       dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -464,13 +750,20 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
   a.act = ws.h;
   a.perm = ws.perm;
   a.items = ws.items;
+  a.sz = dn.sz;
   a.h_out = nullptr;
   a.o_out = expert_out;
   a.out_ld = d_model;
   (void)E;
   (void)T;
-  hipLaunchKernelGGL(w4a16_gemm_kernel<false>, dim3(grid_blocks(ws.max_items, a.tiles)),
-                     dim3(kThreads), 0, stream, a);
+  if (dn.sz) {
+    a.tiles = sz_tiles(false, d_model, d_ff);
+    hipLaunchKernelGGL(w4a16_wide_kernel<false>, dim3(grid_blocks(ws.max_items, a.tiles)),
+                       dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(w4a16_gemm_kernel<false>, dim3(grid_blocks(ws.max_items, a.tiles)),
+                       dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

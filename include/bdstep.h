@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 1
+#define BD_ABI_VERSION 2
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -82,6 +82,12 @@ typedef enum {
  * in fp16); the GEMM subtracts them exactly in fp16, a non-integer zero-point is
  * rounded to the nearest integer first.
  * Supported: group_size == 64, d_model % 128 == 0, d_ff % 64 == 0, d_model and d_ff <= 4096.
+ *
+ * gate_up_sz / down_sz (optional, NULL when absent): the same scales and zero-points laid out
+ * stage-major by moe_w4a16_prepare, so that a GEMM streams them with its weights.  A GEMM
+ * whose array is present runs on 256-row tiles; without it, on 128-row tiles reading scale
+ * and zero directly.  Both contract exact fp16 (q - z) per 64-group and scale each group's
+ * sum in fp32; they differ only in the order of the fp32 sums.
  */
 typedef struct bd_moe_weights {
   int32_t num_experts; /* E, 1..256          */
@@ -95,6 +101,8 @@ typedef struct bd_moe_weights {
   const uint8_t* down_q;
   const uint16_t* down_scale;
   const uint16_t* down_zero;
+  const uint16_t* gate_up_sz;  /* optional, bd_moe_sz_size(w, 0) bytes, 16-byte aligned */
+  const uint16_t* down_sz;     /* optional, bd_moe_sz_size(w, 1) bytes, 16-byte aligned */
 } bd_moe_weights;
 
 /* Library ABI version (BD_ABI_VERSION of the build). */
@@ -104,6 +112,26 @@ int bd_abi_version(void);
 const char* bd_status_string(int status);
 
 /* ------------------------------------------------------------------ MoE FFN */
+
+/*
+ * Bytes of the stage-major scale/zero-point array of the gate/up matrix (matrix 0) or the
+ * down matrix (matrix 1); 0 if the shape is invalid.
+ */
+size_t bd_moe_sz_size(const bd_moe_weights* w, int matrix);
+
+/*
+ * One-time preparation of a layer's weights for the 256-row GEMM tiles: writes the scales
+ * and zero-points of both matrices, stage-major, into the caller's buffers (sizes from
+ * bd_moe_sz_size; 16-byte aligned).  Reads only w's scale and zero arrays.  For every
+ * (expert e, tile t, stage s of 128 contraction elements, tile row r) the entry is the four
+ * fp16 values scale[row][2s], scale[row][2s+1], zero[row][2s], zero[row][2s+1] (0 past the
+ * last group), where the tile row r of gate/up is the gate row of column 128t + r for r < 128
+ * and the up row of column 128t + r - 128 otherwise, and of down the row 256t + r; rows past
+ * the matrix hold 0.  Layout [E][tiles][stages][256][4].  Store the result in gate_up_sz and
+ * down_sz of the weights struct for the GEMM entry points to use it.
+ */
+int moe_w4a16_prepare(const bd_moe_weights* w, uint16_t* gate_up_sz, uint16_t* down_sz,
+                      void* stream);
 
 /*
  * Device workspace bytes needed by the MoE entry points for T tokens.  The same

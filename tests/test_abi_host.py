@@ -48,7 +48,8 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bd_abi_version() == 1
+    version = int(re.search(r"#define BD_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.bd_abi_version() == version
     for s in range(7):
         assert len(lib.bd_status_string(s)) > 0
     assert lib.bd_status_string(99) == b"unknown status"
@@ -57,7 +58,7 @@ def test_version_and_status_strings(lib):
 def _weights(E=128, k=8, d=2816, f=704, g=64, ptr=0x1000):
     from block_diffusion_lm_router_amd._binding import MoeWeightsC
     p = ctypes.c_void_p(ptr)
-    return MoeWeightsC(E, k, d, f, g, p, p, p, p, p, p)
+    return MoeWeightsC(E, k, d, f, g, p, p, p, p, p, p, None, None)
 
 
 def test_moe_workspace_size(lib):
@@ -128,3 +129,22 @@ def test_sampler_validation(lib):
     assert step(P, 8, 100, 1.0, float("inf"), 0, 0, None, None, P, P, P, P, P, 1 << 20, None) == 2
     assert lib.bd_hbm_copy(P, P, 17, None) == 2
     assert lib.bd_hbm_copy(None, P, 16, None) == 1
+
+
+def test_prepare_sizes_and_validation(lib):
+    w = _weights()
+    ref = ctypes.byref(w)
+    # [E][tiles][stages][256 rows][4 halves]: gate/up 6 tiles of 128 columns x 22 stages,
+    # down 11 tiles of 256 rows x 6 stages (11 groups: the last stage holds one).
+    assert lib.bd_moe_sz_size(ref, 0) == 128 * 6 * 22 * 256 * 8
+    assert lib.bd_moe_sz_size(ref, 1) == 128 * 11 * 6 * 256 * 8
+    assert lib.bd_moe_sz_size(ref, 2) == 0
+    p = ctypes.c_void_p(0x1000)
+    assert lib.moe_w4a16_prepare(ref, None, p, None) == 1              # BD_ERR_NULL
+    assert lib.moe_w4a16_prepare(ref, ctypes.c_void_p(0x1008), p, None) == 3   # BD_ERR_ALIGN
+    bad = _weights(g=128)
+    assert lib.moe_w4a16_prepare(ctypes.byref(bad), p, p, None) == 5   # BD_ERR_UNSUPPORTED
+    # a misaligned prepared array is rejected by the GEMM entry points before any launch
+    w.gate_up_sz = 0x1008
+    ws = ctypes.c_void_p(0x10000)
+    assert lib.moe_w4a16_gate_up(ref, 256, p, ws, 1 << 30, None) == 3

@@ -37,8 +37,14 @@ class Layer:
         self.x_d = torch.from_numpy(self.x).cuda()
         self.logits_d = torch.from_numpy(self.logits).cuda()
 
-    def run(self, bd, fused=True):
+    def run(self, bd, fused=True, prepared=True):
+        """One FFN pass; prepared=True uses the stage-major scale/zero arrays (256-row GEMM
+        tiles), False the raw scale and zero arrays (128-row tiles)."""
         import torch
+        if prepared and self.w.sz is None:
+            self.w.prepare()
+        elif not prepared and self.w.sz is not None:
+            self.w.unprepare()
         T, k, d = self.shape.tokens, self.shape.top_k, self.shape.d_model
         ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
         tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
@@ -93,26 +99,77 @@ def check_layer(layer, got, tokens=None):
     return check_ffn_close(y[rows].astype(np.float64), y_ref, "y")
 
 
-def test_tiny_layer(bd):
-    say("tiny layer")
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
+def test_tiny_layer(bd, prepared):
+    say("tiny layer", prepared)
     layer = Layer(bd, workloads.TINY_LAYER)
-    got = layer.run(bd)
+    got = layer.run(bd, prepared=prepared)
     rel = check_layer(layer, got)
     assert rel < 2e-3
-    got2 = layer.run(bd, fused=False)
+    got2 = layer.run(bd, fused=False, prepared=prepared)
     for a, b in zip(got, got2):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
 @pytest.mark.parametrize("T,E,k,d,f", [(1, 4, 1, 128, 64), (3, 8, 3, 256, 192),
                                        (100, 4, 2, 128, 64), (77, 16, 4, 384, 128),
                                        (250, 2, 2, 128, 64)])
-def test_ragged_buckets(bd, T, E, k, d, f):
-    """Buckets of 1..T tokens: partial 16-row tiles, several 32-token items per expert."""
+def test_ragged_buckets(bd, T, E, k, d, f, prepared):
+    """Buckets of 1..T tokens: partial 16-row tiles, several 32-token items per expert;
+    d_ff % 128 == 64 and d_model % 256 == 128 leave the last 256-row tile half empty."""
     shape = workloads.LayerShape(T, d, f, E, k)
-    say("ragged buckets", T, E, k, d, f)
+    say("ragged buckets", T, E, k, d, f, prepared)
     layer = Layer(bd, shape, layer=T + E)
-    check_layer(layer, layer.run(bd))
+    check_layer(layer, layer.run(bd, prepared=prepared))
+
+
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
+@pytest.mark.parametrize("T,E,k,d,f", [(96, 16, 4, 1024, 640), (200, 8, 2, 768, 576),
+                                       (512, 8, 8, 640, 576), (2048, 4, 4, 640, 576),
+                                       (33, 128, 8, 2816, 704)])
+def test_larger_shapes(bd, T, E, k, d, f, prepared):
+    """Odd group counts (576, 704: a half last stage), ragged 256-row tiles (640, 576),
+    experts with many 32-token items, ragged items, the full expert shape."""
+    shape = workloads.LayerShape(T, d, f, E, k)
+    say("larger shapes", T, E, k, d, f, prepared)
+    layer = Layer(bd, shape, layer=7 + T % 5)
+    check_layer(layer, layer.run(bd, prepared=prepared))
+
+
+@pytest.mark.parametrize("d,f,E", [(256, 128, 8), (2816, 704, 4), (640, 576, 3)])
+def test_prepared_scales_layout(bd, d, f, E):
+    """moe_w4a16_prepare writes exactly the documented stage-major layout (bit-exact against a
+    re-indexing of the raw arrays)."""
+    import torch
+    shape = workloads.LayerShape(4, d, f, E, 1)
+    w_np = workloads.make_weights(shape, 5)
+    say("prepared layout", d, f, E)
+    w = bd.MoeWeights.from_numpy(w_np, 1).prepare()
+    torch.cuda.synchronize()
+    for which, (rows_of, G, tiles) in enumerate([
+            (lambda t, r: (r < 128, (0 if r < 128 else f) + 128 * t + (r & 127), 128 * t + (r & 127) < f),
+             d // 64, -(-f // 128)),
+            (lambda t, r: (True, 256 * t + r, 256 * t + r < d), f // 64, -(-d // 256))]):
+        name = "gate_up" if which == 0 else "down"
+        sc = w_np[name + "_scale"].view(np.uint16)
+        ze = w_np[name + "_zero"].view(np.uint16)
+        NS = (G + 1) // 2
+        got = w.sz[which].cpu().numpy().view(np.uint16).reshape(E, tiles, NS, 256, 4)
+        want = np.zeros_like(got)
+        for t in range(tiles):
+            for r in range(256):
+                _, row, ok = rows_of(t, r)
+                if not ok:
+                    continue
+                for s in range(NS):
+                    for j in range(2):
+                        g = 2 * s + j
+                        if g < G:
+                            want[:, t, s, r, j] = sc[:, row, g]
+                            want[:, t, s, r, 2 + j] = ze[:, row, g]
+        assert np.array_equal(got, want), f"{name} layout differs"
+
 
 
 def test_single_expert_and_zero_input(bd):
@@ -161,20 +218,22 @@ def test_combine_bit_identical_and_within_fp16_rounding(bd):
     assert np.all(np.abs(y - ref) <= half_ulp * 1.0001 + fp32_sum)
 
 
-def test_full_layer_sampled_tokens(bd):
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
+def test_full_layer_sampled_tokens(bd, prepared):
     """Full shape (256 tokens, 128 experts, top-8): ids for all, outputs on sampled tokens."""
-    say("full layer")
+    say("full layer", prepared)
     layer = Layer(bd, workloads.LAYER)
-    got = layer.run(bd)
+    got = layer.run(bd, prepared=prepared)
     tokens = np.random.default_rng(0).choice(layer.shape.tokens, 6, replace=False)
     check_layer(layer, got, tokens=tokens)
 
 
-def test_short_zipf_layer(bd):
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
+def test_short_zipf_layer(bd, prepared):
     """64 tokens with Zipf-skewed routing: small and large buckets in one launch."""
-    say("short zipf layer")
+    say("short zipf layer", prepared)
     layer = Layer(bd, workloads.SHORT_LAYER)
-    got = layer.run(bd)
+    got = layer.run(bd, prepared=prepared)
     counts = np.bincount(got[0].ravel(), minlength=128)
     assert counts.max() > 32      # the hottest expert needs several 32-token items
     tokens = np.random.default_rng(1).choice(layer.shape.tokens, 6, replace=False)
