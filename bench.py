@@ -147,30 +147,33 @@ def main():
     acc = torch.empty(P, dtype=torch.uint8, device="cuda")
     # Every launch of the stack is marshalled once up front (bd.bind), so that a step costs
     # the host a few microseconds per launch and the GPU's queue never runs dry: the timed
-    # region then measures the kernels, not the host.  Each gate/up launch of each timed
-    # step is bracketed by its own pair of timing events on the launch stream.
+    # region then measures the kernels, not the host.  A timing event in the stream costs the
+    # GPU a few microseconds of idle time, so each timed step brackets the gate/up launch of
+    # one layer only (layer i mod L at step i): over the timed steps the events sample the
+    # gate/up launches of every layer, at an overhead of one event pair per step.
     stack = []
     for w, router in layers:
         stack.append((bd.bind(bd.moe_route_topk, w, router, ids, tw, ws),
                       bd.bind(bd.moe_w4a16_gate_up, w, x, ws),
                       bd.bind(bd.moe_w4a16_down, w, T, o, ws),
                       bd.bind(bd.moe_combine_fixed_order, o, tw, y)))
-    gu_events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in layers] for _ in range(args.steps)]
+    gu_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+    gu_layer = [i % len(layers) for i in range(args.steps)]
     total = args.warmup + args.steps
     n_acc = torch.zeros(total, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(i, events=None):
+    def step(i, events=None, ev_layer=-1):
         if i % workloads.STACK_STEPS == 0:
             frozen.zero_()
         for li, (route, gate_up, down, combine) in enumerate(stack):
             route()
-            if events is not None:
-                events[li][0].record(stream)
+            if li == ev_layer:
+                events[0].record(stream)
             gate_up()
-            if events is not None:
-                events[li][1].record(stream)
+            if li == ev_layer:
+                events[1].record(stream)
             down()
             combine()
         bd.diffusion_sample_step(logits, sshape.temperature, sshape.bound, sshape.seed,
@@ -184,11 +187,10 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.warmup, total):
-        step(i, gu_events[i - args.warmup])
+        step(i, gu_events[i - args.warmup], gu_layer[i - args.warmup])
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    gu_events = [p for ev in gu_events for p in ev]
 
     # Unfrozen rows seen by each timed step's sampler, from the device's acceptance counts.
     counts = n_acc.cpu().numpy()
@@ -207,7 +209,7 @@ def main():
     value = step_bytes / (ms * 1e-3) / 1e9
 
     gu_ms = np.array([a.elapsed_time(b) for a, b in gu_events])
-    gu_alg = np.array([t * gu_bytes + T * d * 2 + T * k * f * 2 for t in touched] * args.steps,
+    gu_alg = np.array([touched[li] * gu_bytes + T * d * 2 + T * k * f * 2 for li in gu_layer],
                       dtype=np.float64)
     gu_gbs = gu_alg.sum() / (gu_ms.sum() * 1e-3) / 1e9
     traffic = measured_traffic(float(gu_alg.mean()))
@@ -234,7 +236,7 @@ def main():
             "step_algorithmic_bytes": int(step_bytes),
         },
         "roofline": {
-            "kernel": "moe_w4a16_gate_up (permute_x_kernel + w4a16_gemm_kernel<true>)",
+            "kernel": "moe_w4a16_gate_up (bucket_permute_kernel + w4a16_wide_kernel<true>)",
             "bound": "hbm",
             "achieved": round(gu_gbs, 2),
             "peak": HBM_PEAK_GBS,

@@ -75,6 +75,42 @@ __device__ __forceinline__ int wave_min_i32(int v) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
 
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active).  Within each row of
+// 16 lanes the value of the lane 1, 2, 4 and 8 places below is added (DPP row shifts); then
+// the last lane of row 0 and of row 2 is added to rows 1 and 3 (row broadcast of lane 15),
+// and the last lane of row 1 to rows 2 and 3 (row broadcast of lane 31).
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  const int lane = lane_id();
+  const int rl = lane & 15;
+  int t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  if (rl >= 1) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  if (rl >= 2) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  if (rl >= 4) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  if (rl >= 8) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x142, 0xf, 0xf, false);   // row_bcast:15
+  if ((lane & 31) >= 16) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x143, 0xf, 0xf, false);   // row_bcast:31
+  if (lane >= 32) v += t;
+  return v;
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Reorder 8 halves (h0..h7) to (h0,h4,h1,h5,h2,h6,h3,h7): the k-order in which the GEMMs'
+// nibble dequantisation yields weights.
+__device__ __forceinline__ u32x4_t permute8(u32x4_t v) {
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+  return r;
+}
+
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11):
 // ten rounds of the 4x32 S-P network; the key advances by the Weyl increments

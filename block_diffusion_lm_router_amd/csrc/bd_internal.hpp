@@ -33,6 +33,7 @@ struct MoeWorkspace {
   int32_t* perm;     // [T * k] assignment index t*k + j at each bucket position
   uint16_t* h;       // [T * k][d_ff] fp16 GeGLU activations, bucket order, k-permuted
   uint16_t* xp;      // [T][d_model] fp16 activations with k permuted within blocks of 8
+  int32_t* ids;      // [T * k] copy of the top-k expert ids
   int max_items;
 };
 
@@ -40,8 +41,13 @@ int moe_max_items(int T, int E, int k);
 size_t moe_workspace_bytes(int T, int E, int k, int d_model, int d_ff);
 MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_model, int d_ff);
 
+// Top-k ids and weights, the ids also into ws.ids.
 hipError_t launch_route(const float* router_logits, int T, int E, int k, int32_t* topk_ids,
                         float* topk_weights, const MoeWorkspace& ws, hipStream_t stream);
+// Stable grouping of the assignments (ws.ids) by expert into ws, and x permuted into ws.xp,
+// in one launch.
+hipError_t launch_bucket(int T, int E, int k, const uint16_t* x, int d_model,
+                         const MoeWorkspace& ws, hipStream_t stream);
 
 struct W4A16Matrix {
   const uint8_t* q;

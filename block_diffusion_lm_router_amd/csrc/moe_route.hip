@@ -1,5 +1,6 @@
 // Routing kernels of the MoE layer: per-token top-k with softmax weights, then a stable
-// bucketing of the T*k assignments by expert and the work list of touched experts.
+// bucketing of the T*k assignments by expert and the work list of touched experts (run at
+// the start of the gate/up GEMM, in the same launch as the activation permutation).
 //
 // Source: axe-diffusion-ksl-xe model card, "what the model is" (128 experts, top-8 per
 // token) and "the kernels we built" (one launch covers all experts instead of a
@@ -13,8 +14,9 @@ namespace bd {
 namespace {
 
 constexpr int kTopkThreads = 256;
-constexpr int kBucketThreads = 1024;
+constexpr int kMaxTopk = 16;
 constexpr int kMaxE = 256;
+constexpr int kBucketThreads = 1024;
 constexpr int kPassTokens = 1024;         // tokens per bitmask pass of the bucketing
 constexpr int kPassWords = kPassTokens / 64;
 
@@ -25,147 +27,198 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float from_order_key(uint32_t k) {
-  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-  return __builtin_bit_cast(float, u);
-}
+typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, kWave);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-// One wave per token.  Key = (order(logit) << 32) | (0xffffffff - expert): the maximum
-// key is the largest logit, the lower expert id first among equal logits.
+// Top-k of one token per block.  Key of expert e = (order(logit) << 32) | (0xffffffff - e):
+// keys are distinct, a larger logit gives a larger key and the lower expert id wins a tie.
+// The rank of a key is the number of the token's keys above it; thread (i, part) counts
+// the keys above key i in one of 256/Ep contiguous parts of the key list (read back from
+// LDS as broadcasts), the parts are summed, and rank r < k puts expert i in slot r.
+// Weights = softmax over the k selected logits, summed in a fixed order.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ logits,
                                                             int T, int E, int k,
                                                             int32_t* __restrict__ ids,
+                                                            int32_t* __restrict__ ids_copy,
                                                             float* __restrict__ weights) {
-  const int t = blockIdx.x * (kTopkThreads / kWave) + threadIdx.x / kWave;
-  if (t >= T) return;  // uniform per wave
-  const int lane = lane_id();
-  uint64_t key[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = e < E ? ((uint64_t)order_key(logits[(size_t)t * E + e]) << 32) | (0xffffffffu - (uint32_t)e)
-                   : 0ull;
-  }
-  int my_id = 0;
-  float my_val = 0.f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t b = key[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) b = key[i] > b ? key[i] : b;
-    b = wave_max_u64(b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (key[i] == b) key[i] = 0ull;
-    if (lane == j) {
-      my_id = (int)(0xffffffffu - (uint32_t)b);
-      my_val = from_order_key((uint32_t)(b >> 32));
-    }
-  }
-  const float l0 = readlane_f32(my_val, 0);
-  const float ex = lane < k ? expf(my_val - l0) : 0.f;
-  const float sum = wave_sum(ex);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    weights[(size_t)t * k + lane] = ex / sum;
-  }
-}
-
-// Inclusive scan of 256 ints in LDS by the first 256 threads (Hillis-Steele).
-__device__ void scan256(int* buf, int tid) {
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    int v = 0;
-    if (tid < kMaxE && tid >= off) v = buf[tid - off];
-    __syncthreads();
-    if (tid < kMaxE) buf[tid] += v;
-    __syncthreads();
-  }
-}
-
-// One block.  Bucket positions are stable in assignment order a = t*k + j: the rank of
-// (t, j) inside expert e's bucket is the number of earlier tokens routed to e, counted
-// with per-expert token bitmasks (a token picks an expert at most once).
-__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* __restrict__ ids,
-                                                                int T, int k, int E,
-                                                                int32_t* __restrict__ offsets,
-                                                                int32_t* __restrict__ items,
-                                                                int32_t* __restrict__ perm) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int off[kMaxE];
-  __shared__ int itoff[kMaxE];
-  __shared__ int running[kMaxE];
-  __shared__ unsigned long long bits[kMaxE * kPassWords];
-  __shared__ int pre[kMaxE * kPassWords];
+  __shared__ __attribute__((aligned(16))) unsigned long long keys[kMaxE];
+  __shared__ int part_rank[kTopkThreads];
+  __shared__ int sel_id[kMaxTopk];
+  __shared__ float sel_val[kMaxTopk];
   const int tid = threadIdx.x;
-  const int A = T * k;
-  if (tid < kMaxE) {
-    cnt[tid] = 0;
-    running[tid] = 0;
+  const int t = blockIdx.x;
+  const int Ep = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
+  const int parts = kTopkThreads / Ep;
+  const int span = Ep / parts;                 // keys per part: 16, 64 or 256
+  const int i = tid % Ep, part = tid / Ep;
+  float val = 0.f;
+  uint64_t key = 0ull;
+  if (i < E) {
+    val = logits[(size_t)t * E + i];
+    key = ((uint64_t)order_key(val) << 32) | (0xffffffffu - (uint32_t)i);
   }
+  if (part == 0) keys[i] = key;                // zeros past E never outrank a key
   __syncthreads();
-  for (int a = tid; a < A; a += kBucketThreads) atomicAdd(&cnt[ids[a]], 1);
-  __syncthreads();
-  if (tid < kMaxE) {
-    off[tid] = cnt[tid];
-    itoff[tid] = (cnt[tid] + kItemTokens - 1) / kItemTokens;
+  int r = 0;
+  const unsigned long long* kp = keys + part * span;
+#pragma unroll 8
+  for (int j = 0; j < span; j += 2) {
+    const u64x2_t o = *reinterpret_cast<const u64x2_t*>(kp + j);
+    r += (o[0] > key) + (o[1] > key);
   }
+  part_rank[tid] = r;
   __syncthreads();
-  scan256(off, tid);
-  scan256(itoff, tid);
-  // inclusive -> exclusive, write offsets and the work list
-  if (tid < E) {
-    const int c = cnt[tid];
-    const int o = off[tid] - c;
-    const int ni = (c + kItemTokens - 1) / kItemTokens;
-    const int io = itoff[tid] - ni;
-    offsets[tid] = o;
-    for (int i = 0; i < ni; ++i) {
-      int32_t* it = items + 1 + 3 * (io + i);
-      it[0] = tid;
-      it[1] = o + i * kItemTokens;
-      it[2] = min(kItemTokens, c - i * kItemTokens);
+  if (part == 0 && i < E) {
+    int rank = 0;
+    for (int p = 0; p < parts; ++p) rank += part_rank[p * Ep + i];
+    if (rank < k) {
+      sel_id[rank] = i;
+      sel_val[rank] = val;
     }
   }
-  if (tid == 0) {
-    offsets[E] = A;
-    items[0] = itoff[E - 1];
+  __syncthreads();
+  if (tid < kWave) {
+    const int lane = tid;
+    const int my_id = lane < k ? sel_id[lane] : 0;
+    const float my_val = lane < k ? sel_val[lane] : 0.f;
+    const float l0 = readlane_f32(my_val, 0);
+    const float ex = lane < k ? expf(my_val - l0) : 0.f;
+    const float sum = wave_sum(ex);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = my_id;
+      ids_copy[(size_t)t * k + lane] = my_id;
+      weights[(size_t)t * k + lane] = ex / sum;
+    }
+  }
+}
+
+struct BucketArgs {
+  const int32_t* ids;      // [T * k]
+  int T, k, E;
+  int32_t* offsets;        // [E + 1]
+  int32_t* items;          // [0] = count, then (expert, first position, tokens)
+  int32_t* perm;           // [T * k]
+  const u32x4_t* x;        // [T * d_model / 8]
+  u32x4_t* xp;
+  int n8;
+};
+
+struct BucketShared {
+  unsigned long long bits[kMaxE * kPassWords];   // token bitmask of each expert, one pass
+  int wpre[kMaxE * kPassWords];                  // bucket rank at the start of each word
+  int cnt[kMaxE];
+  int eoff[kMaxE];
+  int ecnt[kMaxE];
+  int ioff[kMaxE + 1];
+  int wsum[8];
+};
+
+// Called by every thread of the block.  Thread e < Ep holds tot = the assignment count of
+// expert e (0 past E).  Exclusive prefixes over experts of the counts and of the item
+// counts ceil(tot / kItemTokens), by wave scans and the wave totals; then the offsets and
+// the work list (item it belongs to the last expert whose first item is <= it).
+__device__ void expert_scan(int tot, int E, int Ep, int A, BucketShared& sh,
+                            int32_t* __restrict__ offsets, int32_t* __restrict__ items) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int ni = (tot + kItemTokens - 1) / kItemTokens;
+  int it = 0, ii = 0;
+  if (tid < Ep) {                               // whole waves: Ep is a multiple of 64
+    it = wave_incl_scan_i32(tot);
+    ii = wave_incl_scan_i32(ni);
+    if (lane == kWave - 1) {
+      sh.wsum[wave] = it;
+      sh.wsum[4 + wave] = ii;
+    }
   }
   __syncthreads();
-  if (tid < kMaxE) off[tid] -= cnt[tid];
+  if (tid < Ep) {
+    int bt = 0, bi = 0;
+    for (int w = 0; w < wave; ++w) {
+      bt += sh.wsum[w];
+      bi += sh.wsum[4 + w];
+    }
+    const int ex_t = bt + it - tot, ex_i = bi + ii - ni;
+    if (tid < E) {
+      sh.eoff[tid] = ex_t;
+      sh.ecnt[tid] = tot;
+      sh.ioff[tid] = ex_i;
+      offsets[tid] = ex_t;
+    }
+    if (tid == Ep - 1) {                        // inclusive totals (experts past E hold 0)
+      sh.ioff[E] = bi + ii;
+      items[0] = bi + ii;
+      offsets[E] = A;
+    }
+  }
   __syncthreads();
-  for (int t0 = 0; t0 < T; t0 += kPassTokens) {
-    for (int i = tid; i < kMaxE * kPassWords; i += kBucketThreads) bits[i] = 0ull;
+  const int nitems = sh.ioff[E];
+  for (int m = tid; m < nitems; m += kBucketThreads) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sh.ioff[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    const int q = m - sh.ioff[lo];
+    int32_t* out = items + 1 + 3 * m;
+    out[0] = lo;
+    out[1] = sh.eoff[lo] + q * kItemTokens;
+    out[2] = min(kItemTokens, sh.ecnt[lo] - q * kItemTokens);
+  }
+}
+
+// Block 0: the bucketing.  Bucket position of assignment a = (t, j) routed to e is
+// offsets[e] + (tokens t' < t routed to e), so each bucket lists its assignments by
+// ascending token.  Tokens are taken in passes of kPassTokens: a bitmask per expert marks
+// the pass's tokens routed to it, popcounts of the words give the rank at each word's
+// start, and the rank of (t, j) adds the popcount of the bits below t in its word.  With
+// one pass the counts come from the bitmasks; with several, from a histogram first.
+// Blocks 1..: x -> xp with every 8 consecutive halves in the GEMMs' k-order.
+__global__ __launch_bounds__(kBucketThreads) void bucket_permute_kernel(BucketArgs g) {
+  if (blockIdx.x > 0) {
+    const int i = (blockIdx.x - 1) * kBucketThreads + threadIdx.x;
+    if (i < g.n8) g.xp[i] = permute8(g.x[i]);
+    return;
+  }
+  __shared__ BucketShared sh;
+  const int tid = threadIdx.x;
+  const int T = g.T, k = g.k, E = g.E, A = T * k;
+  const int Ep = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
+  const int npass = (T + kPassTokens - 1) / kPassTokens;
+  int run = 0;                                  // thread e < E: rank reached by earlier passes
+  if (npass > 1) {
+    if (tid < kMaxE) sh.cnt[tid] = 0;
     __syncthreads();
-    const int a0 = t0 * k, a1 = min(T, t0 + kPassTokens) * k;
+    for (int a = tid; a < A; a += kBucketThreads) atomicAdd(&sh.cnt[g.ids[a]], 1);
+    __syncthreads();
+    expert_scan(tid < E ? sh.cnt[tid] : 0, E, Ep, A, sh, g.offsets, g.items);
+  }
+  for (int p = 0; p < npass; ++p) {
+    const int t0 = p * kPassTokens;
+    const int nt = min(kPassTokens, T - t0);
+    const int W = (nt + 63) / 64;
+    for (int i = tid; i < E * kPassWords; i += kBucketThreads) sh.bits[i] = 0ull;
+    __syncthreads();
+    const int a0 = t0 * k, a1 = (t0 + nt) * k;
     for (int a = a0 + tid; a < a1; a += kBucketThreads) {
       const int lt = a / k - t0;
-      atomicOr(&bits[ids[a] * kPassWords + (lt >> 6)], 1ull << (lt & 63));
+      atomicOr(&sh.bits[g.ids[a] * kPassWords + (lt >> 6)], 1ull << (lt & 63));
     }
     __syncthreads();
     if (tid < E) {
-      int r = running[tid];
-      for (int w = 0; w < kPassWords; ++w) {
-        pre[tid * kPassWords + w] = r;
-        r += __popcll(bits[tid * kPassWords + w]);
+      for (int w = 0; w < W; ++w) {
+        sh.wpre[tid * kPassWords + w] = run;
+        run += __popcll(sh.bits[tid * kPassWords + w]);
       }
-      running[tid] = r;
     }
+    if (npass == 1) expert_scan(tid < E ? run : 0, E, Ep, A, sh, g.offsets, g.items);
     __syncthreads();
     for (int a = a0 + tid; a < a1; a += kBucketThreads) {
+      const int e = g.ids[a];
       const int lt = a / k - t0;
-      const int e = ids[a];
-      const int w = lt >> 6;
-      const unsigned long long below = (1ull << (lt & 63)) - 1ull;
-      const int rank = pre[e * kPassWords + w] + __popcll(bits[e * kPassWords + w] & below);
-      perm[off[e] + rank] = a;
+      const int w = e * kPassWords + (lt >> 6);
+      const int rank = sh.wpre[w] + __popcll(sh.bits[w] & ((1ull << (lt & 63)) - 1ull));
+      g.perm[sh.eoff[e] + rank] = a;
     }
     __syncthreads();
   }
@@ -181,7 +234,8 @@ int moe_max_items(int T, int E, int k) {
 size_t moe_workspace_bytes(int T, int E, int k, int d_model, int d_ff) {
   const size_t A = (size_t)T * k;
   return align_up((size_t)(E + 1) * 4) + align_up((size_t)(1 + 3 * moe_max_items(T, E, k)) * 4) +
-         align_up(A * 4) + align_up(A * (size_t)d_ff * 2) + align_up((size_t)T * d_model * 2);
+         align_up(A * 4) + align_up(A * (size_t)d_ff * 2) + align_up((size_t)T * d_model * 2) +
+         align_up(A * 4);
 }
 
 MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_model, int d_ff) {
@@ -198,19 +252,33 @@ MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_model, i
   ws.h = reinterpret_cast<uint16_t*>(p);
   p += align_up(A * (size_t)d_ff * 2);
   ws.xp = reinterpret_cast<uint16_t*>(p);
-  (void)d_model;
+  p += align_up((size_t)T * d_model * 2);
+  ws.ids = reinterpret_cast<int32_t*>(p);
   return ws;
 }
 
 hipError_t launch_route(const float* router_logits, int T, int E, int k, int32_t* topk_ids,
                         float* topk_weights, const MoeWorkspace& ws, hipStream_t stream) {
-  const int per_block = kTopkThreads / kWave;
-  hipLaunchKernelGGL(topk_kernel, dim3((T + per_block - 1) / per_block), dim3(kTopkThreads), 0,
-                     stream, router_logits, T, E, k, topk_ids, topk_weights);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, topk_ids, T, k, E,
-                     ws.offsets, ws.items, ws.perm);
+  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(kTopkThreads), 0, stream, router_logits, T, E, k,
+                     topk_ids, ws.ids, topk_weights);
+  return hipGetLastError();
+}
+
+hipError_t launch_bucket(int T, int E, int k, const uint16_t* x, int d_model,
+                         const MoeWorkspace& ws, hipStream_t stream) {
+  BucketArgs g;
+  g.ids = ws.ids;
+  g.T = T;
+  g.k = k;
+  g.E = E;
+  g.offsets = ws.offsets;
+  g.items = ws.items;
+  g.perm = ws.perm;
+  g.x = reinterpret_cast<const u32x4_t*>(x);
+  g.xp = reinterpret_cast<u32x4_t*>(ws.xp);
+  g.n8 = T * d_model / 8;
+  const int blocks = 1 + (g.n8 + kBucketThreads - 1) / kBucketThreads;
+  hipLaunchKernelGGL(bucket_permute_kernel, dim3(blocks), dim3(kBucketThreads), 0, stream, g);
   return hipGetLastError();
 }
 

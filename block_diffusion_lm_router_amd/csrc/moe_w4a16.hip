@@ -155,17 +155,6 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 zc1, _Float16 z
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// Reorder 8 halves (h0..h7) to (h0,h4,h1,h5,h2,h6,h3,h7).
-__device__ __forceinline__ u32x4_t permute8(u32x4_t v) {
-  u32x4_t r;
-  r[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-  r[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-  r[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-  return r;
-}
 
 __device__ __forceinline__ float gelu_tanh(float a) {
   const float u = 0.7978845608028654f * fmaf(0.044715f * a, a * a, a);
@@ -666,13 +655,6 @@ __global__ __launch_bounds__(256) void prep_sz_kernel(const uint16_t* __restrict
   out[i] = v;
 }
 
-// x [T][d] -> xp [T][d] with every 8 consecutive halves reordered to (0,4,1,5,2,6,3,7).
-__global__ __launch_bounds__(256) void permute_x_kernel(const u32x4_t* __restrict__ x,
-                                                        u32x4_t* __restrict__ xp, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) xp[i] = permute8(x[i]);
-}
-
 int grid_blocks(int max_items, int tiles) {
   return ((max_items + kXcds - 1) / kXcds) * kXcds * tiles;
 }
@@ -719,11 +701,8 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.h_out = ws.h;
   a.o_out = nullptr;
   a.out_ld = d_ff;
-  (void)E;
-  const int n8 = T * d_model / 8;
-  hipLaunchKernelGGL(permute_x_kernel, dim3((n8 + 255) / 256), dim3(256), 0, stream,
-                     reinterpret_cast<const u32x4_t*>(x), reinterpret_cast<u32x4_t*>(ws.xp), n8);
-  hipError_t err = hipGetLastError();
+  // Group the assignments by expert and permute x (one launch), then the GEMM.
+  hipError_t err = launch_bucket(T, E, top_k, x, d_model, ws, stream);
   if (err != hipSuccess) return err;
   if (gu.sz) {
     a.tiles = sz_tiles(true, d_model, d_ff);
