@@ -120,7 +120,7 @@ def main():
     for l in range(n_layers):
         w_np = workloads.make_weights(shape, l)
         r_np = workloads.make_router_logits(shape, l)
-        layers.append((bd.MoeWeights.from_numpy(w_np, k, prepare=True),
+        layers.append((bd.MoeWeights.from_numpy(w_np, k, prepare=True, drop_raw=True),
                        torch.from_numpy(r_np).cuda()))
         if l == 0:
             layer0 = (x_np, r_np, w_np)

@@ -42,8 +42,8 @@ class MoeWeightsC(ctypes.Structure):
         ("down_q", _P),
         ("down_scale", _P),
         ("down_zero", _P),
-        ("gate_up_sz", _P),
-        ("down_sz", _P),
+        ("gate_up_packed", _P),
+        ("down_packed", _P),
     ]
 
 
@@ -53,7 +53,7 @@ SIGNATURES = {
     "bd_abi_version": (_I, []),
     "bd_status_string": (ctypes.c_char_p, [_I]),
     "bd_moe_workspace_size": (_SZ, [_I, _W]),
-    "bd_moe_sz_size": (_SZ, [_W, _I]),
+    "bd_moe_packed_size": (_SZ, [_W, _I]),
     "moe_w4a16_prepare": (_I, [_W, _P, _P, _P]),
     "moe_route_topk": (_I, [_W, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_w4a16_gate_up": (_I, [_W, _I, _P, _P, _SZ, _P]),
@@ -159,36 +159,44 @@ class MoeWeights:
         ptrs = {k: _ptr(tensors[k], dtypes.get(k, torch.float16), k) for k in self.KEYS}
         self.c = MoeWeightsC(E, top_k, self.d_model, self.d_ff, group_size,
                              *[ptrs[k] for k in self.KEYS], None, None)
-        self.sz = None
+        self.packed = None
 
-    def prepare(self):
-        """Build the stage-major scale/zero-point arrays (moe_w4a16_prepare) and attach them,
-        so the GEMMs use their 256-row tiles.  Returns self."""
+    def prepare(self, drop_raw=False):
+        """Repack both matrices (moe_w4a16_prepare) and attach the packed streams, so the
+        GEMMs use their 256-row tiles.  drop_raw=True then releases the raw arrays (the GEMMs
+        no longer read them; the 128-row path is gone for this object).  Returns self."""
         lib = load()
-        sizes = [lib.bd_moe_sz_size(self.ref(), m) for m in (0, 1)]
+        sizes = [lib.bd_moe_packed_size(self.ref(), m) for m in (0, 1)]
         if 0 in sizes:
-            raise BdError("bd_moe_sz_size: invalid shape")
+            raise BdError("bd_moe_packed_size: invalid shape")
         dev = self.tensors["gate_up_q"].device
-        self.sz = [torch.empty(n // 2, dtype=torch.int16, device=dev) for n in sizes]
-        _check(lib.moe_w4a16_prepare(self.ref(), ctypes.c_void_p(self.sz[0].data_ptr()),
-                                     ctypes.c_void_p(self.sz[1].data_ptr()), _stream()),
+        self.packed = [torch.empty(n, dtype=torch.uint8, device=dev) for n in sizes]
+        _check(lib.moe_w4a16_prepare(self.ref(), ctypes.c_void_p(self.packed[0].data_ptr()),
+                                     ctypes.c_void_p(self.packed[1].data_ptr()), _stream()),
                "moe_w4a16_prepare")
-        self.c.gate_up_sz = self.sz[0].data_ptr()
-        self.c.down_sz = self.sz[1].data_ptr()
+        self.c.gate_up_packed = self.packed[0].data_ptr()
+        self.c.down_packed = self.packed[1].data_ptr()
+        if drop_raw:
+            for k in self.KEYS:
+                setattr(self.c, k, None)
+            self.tensors = {}
         return self
 
     def unprepare(self):
-        """Detach the stage-major arrays (the GEMMs go back to their 128-row tiles)."""
-        self.c.gate_up_sz = None
-        self.c.down_sz = None
-        self.sz = None
+        """Detach the packed streams (the GEMMs go back to their 128-row tiles)."""
+        if not self.tensors:
+            raise BdError("the raw weight arrays were released")
+        self.c.gate_up_packed = None
+        self.c.down_packed = None
+        self.packed = None
         return self
 
     @classmethod
-    def from_numpy(cls, arrays, top_k, device="cuda", group_size=64, prepare=False):
+    def from_numpy(cls, arrays, top_k, device="cuda", group_size=64, prepare=False,
+                   drop_raw=False):
         t = {k: torch.from_numpy(arrays[k]).to(device) for k in cls.KEYS}
         w = cls(t, top_k, group_size)
-        return w.prepare() if prepare else w
+        return w.prepare(drop_raw=drop_raw) if prepare else w
 
     def ref(self):
         return ctypes.byref(self.c)

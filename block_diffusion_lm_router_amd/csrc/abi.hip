@@ -35,27 +35,29 @@ int check_workspace(const void* ws, size_t have, size_t need) {
   return BD_OK;
 }
 
-int check_gate_up_weights(const bd_moe_weights* w) {
-  if (!w->gate_up_q || !w->gate_up_scale || !w->gate_up_zero) return BD_ERR_NULL;
-  if (!aligned16(w->gate_up_q) || !aligned16(w->gate_up_scale) || !aligned16(w->gate_up_zero) ||
-      !aligned16(w->gate_up_sz))
-    return BD_ERR_ALIGN;
+// A matrix is usable by the GEMMs through its packed stream (then the raw arrays may be NULL)
+// or through its raw nibble, scale and zero-point arrays.
+int check_matrix(const uint8_t* q, const uint16_t* scale, const uint16_t* zero,
+                 const uint8_t* packed) {
+  if (packed) return aligned16(packed) ? BD_OK : BD_ERR_ALIGN;
+  if (!q || !scale || !zero) return BD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(scale) || !aligned16(zero)) return BD_ERR_ALIGN;
   return BD_OK;
+}
+
+int check_gate_up_weights(const bd_moe_weights* w) {
+  return check_matrix(w->gate_up_q, w->gate_up_scale, w->gate_up_zero, w->gate_up_packed);
 }
 
 int check_down_weights(const bd_moe_weights* w) {
-  if (!w->down_q || !w->down_scale || !w->down_zero) return BD_ERR_NULL;
-  if (!aligned16(w->down_q) || !aligned16(w->down_scale) || !aligned16(w->down_zero) ||
-      !aligned16(w->down_sz))
-    return BD_ERR_ALIGN;
-  return BD_OK;
+  return check_matrix(w->down_q, w->down_scale, w->down_zero, w->down_packed);
 }
 
 bd::W4A16Matrix gate_up_of(const bd_moe_weights* w) {
-  return bd::W4A16Matrix{w->gate_up_q, w->gate_up_scale, w->gate_up_zero, w->gate_up_sz};
+  return bd::W4A16Matrix{w->gate_up_q, w->gate_up_scale, w->gate_up_zero, w->gate_up_packed};
 }
 bd::W4A16Matrix down_of(const bd_moe_weights* w) {
-  return bd::W4A16Matrix{w->down_q, w->down_scale, w->down_zero, w->down_sz};
+  return bd::W4A16Matrix{w->down_q, w->down_scale, w->down_zero, w->down_packed};
 }
 
 int check_sample_shape(int P, int V, float temperature) {
@@ -84,24 +86,29 @@ const char* bd_status_string(int status) {
   }
 }
 
-size_t bd_moe_sz_size(const bd_moe_weights* w, int matrix) {
+size_t bd_moe_packed_size(const bd_moe_weights* w, int matrix) {
   if (check_moe_shape(w, 1) != BD_OK || (matrix != 0 && matrix != 1)) return 0;
-  return bd::sz_prep_bytes(matrix == 0, w->num_experts, w->d_model, w->d_ff);
+  return bd::pk_bytes(matrix == 0, w->num_experts, w->d_model, w->d_ff);
 }
 
-int moe_w4a16_prepare(const bd_moe_weights* w, uint16_t* gate_up_sz, uint16_t* down_sz,
+int moe_w4a16_prepare(const bd_moe_weights* w, uint8_t* gate_up_packed, uint8_t* down_packed,
                       void* stream) {
   int st = check_moe_shape(w, 1);
   if (st != BD_OK) return st;
-  if (!gate_up_sz || !down_sz || !w->gate_up_scale || !w->gate_up_zero || !w->down_scale ||
-      !w->down_zero)
+  if (!gate_up_packed || !down_packed || !w->gate_up_q || !w->gate_up_scale ||
+      !w->gate_up_zero || !w->down_q || !w->down_scale || !w->down_zero)
     return BD_ERR_NULL;
-  if (!aligned16(gate_up_sz) || !aligned16(down_sz)) return BD_ERR_ALIGN;
-  st = to_status(bd::launch_prep_sz(gate_up_of(w), true, w->num_experts, w->d_model, w->d_ff,
-                                    gate_up_sz, as_stream(stream)));
+  if (!aligned16(gate_up_packed) || !aligned16(down_packed) || !aligned16(w->gate_up_q) ||
+      !aligned16(w->down_q))
+    return BD_ERR_ALIGN;
+  bd::W4A16Matrix gu = gate_up_of(w), dn = down_of(w);
+  gu.pk = nullptr;
+  dn.pk = nullptr;
+  st = to_status(bd::launch_pack(gu, true, w->num_experts, w->d_model, w->d_ff, gate_up_packed,
+                                 as_stream(stream)));
   if (st != BD_OK) return st;
-  return to_status(bd::launch_prep_sz(down_of(w), false, w->num_experts, w->d_model, w->d_ff,
-                                      down_sz, as_stream(stream)));
+  return to_status(bd::launch_pack(dn, false, w->num_experts, w->d_model, w->d_ff, down_packed,
+                                   as_stream(stream)));
 }
 
 size_t bd_moe_workspace_size(int T, const bd_moe_weights* w) {

@@ -53,13 +53,13 @@ struct W4A16Matrix {
   const uint8_t* q;
   const uint16_t* scale;
   const uint16_t* zero;
-  const uint16_t* sz;   // stage-major scales/zero-points, or nullptr
+  const uint8_t* pk;    // packed stream for the 256-row tiles, or nullptr
 };
 
-int sz_tiles(bool gated, int d_model, int d_ff);
-size_t sz_prep_bytes(bool gated, int E, int d_model, int d_ff);
-hipError_t launch_prep_sz(const W4A16Matrix& m, bool gated, int E, int d_model, int d_ff,
-                          uint16_t* out, hipStream_t stream);
+int pk_tiles(bool gated, int d_model, int d_ff);
+size_t pk_bytes(bool gated, int E, int d_model, int d_ff);
+hipError_t launch_pack(const W4A16Matrix& m, bool gated, int E, int d_model, int d_ff,
+                       uint8_t* out, hipStream_t stream);
 
 hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, int top_k, int T,
                           const uint16_t* x, const MoeWorkspace& ws, hipStream_t stream);

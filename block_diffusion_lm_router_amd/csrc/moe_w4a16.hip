@@ -107,7 +107,7 @@ struct GemmArgs {
   const uint16_t* act;     // gate/up: x [T][K]; down: h [T*k][K] (bucket order); both k-permuted
   const int32_t* perm;     // bucket position -> assignment t*k + j
   const int32_t* items;    // [0] = count, then (expert, first position, tokens)
-  const uint16_t* sz;      // stage-major scales/zero-points (wide kernel), see prep_sz_kernel
+  const uint8_t* pk;       // packed stream (packed kernel), see pack_kernel
   uint16_t* h_out;         // gate/up output [T*k][d_ff]
   float* o_out;            // down output [T*k][d_model]
   int out_ld;
@@ -401,106 +401,100 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(GemmArgs a) {
 }
 
 
-// ------------------------------------------------------------------ wide kernel
-//
-// The same GEMM on 256-row tiles, for weights whose scales and zero-points have been laid
-// out stage-major by prep_sz_kernel.  Per stage a block moves 16 KB of packed weights, at
-// most 8 KB of activation rows and 2 KB of scales/zero-points; the activation rows are shared
-// by twice the weight rows of the 128-row tiles, which halves the bytes the CU's memory
-// pipeline moves per weight byte, and the scales and zero-points stream with the stage
-// instead of filling a per-block table.  Each wave owns 32 whole rows (both groups of every
-// stage), so there is no cross-wave reduction: gate/up wave w holds gate columns 16w..16w+15
-// of the tile and the matching up rows; down wave w holds rows 32w..32w+31.  A tile past the
-// end of the matrix (d_ff % 128 == 64 for gate/up, d_model % 256 == 128 for down) leaves its
-// last four waves without rows: they skip their weight loads and compute and keep their
-// share of the activation and scale loads.
-constexpr int kWdRows = 256;
-constexpr int kWdWBytes = kWdRows * kWRowBytes;                // 16 KB
-constexpr int kWdXBytes = kItemTokens * kXRowBytes;            // 8 KB
-constexpr int kWdSZBytes = kWdRows * 8;                        // 2 KB: [row][s0 s1 z0 z1]
-constexpr int kWdSlot = kWdWBytes + kWdXBytes + kWdSZBytes;
-constexpr int kWdSlots = 3;                                     // two stages in flight
-constexpr int kWdLds = kWdSlots * kWdSlot;
-static_assert(kWdLds <= 80 * 1024, "two wide blocks per CU");
-static_assert(kSG == 2 && kItemTokens == 32 && kXRowBytes == 256, "wide stage geometry");
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  if constexpr (N > 0) {
-    if (n >= N) {
-      wait_vmcnt<N>();
-      return;
-    }
-    wait_vmcnt_upto<N - 1>(n);
-  } else {
-    wait_vmcnt<0>();
-  }
+int grid_blocks(int max_items, int tiles) {
+  return ((max_items + kXcds - 1) / kXcds) * kXcds * tiles;
 }
 
-template <bool GATED, int NMT>
-__device__ __forceinline__ void wide_item(const GemmArgs& a, char* lds, int e, int pos0,
-                                          int mcount, int tile) {
-  constexpr int kDepth = kWdSlots - 1;
+// ------------------------------------------------------------------ packed kernel
+//
+// The same GEMM on 256-row tiles over weights repacked once by pack_kernel.  The packed
+// stream of an (expert, tile) is its stages in order, each 18 KB: for waves w = 0..7 and row
+// sets S = A, B the 1 KB that wave w's lanes consume (lane (n, kb): row n of the set, bytes
+// 8kb..8kb+7 of group 2s and of group 2s+1), then 2 KB of scales and zero-points (for wave w,
+// row n: scale and zero-point of groups 2s and 2s+1 of row n of set A, then of set B).  Every
+// wave therefore streams its own weights, scales and zero-points straight into registers with
+// 16-byte loads over contiguous 1 KB runs, kDepth stages ahead, with no LDS and no barrier on
+// that path; the loads are unconditional, so the compiler counts them exactly.  Only the
+// activation tile of a stage is shared by the 8 waves: each wave loads its share into registers
+// with the stage's other loads and writes it to an LDS double buffer one stage ahead of use.
+//
+// Rows: gate/up wave w holds gate columns 16w..16w+15 of the tile (set A) and the matching up
+// rows (set B); down wave w holds rows 32w..32w+31 (A: first 16, B: next 16).  A tile past the
+// end of the matrix (d_ff % 128 == 64, d_model % 256 == 128) leaves waves 4..7 without rows:
+// they re-load wave w-4's stream (L2 hits), keep their activation duties and skip compute.
+constexpr int kPkRows = 256;
+constexpr int kPkWBytes = kPkRows * kWRowBytes;                 // 16 KB of nibbles per stage
+constexpr int kPkSZBytes = kPkRows * 8;                         // 2 KB of scales/zero-points
+constexpr int kPkStage = kPkWBytes + kPkSZBytes;                // 18 KB
+constexpr int kPkChunks = kPkStage / 16;
+constexpr int kPkDepth = 3;                                     // stages in registers ahead
+constexpr int kPkXSlot = kItemTokens * kXRowBytes;              // 8 KB
+static_assert(kSG == 2 && kItemTokens == 32 && kXRowBytes == 256, "packed stage geometry");
+
+struct PkStage {
+  u32x4_t wa, wb, sz, x;
+};
+
+template <bool GATED, int NMT, int NSC>
+__device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e, int pos0,
+                                            int mcount, int tile) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int kb = lane >> 4;
   const int G = a.K >> 6;
-  const int NS = (G + 1) >> 1;
-  const size_t rowbytes = (size_t)(a.K >> 1);
+  const int NS = NSC > 0 ? NSC : (G + 1) >> 1;
   const DequantConsts dq = dequant_consts();
 
-  // Rows of this wave (set A, set B) within the tile and whether they exist.
-  const int rows_here = GATED ? min(128, a.d_ff - tile * 128) : min(kWdRows, a.R - tile * kWdRows);
+  const int rows_here = GATED ? min(128, a.d_ff - tile * 128) : min(kPkRows, a.R - tile * kPkRows);
   const bool valid = GATED ? wave * 16 < rows_here : wave * 32 < rows_here;
-  const int rA = GATED ? wave * 16 + n : wave * 32 + n;           // tile row of set A
-  const int rB = GATED ? 128 + wave * 16 + n : wave * 32 + 16 + n;
-  // Load duties: weights (valid waves, two loads), activation rows 4w..4w+3 (waves below
-  // 4 * NMT), scales/zero-points rows 128(w-6).. (waves 6 and 7).
-  const bool xload = wave < 4 * NMT;
-  const bool szload = wave >= 6;
-  const int my_loads = (valid ? 2 : 0) + (xload ? 1 : 0) + (szload ? 1 : 0);
+  const int lw = valid ? wave : wave - 4;              // whose stream this wave loads
+  // Loads address a block-uniform base plus a 32-bit lane offset, so that they take the
+  // scalar-base form and no 64-bit address registers are held per stream.
+  const char* pk = reinterpret_cast<const char*>(a.pk) +
+                   ((size_t)e * a.tiles + tile) * (size_t)NS * kPkStage;
+  const uint32_t wa_off = ((lw * 2 + 0) * 64 + lane) * 16;
+  const uint32_t sz_off = kPkWBytes + (lw * 16 + n) * 16;
 
-  // Weight load of set S: tile rows base..base+15, lane -> (row lane/4, chunk slot lane%4)
-  // holding global chunk (lane%4) ^ wswz(row).
-  const int wr = lane >> 2;
-  const int wchunk = (lane & 3) ^ wswz(wr);
-  auto mrow = [&](int tr) -> int {       // matrix row of tile row tr (of this expert)
-    if (GATED) return (tr < 128 ? 0 : a.d_ff) + tile * 128 + (tr & 127);
-    return tile * kWdRows + tr;
-  };
-  const uint8_t* wsrcA = a.q + ((size_t)e * a.R + mrow(rA - n + wr)) * rowbytes;
-  const uint8_t* wsrcB = a.q + ((size_t)e * a.R + mrow(rB - n + wr)) * rowbytes;
-  // Activation load: rows 4w + lane/16.
-  const int xm = wave * 4 + (lane >> 4);
-  const int xchunk = (lane & 15) ^ xswz(xm);
-  const uint16_t* xsrc;
+  // Activation share: NMT = 2: rows 4w + lane/16, 16 bytes at chunk lane % 16 of the stage;
+  // NMT = 1: rows 2w + lane/32, 8 bytes (half lane % 2 of chunk (lane % 32) / 2).
+  const int xm = NMT == 2 ? wave * 4 + (lane >> 4) : wave * 2 + (lane >> 5);
+  const int xc = NMT == 2 ? (lane & 15) : ((lane & 31) >> 1);
+  const int xh = NMT == 2 ? 0 : (lane & 1);
+  uint32_t x_off;
   {
     const int mm = min(xm, mcount - 1);
     const int row = GATED ? a.perm[pos0 + mm] / a.top_k : pos0 + mm;
-    xsrc = a.act + (size_t)row * a.K;
+    x_off = ((uint32_t)row * (uint32_t)a.K + xc * 8 + xh * 4) * 2;
   }
-  // Scale/zero-point load: stage-major block of this (expert, tile), 2 KB per stage.
-  const char* szsrc = reinterpret_cast<const char*>(a.sz) +
-                      ((size_t)e * a.tiles + tile) * NS * kWdSZBytes + max(wave - 6, 0) * 1024 + lane * 16;
+  const bool x_tail = xc * 8 >= (a.K & 127);             // chunk past K in a half stage
+  const char* act = reinterpret_cast<const char*>(a.act);
+  const int xdst = xm * kXRowBytes + ((xc ^ xswz(xm)) << 4) + xh * 8;
 
-  auto dma = [&](int c, int slot) {
-    char* st = lds + slot * kWdSlot;
-    if (valid) {
-      int byte = c * kWRowBytes + wchunk * 16;
-      if ((byte >> 5) >= G) byte &= 31;
-      __builtin_amdgcn_global_load_lds(wsrcA + byte, st + (wave * 2 + 0) * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(wsrcB + byte, st + (wave * 2 + 1) * 1024, 16, 0, 0);
+  auto load = [&](int c) {
+    const int cl = min(c, NS - 1);
+    const char* st = pk + (size_t)cl * kPkStage;
+    // the half stage past an odd G re-reads the row's first chunk (never used)
+    const uint32_t xo = x_off + ((cl * kStageK * 2 + 256 > a.K * 2 && x_tail) ? 0u : (uint32_t)cl * kStageK * 2);
+    PkStage r;
+    if (NMT == 2) {
+      r.x = *reinterpret_cast<const u32x4_t*>(act + xo);
+    } else {
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(act + xo);
+      r.x = u32x4_t{v[0], v[1], 0u, 0u};
     }
-    if (xload) {
-      int col = c * kStageK + xchunk * 8;
-      if (col >= a.K) col &= 63;
-      __builtin_amdgcn_global_load_lds(xsrc + col, st + kWdWBytes + wave * 1024, 16, 0, 0);
-    }
-    if (szload)
-      __builtin_amdgcn_global_load_lds(szsrc + (size_t)c * kWdSZBytes,
-                                       st + kWdWBytes + kWdXBytes + (wave - 6) * 1024, 16, 0, 0);
+    r.wa = *reinterpret_cast<const u32x4_t*>(st + wa_off);
+    r.wb = *reinterpret_cast<const u32x4_t*>(st + wa_off + 1024);
+    r.sz = *reinterpret_cast<const u32x4_t*>(st + sz_off);
+    return r;
+  };
+  auto put_x = [&](const PkStage& r, int slot) {
+    char* d = lds + slot * kPkXSlot + xdst;
+    if (NMT == 2)
+      *reinterpret_cast<u32x4_t*>(d) = r.x;
+    else
+      *reinterpret_cast<u32x2_t*>(d) = u32x2_t{r.x[0], r.x[1]};
   };
 
   float4_t totA[NMT], totB[NMT];
@@ -508,30 +502,23 @@ __device__ __forceinline__ void wide_item(const GemmArgs& a, char* lds, int e, i
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) totA[mt] = totB[mt] = zero4;
 
-  auto compute = [&](int c, int slot) {
-    const char* st = lds + slot * kWdSlot;
-    const char* wA = st + (wave * 2 + 0) * 1024 + n * kWRowBytes;
-    const char* wB = st + (wave * 2 + 1) * 1024 + n * kWRowBytes;
-    const char* xt = st + kWdWBytes;
-    const char* sz = st + kWdWBytes + kWdXBytes;
-    const half4_t szA = __builtin_bit_cast(half4_t, *reinterpret_cast<const u32x2_t*>(sz + rA * 8));
-    const half4_t szB = __builtin_bit_cast(half4_t, *reinterpret_cast<const u32x2_t*>(sz + rB * 8));
+  auto compute = [&](const PkStage& r, int c, int slot) {
+    const char* xt = lds + slot * kPkXSlot;
+    // [scale g0, scale g1, zero g0, zero g1] of the lane's row in set A, then set B
+    const half4_t szA = __builtin_bit_cast(half4_t, u32x2_t{r.sz[0], r.sz[1]});
+    const half4_t szB = __builtin_bit_cast(half4_t, u32x2_t{r.sz[2], r.sz[3]});
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int g = 2 * c + j;
       if (g >= G) break;
-      const int chunk = 2 * j + (kb >> 1);
-      const u32x2_t wa = *reinterpret_cast<const u32x2_t*>(wA + ((chunk ^ wswz(n)) << 4) + ((kb & 1) << 3));
-      const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(wB + ((chunk ^ wswz(n)) << 4) + ((kb & 1) << 3));
-      const _Float16 sA = szA[j], zA = szA[2 + j];
-      const _Float16 sB = szB[j], zB = szB[2 + j];
+      const _Float16 zA = szA[2 + j], zB = szB[2 + j];
       const _Float16 za1 = -((_Float16)1024.f + zA), za2 = -((_Float16)64.f + zA);
       const _Float16 zb1 = -((_Float16)1024.f + zB), zb2 = -((_Float16)64.f + zB);
-      const float fsA = (float)sA, fsB = (float)sB;
-      const half8_t bA0 = dequant8(wa[0], za1, za2, dq);
-      const half8_t bA1 = dequant8(wa[1], za1, za2, dq);
-      const half8_t bB0 = dequant8(wb[0], zb1, zb2, dq);
-      const half8_t bB1 = dequant8(wb[1], zb1, zb2, dq);
+      const float fsA = (float)szA[j], fsB = (float)szB[j];
+      const half8_t bA0 = dequant8(r.wa[2 * j], za1, za2, dq);
+      const half8_t bA1 = dequant8(r.wa[2 * j + 1], za1, za2, dq);
+      const half8_t bB0 = dequant8(r.wb[2 * j], zb1, zb2, dq);
+      const half8_t bB1 = dequant8(r.wb[2 * j + 1], zb1, zb2, dq);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int m = mt * 16 + n;
@@ -544,32 +531,47 @@ __device__ __forceinline__ void wide_item(const GemmArgs& a, char* lds, int e, i
         float4_t accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bB0, zero4, 0, 0, 0);
         accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bB1, accB, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          totA[mt][r] = fmaf(fsA, accA[r], totA[mt][r]);
-          totB[mt][r] = fmaf(fsB, accB[r], totB[mt][r]);
+        for (int q = 0; q < 4; ++q) {
+          totA[mt][q] = fmaf(fsA, accA[q], totA[mt][q]);
+          totB[mt][q] = fmaf(fsB, accB[q], totB[mt][q]);
         }
       }
     }
   };
 
-  // Same pipeline as the tile kernel: kDepth stages in flight, every wave issuing its fixed
-  // share of loads every stage (stages past the end re-read the last one into ring slots no
-  // stage reads), so waiting until at most my_loads * (kDepth - 1) of this wave's loads are
-  // outstanding completes the stage's loads; the barrier publishes every wave's.
+  // Stage c sits in buf[c % kPkDepth] from iteration c - kPkDepth on; its activation share is
+  // written to LDS slot c % 2 during iteration c - 1, and the barrier that ends iteration c - 1
+  // publishes it.  The barrier ending iteration c also frees slot c % 2 for stage c + 2.
+  PkStage buf[kPkDepth];
 #pragma unroll
-  for (int s = 0; s < kDepth; ++s) dma(min(s, NS - 1), s);
-  for (int c = 0; c < NS; c += kWdSlots) {
+  for (int s2 = 0; s2 < kPkDepth; ++s2) buf[s2] = load(s2);
+  put_x(buf[0], 0);
+  lds_barrier();
+  if constexpr (NSC > 0) {
+    // Contraction dims with a specialisation: the stage loop is unrolled completely, so
+    // every stage's registers are distinct values in straight-line code and each wait the
+    // compiler places covers exactly the loads that stage needs.
 #pragma unroll
-    for (int u = 0; u < kWdSlots; ++u) {
-      const int cc = c + u;
-      if (cc >= NS) break;
-      wait_vmcnt_upto<4 * (kDepth - 1)>(my_loads * (kDepth - 1));
-      lds_barrier();
-      dma(min(cc + kDepth, NS - 1), (u + kDepth) % kWdSlots);
-      if (valid) compute(cc, u);
+    for (int cc = 0; cc < NSC; ++cc) {
+      if (cc + 1 < NSC) put_x(buf[(cc + 1) % kPkDepth], (cc + 1) & 1);
+      if (valid) compute(buf[cc % kPkDepth], cc, cc & 1);
+      if (cc + kPkDepth < NSC) buf[cc % kPkDepth] = load(cc + kPkDepth);
+      if (cc + 1 < NSC) lds_barrier();
+    }
+  } else {
+    // Other dims: whole rounds of kPkDepth stages (stages past the end load the last stage
+    // again and skip compute), the same loads in the same order on every path.
+    for (int c = 0; c < NS; c += kPkDepth) {
+#pragma unroll
+      for (int u = 0; u < kPkDepth; ++u) {
+        const int cc = c + u;
+        put_x(buf[(u + 1) % kPkDepth], (u + 1 + c) & 1);
+        if (valid && cc < NS) compute(buf[u], cc, (u + c) & 1);
+        buf[u] = load(cc + kPkDepth);
+        lds_barrier();
+      }
     }
   }
-  wait_vmcnt<0>();   // no LDS write may still be in flight when the block ends
   if (!valid) return;
 
   // Epilogue: D lane layout = tokens 4kb..4kb+3 of row n.
@@ -587,7 +589,7 @@ __device__ __forceinline__ void wide_item(const GemmArgs& a, char* lds, int e, i
         a.h_out[(size_t)(pos0 + m) * a.d_ff + pcol] = __builtin_bit_cast(uint16_t, h16);
       } else {
         const int slot = a.perm[pos0 + m];
-        const int row = tile * kWdRows + wave * 32 + n;
+        const int row = tile * kPkRows + wave * 32 + n;
         a.o_out[(size_t)slot * a.out_ld + row] = totA[mt][r];
         a.o_out[(size_t)slot * a.out_ld + row + 16] = totB[mt][r];
       }
@@ -595,9 +597,10 @@ __device__ __forceinline__ void wide_item(const GemmArgs& a, char* lds, int e, i
   }
 }
 
-template <bool GATED>
-__global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kWdLds];
+// NSC > 0: compiled for exactly NSC stages (the caller checks); 0: any number of stages.
+template <bool GATED, int NSC>
+__global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kPkXSlot];
   const int b = blockIdx.x;
   const int local = b / kXcds;
   const int item = (local / a.tiles) * kXcds + (b % kXcds);
@@ -607,79 +610,105 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(GemmArgs a) {
   const int pos0 = a.items[2 + 3 * item];
   const int mcount = a.items[3 + 3 * item];
   if (mcount > 16)
-    wide_item<GATED, 2>(a, lds, e, pos0, mcount, tile);
+    packed_item<GATED, 2, NSC>(a, lds, e, pos0, mcount, tile);
   else
-    wide_item<GATED, 1>(a, lds, e, pos0, mcount, tile);
+    packed_item<GATED, 1, NSC>(a, lds, e, pos0, mcount, tile);
 }
 
-// Stage-major scales and zero-points for the wide kernel.  Entry (e, tile, stage s, row r)
-// is 4 halves: scale and zero-point of groups 2s and 2s+1 (0 past the last group) of tile
-// row r (gate/up: r < 128 the gate row of column 128 tile + r, else the matching up row;
-// down: row 256 tile + r), 0 for rows past the matrix.  One thread per entry.
-__global__ __launch_bounds__(256) void prep_sz_kernel(const uint16_t* __restrict__ scale,
-                                                      const uint16_t* __restrict__ zero, int R,
-                                                      int G, int tiles, int NS, int gated,
-                                                      int d_ff, size_t entries,
-                                                      u32x2_t* __restrict__ out) {
+// Stage counts with a fully unrolled kernel: the contraction dims 2816 (gate/up) and 704
+// (down) of the 26B-A4B expert shape.
+template <bool GATED>
+void launch_packed(const GemmArgs& a, int max_items, hipStream_t stream) {
+  const int NS = (a.K / 64 + 1) / 2;
+  const dim3 grid(grid_blocks(max_items, a.tiles)), block(kThreads);
+  if (NS == 22)
+    hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 22>), grid, block, 0, stream, a);
+  else if (NS == 6)
+    hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 6>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 0>), grid, block, 0, stream, a);
+}
+
+// Repacking into the packed stream (layout above).  One thread per 16-byte chunk of the output;
+// rows past the matrix and the group past an odd G are written as zeros.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ scale,
+                                                   const uint16_t* __restrict__ zero, int R, int K,
+                                                   int tiles, int gated, int d_ff, size_t chunks,
+                                                   u32x4_t* __restrict__ out) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= entries) return;
-  const int r = (int)(i % kWdRows);
-  const size_t q = i / kWdRows;
-  const int s = (int)(q % NS);
-  const int tile = (int)((q / NS) % tiles);
-  const size_t e = q / ((size_t)NS * tiles);
-  int row;
-  bool ok;
-  if (gated) {
-    const int col = tile * 128 + (r & 127);
-    ok = col < d_ff;
-    row = (r < 128 ? 0 : d_ff) + col;
-  } else {
-    row = tile * kWdRows + r;
-    ok = row < R;
-  }
+  if (i >= chunks) return;
+  const int G = K / 64, NS = (G + 1) / 2;
+  const int ch = (int)(i % kPkChunks);
+  const size_t qs = i / kPkChunks;
+  const int s = (int)(qs % NS);
+  const int tile = (int)((qs / NS) % tiles);
+  const size_t e = qs / ((size_t)NS * tiles);
+  // matrix row of tile row tr, or -1 past the matrix
+  auto mrow = [&](int tr) -> int {
+    if (gated) {
+      const int col = tile * 128 + (tr & 127);
+      return col < d_ff ? (tr < 128 ? 0 : d_ff) + col : -1;
+    }
+    const int row = tile * kPkRows + tr;
+    return row < R ? row : -1;
+  };
+  auto tile_row = [&](int w, int set, int nn) {
+    return gated ? (set ? 128 : 0) + w * 16 + nn : w * 32 + set * 16 + nn;
+  };
   const int g0 = 2 * s, g1 = 2 * s + 1;
-  uint32_t s0 = 0, s1 = 0, z0 = 0, z1 = 0;
-  if (ok) {
-    const size_t base = (e * R + row) * (size_t)G;
-    s0 = scale[base + g0];
-    z0 = zero[base + g0];
-    if (g1 < G) {
-      s1 = scale[base + g1];
-      z1 = zero[base + g1];
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (ch < kPkWBytes / 16) {
+    const int w = ch / 128, set = (ch / 64) & 1, l = ch & 63;
+    const int row = mrow(tile_row(w, set, l & 15));
+    const int kbl = l >> 4;
+    if (row >= 0) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(q + ((size_t)e * R + row) * (K / 2));
+      v[0] = src[(g0 * 32 + kbl * 8) / 4];
+      v[1] = src[(g0 * 32 + kbl * 8) / 4 + 1];
+      if (g1 < G) {
+        v[2] = src[(g1 * 32 + kbl * 8) / 4];
+        v[3] = src[(g1 * 32 + kbl * 8) / 4 + 1];
+      }
+    }
+  } else {
+    const int idx = ch - kPkWBytes / 16;
+    const int w = idx / 16, nn = idx & 15;
+#pragma unroll
+    for (int set = 0; set < 2; ++set) {
+      const int row = mrow(tile_row(w, set, nn));
+      if (row < 0) continue;
+      const size_t base = ((size_t)e * R + row) * G;
+      const uint32_t s0 = scale[base + g0], z0 = zero[base + g0];
+      const uint32_t s1 = g1 < G ? scale[base + g1] : 0u, z1 = g1 < G ? zero[base + g1] : 0u;
+      v[2 * set] = s0 | (s1 << 16);
+      v[2 * set + 1] = z0 | (z1 << 16);
     }
   }
-  u32x2_t v;
-  v[0] = s0 | (s1 << 16);
-  v[1] = z0 | (z1 << 16);
   out[i] = v;
 }
 
-int grid_blocks(int max_items, int tiles) {
-  return ((max_items + kXcds - 1) / kXcds) * kXcds * tiles;
-}
 
 }  // namespace
 
-int sz_tiles(bool gated, int d_model, int d_ff) {
-  return gated ? (d_ff + 127) / 128 : (d_model + kWdRows - 1) / kWdRows;
+int pk_tiles(bool gated, int d_model, int d_ff) {
+  return gated ? (d_ff + 127) / 128 : (d_model + kPkRows - 1) / kPkRows;
 }
 
-size_t sz_prep_bytes(bool gated, int E, int d_model, int d_ff) {
+size_t pk_bytes(bool gated, int E, int d_model, int d_ff) {
   const int K = gated ? d_model : d_ff;
   const int NS = (K / 64 + 1) / 2;
-  return (size_t)E * sz_tiles(gated, d_model, d_ff) * NS * kWdSZBytes;
+  return (size_t)E * pk_tiles(gated, d_model, d_ff) * NS * kPkStage;
 }
 
-hipError_t launch_prep_sz(const W4A16Matrix& m, bool gated, int E, int d_model, int d_ff,
-                          uint16_t* out, hipStream_t stream) {
+hipError_t launch_pack(const W4A16Matrix& m, bool gated, int E, int d_model, int d_ff,
+                       uint8_t* out, hipStream_t stream) {
   const int K = gated ? d_model : d_ff;
   const int R = gated ? 2 * d_ff : d_model;
-  const int G = K / 64, NS = (G + 1) / 2, tiles = sz_tiles(gated, d_model, d_ff);
-  const size_t entries = (size_t)E * tiles * NS * kWdRows;
-  hipLaunchKernelGGL(prep_sz_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, stream,
-                     m.scale, m.zero, R, G, tiles, NS, gated ? 1 : 0, d_ff, entries,
-                     reinterpret_cast<u32x2_t*>(out));
+  const size_t chunks = pk_bytes(gated, E, d_model, d_ff) / 16;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+                     m.q, m.scale, m.zero, R, K, pk_tiles(gated, d_model, d_ff), gated ? 1 : 0,
+                     d_ff, chunks, reinterpret_cast<u32x4_t*>(out));
   return hipGetLastError();
 }
 
@@ -697,17 +726,16 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.act = ws.xp;
   a.perm = ws.perm;
   a.items = ws.items;
-  a.sz = gu.sz;
+  a.pk = gu.pk;
   a.h_out = ws.h;
   a.o_out = nullptr;
   a.out_ld = d_ff;
   // Group the assignments by expert and permute x (one launch), then the GEMM.
   hipError_t err = launch_bucket(T, E, top_k, x, d_model, ws, stream);
   if (err != hipSuccess) return err;
-  if (gu.sz) {
-    a.tiles = sz_tiles(true, d_model, d_ff);
-    hipLaunchKernelGGL(w4a16_wide_kernel<true>, dim3(grid_blocks(ws.max_items, a.tiles)),
-                       dim3(kThreads), 0, stream, a);
+  if (gu.pk) {
+    a.tiles = pk_tiles(true, d_model, d_ff);
+    launch_packed<true>(a, ws.max_items, stream);
   } else {
     hipLaunchKernelGGL(w4a16_gemm_kernel<true>, dim3(grid_blocks(ws.max_items, a.tiles)),
                        dim3(kThreads), 0, stream, a);
@@ -729,16 +757,15 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
   a.act = ws.h;
   a.perm = ws.perm;
   a.items = ws.items;
-  a.sz = dn.sz;
+  a.pk = dn.pk;
   a.h_out = nullptr;
   a.o_out = expert_out;
   a.out_ld = d_model;
   (void)E;
   (void)T;
-  if (dn.sz) {
-    a.tiles = sz_tiles(false, d_model, d_ff);
-    hipLaunchKernelGGL(w4a16_wide_kernel<false>, dim3(grid_blocks(ws.max_items, a.tiles)),
-                       dim3(kThreads), 0, stream, a);
+  if (dn.pk) {
+    a.tiles = pk_tiles(false, d_model, d_ff);
+    launch_packed<false>(a, ws.max_items, stream);
   } else {
     hipLaunchKernelGGL(w4a16_gemm_kernel<false>, dim3(grid_blocks(ws.max_items, a.tiles)),
                        dim3(kThreads), 0, stream, a);

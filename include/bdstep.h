@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 2
+#define BD_ABI_VERSION 3
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -83,11 +83,12 @@ typedef enum {
  * rounded to the nearest integer first.
  * Supported: group_size == 64, d_model % 128 == 0, d_ff % 64 == 0, d_model and d_ff <= 4096.
  *
- * gate_up_sz / down_sz (optional, NULL when absent): the same scales and zero-points laid out
- * stage-major by moe_w4a16_prepare, so that a GEMM streams them with its weights.  A GEMM
- * whose array is present runs on 256-row tiles; without it, on 128-row tiles reading scale
- * and zero directly.  Both contract exact fp16 (q - z) per 64-group and scale each group's
- * sum in fp32; they differ only in the order of the fp32 sums.
+ * gate_up_packed / down_packed (optional, NULL when absent): the matrix repacked once by
+ * moe_w4a16_prepare into the stream the 256-row GEMM tiles consume.  A GEMM whose packed
+ * stream is present reads only that stream (its q, scale and zero pointers may then be NULL);
+ * without it the GEMM runs on 128-row tiles over q, scale and zero.  Both contract exact fp16
+ * (q - z) per 64-group and scale each group's sum in fp32; they differ only in the order of
+ * the fp32 sums.
  */
 typedef struct bd_moe_weights {
   int32_t num_experts; /* E, 1..256          */
@@ -101,8 +102,8 @@ typedef struct bd_moe_weights {
   const uint8_t* down_q;
   const uint16_t* down_scale;
   const uint16_t* down_zero;
-  const uint16_t* gate_up_sz;  /* optional, bd_moe_sz_size(w, 0) bytes, 16-byte aligned */
-  const uint16_t* down_sz;     /* optional, bd_moe_sz_size(w, 1) bytes, 16-byte aligned */
+  const uint8_t* gate_up_packed;  /* optional, bd_moe_packed_size(w, 0) bytes, 16-byte aligned */
+  const uint8_t* down_packed;     /* optional, bd_moe_packed_size(w, 1) bytes, 16-byte aligned */
 } bd_moe_weights;
 
 /* Library ABI version (BD_ABI_VERSION of the build). */
@@ -114,23 +115,31 @@ const char* bd_status_string(int status);
 /* ------------------------------------------------------------------ MoE FFN */
 
 /*
- * Bytes of the stage-major scale/zero-point array of the gate/up matrix (matrix 0) or the
- * down matrix (matrix 1); 0 if the shape is invalid.
+ * Bytes of the packed stream of the gate/up matrix (matrix 0) or the down matrix (matrix 1);
+ * 0 if the shape is invalid.
  */
-size_t bd_moe_sz_size(const bd_moe_weights* w, int matrix);
+size_t bd_moe_packed_size(const bd_moe_weights* w, int matrix);
 
 /*
- * One-time preparation of a layer's weights for the 256-row GEMM tiles: writes the scales
- * and zero-points of both matrices, stage-major, into the caller's buffers (sizes from
- * bd_moe_sz_size; 16-byte aligned).  Reads only w's scale and zero arrays.  For every
- * (expert e, tile t, stage s of 128 contraction elements, tile row r) the entry is the four
- * fp16 values scale[row][2s], scale[row][2s+1], zero[row][2s], zero[row][2s+1] (0 past the
- * last group), where the tile row r of gate/up is the gate row of column 128t + r for r < 128
- * and the up row of column 128t + r - 128 otherwise, and of down the row 256t + r; rows past
- * the matrix hold 0.  Layout [E][tiles][stages][256][4].  Store the result in gate_up_sz and
- * down_sz of the weights struct for the GEMM entry points to use it.
+ * One-time repacking of a layer's weights for the 256-row GEMM tiles, into the caller's
+ * buffers (sizes from bd_moe_packed_size; 16-byte aligned).  Reads w's q, scale and zero
+ * arrays of both matrices (all required here).
+ *
+ * A tile covers 256 tile rows: for gate/up, tile row r < 128 is the gate row of column
+ * 128t + r and tile row r >= 128 the up row of column 128t + r - 128; for down, tile row r
+ * is row 256t + r.  Rows past the matrix and the group past an odd number of groups are
+ * written as zeros.  The stream is [E][tiles][stages][18432 bytes]; a stage covers 128
+ * contraction elements (groups 2s and 2s+1) and holds
+ *   bytes 0..16383: for w = 0..7, set S = 0, 1, lane l = 0..63 (n = l % 16, b = l / 16), at
+ *     ((2w + S) * 64 + l) * 16: packed bytes 8b..8b+7 of group 2s, then of group 2s+1, of
+ *     tile row R(w, S, n), where R = 128S + 16w + n for gate/up and 32w + 16S + n for down;
+ *   bytes 16384..18431: for w = 0..7, n = 0..15, at 16384 + (16w + n) * 16: the fp16 values
+ *     scale[2s], scale[2s+1], zero[2s], zero[2s+1] of tile row R(w, 0, n), then the same four
+ *     of tile row R(w, 1, n).
+ * Store the results in gate_up_packed and down_packed of the weights struct for the GEMM
+ * entry points to use them.
  */
-int moe_w4a16_prepare(const bd_moe_weights* w, uint16_t* gate_up_sz, uint16_t* down_sz,
+int moe_w4a16_prepare(const bd_moe_weights* w, uint8_t* gate_up_packed, uint8_t* down_packed,
                       void* stream);
 
 /*

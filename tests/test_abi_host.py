@@ -134,17 +134,17 @@ def test_sampler_validation(lib):
 def test_prepare_sizes_and_validation(lib):
     w = _weights()
     ref = ctypes.byref(w)
-    # [E][tiles][stages][256 rows][4 halves]: gate/up 6 tiles of 128 columns x 22 stages,
-    # down 11 tiles of 256 rows x 6 stages (11 groups: the last stage holds one).
-    assert lib.bd_moe_sz_size(ref, 0) == 128 * 6 * 22 * 256 * 8
-    assert lib.bd_moe_sz_size(ref, 1) == 128 * 11 * 6 * 256 * 8
-    assert lib.bd_moe_sz_size(ref, 2) == 0
+    # [E][tiles][stages][18432 bytes]: gate/up 6 tiles of 128 columns x 22 stages, down 11
+    # tiles of 256 rows x 6 stages (11 groups: the last stage holds one).
+    assert lib.bd_moe_packed_size(ref, 0) == 128 * 6 * 22 * 18432
+    assert lib.bd_moe_packed_size(ref, 1) == 128 * 11 * 6 * 18432
+    assert lib.bd_moe_packed_size(ref, 2) == 0
     p = ctypes.c_void_p(0x1000)
     assert lib.moe_w4a16_prepare(ref, None, p, None) == 1              # BD_ERR_NULL
     assert lib.moe_w4a16_prepare(ref, ctypes.c_void_p(0x1008), p, None) == 3   # BD_ERR_ALIGN
     bad = _weights(g=128)
     assert lib.moe_w4a16_prepare(ctypes.byref(bad), p, p, None) == 5   # BD_ERR_UNSUPPORTED
-    # a misaligned prepared array is rejected by the GEMM entry points before any launch
-    w.gate_up_sz = 0x1008
+    # a misaligned packed stream is rejected by the GEMM entry points before any launch
+    w.gate_up_packed = 0x1008
     ws = ctypes.c_void_p(0x10000)
     assert lib.moe_w4a16_gate_up(ref, 256, p, ws, 1 << 30, None) == 3

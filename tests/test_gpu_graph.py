@@ -50,12 +50,13 @@ def _poison(bufs):
     y.fill_(float("nan"))
 
 
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "packed256"])
 @pytest.mark.parametrize("shape", [workloads.TINY_LAYER, workloads.SHORT_LAYER],
                          ids=["tiny", "short"])
-def test_moe_layer_graph_replays(bd, shape):
+def test_moe_layer_graph_replays(bd, shape, prepared):
     import torch
-    say("graph moe layer", shape.tokens, shape.d_model, shape.experts, shape.top_k)
-    w = bd.MoeWeights.from_numpy(workloads.make_weights(shape, 0), shape.top_k)
+    say("graph moe layer", shape.tokens, shape.d_model, shape.experts, shape.top_k, prepared)
+    w = bd.MoeWeights.from_numpy(workloads.make_weights(shape, 0), shape.top_k, prepare=prepared)
     x = torch.from_numpy(workloads.make_activations(shape)).cuda()
     logits = torch.from_numpy(workloads.make_router_logits(shape, 0)).cuda()
     # a second routing of the same layer, run eagerly between replays to disturb the workspace

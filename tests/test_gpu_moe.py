@@ -38,12 +38,12 @@ class Layer:
         self.logits_d = torch.from_numpy(self.logits).cuda()
 
     def run(self, bd, fused=True, prepared=True):
-        """One FFN pass; prepared=True uses the stage-major scale/zero arrays (256-row GEMM
-        tiles), False the raw scale and zero arrays (128-row tiles)."""
+        """One FFN pass; prepared=True uses the packed streams (256-row GEMM tiles), False the
+        raw nibble, scale and zero arrays (128-row tiles)."""
         import torch
-        if prepared and self.w.sz is None:
+        if prepared and self.w.packed is None:
             self.w.prepare()
-        elif not prepared and self.w.sz is not None:
+        elif not prepared and self.w.packed is not None:
             self.w.unprepare()
         T, k, d = self.shape.tokens, self.shape.top_k, self.shape.d_model
         ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
@@ -99,7 +99,7 @@ def check_layer(layer, got, tokens=None):
     return check_ffn_close(y[rows].astype(np.float64), y_ref, "y")
 
 
-@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "packed256"])
 def test_tiny_layer(bd, prepared):
     say("tiny layer", prepared)
     layer = Layer(bd, workloads.TINY_LAYER)
@@ -111,7 +111,7 @@ def test_tiny_layer(bd, prepared):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "packed256"])
 @pytest.mark.parametrize("T,E,k,d,f", [(1, 4, 1, 128, 64), (3, 8, 3, 256, 192),
                                        (100, 4, 2, 128, 64), (77, 16, 4, 384, 128),
                                        (250, 2, 2, 128, 64)])
@@ -124,7 +124,7 @@ def test_ragged_buckets(bd, T, E, k, d, f, prepared):
     check_layer(layer, layer.run(bd, prepared=prepared))
 
 
-@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "packed256"])
 @pytest.mark.parametrize("T,E,k,d,f", [(96, 16, 4, 1024, 640), (200, 8, 2, 768, 576),
                                        (512, 8, 8, 640, 576), (2048, 4, 4, 640, 576),
                                        (33, 128, 8, 2816, 704)])
@@ -137,39 +137,82 @@ def test_larger_shapes(bd, T, E, k, d, f, prepared):
     check_layer(layer, layer.run(bd, prepared=prepared))
 
 
-@pytest.mark.parametrize("d,f,E", [(256, 128, 8), (2816, 704, 4), (640, 576, 3)])
-def test_prepared_scales_layout(bd, d, f, E):
-    """moe_w4a16_prepare writes exactly the documented stage-major layout (bit-exact against a
-    re-indexing of the raw arrays)."""
+def packed_stream(w_np, which, d, f, E):
+    """The packed stream moe_w4a16_prepare documents, rebuilt by re-indexing the raw arrays:
+    [E][tiles][stages][18432 B], per stage the nibble runs of (wave, set, lane) and then the
+    (scale, zero) pairs of (wave, row)."""
+    name = "gate_up" if which == 0 else "down"
+    q = w_np[name + "_q"]
+    sc = w_np[name + "_scale"].view(np.uint16)
+    ze = w_np[name + "_zero"].view(np.uint16)
+    K = d if which == 0 else f
+    R = 2 * f if which == 0 else d
+    G, tiles = K // 64, (-(-f // 128) if which == 0 else -(-d // 256))
+    NS = (G + 1) // 2
+
+    def mrow(t, tr):
+        if which == 0:
+            col = 128 * t + (tr & 127)
+            return (0 if tr < 128 else f) + col if col < f else -1
+        row = 256 * t + tr
+        return row if row < R else -1
+
+    def tile_row(w, S, n):
+        return 128 * S + 16 * w + n if which == 0 else 32 * w + 16 * S + n
+
+    out = np.zeros((E, tiles, NS, 18432), dtype=np.uint8)
+    for t in range(tiles):
+        for s in range(NS):
+            g0, g1 = 2 * s, 2 * s + 1
+            for w in range(8):
+                for S in range(2):
+                    for l in range(64):
+                        n, b = l % 16, l // 16
+                        row = mrow(t, tile_row(w, S, n))
+                        if row < 0:
+                            continue
+                        o = ((2 * w + S) * 64 + l) * 16
+                        out[:, t, s, o:o + 8] = q[:, row, 32 * g0 + 8 * b:32 * g0 + 8 * b + 8]
+                        if g1 < G:
+                            out[:, t, s, o + 8:o + 16] = q[:, row, 32 * g1 + 8 * b:32 * g1 + 8 * b + 8]
+                for n in range(16):
+                    for S in range(2):
+                        row = mrow(t, tile_row(w, S, n))
+                        if row < 0:
+                            continue
+                        vals = [sc[:, row, g0], sc[:, row, g1] if g1 < G else 0 * sc[:, row, g0],
+                                ze[:, row, g0], ze[:, row, g1] if g1 < G else 0 * ze[:, row, g0]]
+                        o = 16384 + (16 * w + n) * 16 + 8 * S
+                        out[:, t, s, o:o + 8] = np.stack(vals, axis=-1).astype(np.uint16).view(np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("d,f,E", [(256, 128, 3), (384, 192, 2), (640, 576, 2)])
+def test_packed_layout(bd, d, f, E):
+    """moe_w4a16_prepare writes exactly the documented packed stream (bit-exact against a
+    re-indexing of the raw arrays): odd group counts, ragged last tiles, both matrices."""
     import torch
     shape = workloads.LayerShape(4, d, f, E, 1)
     w_np = workloads.make_weights(shape, 5)
-    say("prepared layout", d, f, E)
+    say("packed layout", d, f, E)
     w = bd.MoeWeights.from_numpy(w_np, 1).prepare()
     torch.cuda.synchronize()
-    for which, (rows_of, G, tiles) in enumerate([
-            (lambda t, r: (r < 128, (0 if r < 128 else f) + 128 * t + (r & 127), 128 * t + (r & 127) < f),
-             d // 64, -(-f // 128)),
-            (lambda t, r: (True, 256 * t + r, 256 * t + r < d), f // 64, -(-d // 256))]):
-        name = "gate_up" if which == 0 else "down"
-        sc = w_np[name + "_scale"].view(np.uint16)
-        ze = w_np[name + "_zero"].view(np.uint16)
-        NS = (G + 1) // 2
-        got = w.sz[which].cpu().numpy().view(np.uint16).reshape(E, tiles, NS, 256, 4)
-        want = np.zeros_like(got)
-        for t in range(tiles):
-            for r in range(256):
-                _, row, ok = rows_of(t, r)
-                if not ok:
-                    continue
-                for s in range(NS):
-                    for j in range(2):
-                        g = 2 * s + j
-                        if g < G:
-                            want[:, t, s, r, j] = sc[:, row, g]
-                            want[:, t, s, r, 2 + j] = ze[:, row, g]
-        assert np.array_equal(got, want), f"{name} layout differs"
+    for which in (0, 1):
+        want = packed_stream(w_np, which, d, f, E)
+        got = w.packed[which].cpu().numpy().reshape(want.shape)
+        assert np.array_equal(got, want), f"matrix {which}: packed stream differs"
 
+
+def test_packed_without_raw_arrays(bd):
+    """With the packed streams attached the GEMMs never read the raw arrays: releasing them
+    leaves the results bit-identical."""
+    say("packed, raw arrays released")
+    layer = Layer(bd, workloads.SHORT_LAYER)
+    got = layer.run(bd, prepared=True)
+    layer.w = bd.MoeWeights.from_numpy(layer.w_np, layer.shape.top_k, prepare=True, drop_raw=True)
+    got2 = layer.run(bd, prepared=True)
+    for a, b in zip(got, got2):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 def test_single_expert_and_zero_input(bd):
@@ -218,7 +261,7 @@ def test_combine_bit_identical_and_within_fp16_rounding(bd):
     assert np.all(np.abs(y - ref) <= half_ulp * 1.0001 + fp32_sum)
 
 
-@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "packed256"])
 def test_full_layer_sampled_tokens(bd, prepared):
     """Full shape (256 tokens, 128 experts, top-8): ids for all, outputs on sampled tokens."""
     say("full layer", prepared)
@@ -228,7 +271,7 @@ def test_full_layer_sampled_tokens(bd, prepared):
     check_layer(layer, got, tokens=tokens)
 
 
-@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "wide256"])
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "packed256"])
 def test_short_zipf_layer(bd, prepared):
     """64 tokens with Zipf-skewed routing: small and large buckets in one launch."""
     say("short zipf layer", prepared)
