@@ -4,16 +4,20 @@ Two modes:
 
   stats    from a `rocprofv3 --kernel-trace --stats -f csv` run: per-kernel calls and
            durations, largest total first.
-  traffic  from two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a workload and
-           the same two counters read on bd_hbm_copy of a known size (the calibration): HBM
-           bytes per call of an entry point, as the mean per-dispatch counter of every kernel
-           the entry point launches, summed, times the copy's bytes-per-counter-unit.
+  traffic  HBM bytes per call of an entry point, from `rocprofv3 --pmc` runs of a workload and
+           of bd_hbm_copy over a known number of bytes (the calibration):
+             * FETCH_SIZE and WRITE_SIZE (one run each), each scaled by the bytes the copy moved
+               per unit the same counter read on it;
+             * optionally the raw request counters TCC_EA0_RDREQ_{32B,64B,128B}_sum and
+               TCC_EA0_WRREQ_64B_sum (32/64/128-byte reads, 64-byte writes), checked the same
+               way on the copy.
+           The per-dispatch mean of every kernel the entry point launches is summed.
 
 Usage:
   python -m block_diffusion_lm_router_amd.profsum stats --csv X_kernel_stats.csv \
       --command "..." --out profiles/NAME.txt
-  python -m block_diffusion_lm_router_amd.profsum traffic --fetch A_counter_collection.csv \
-      --write B_counter_collection.csv --copy-fetch C.csv --copy-write D.csv \
+  python -m block_diffusion_lm_router_amd.profsum traffic --fetch A.csv --write B.csv \
+      --copy-fetch C.csv --copy-write D.csv [--req E.csv --copy-req F.csv] \
       --copy-bytes 1073741824 --kernel REGEX [--kernel REGEX ...] --entry NAME \
       --command "..." --out profiles/NAME.json
 """
@@ -29,17 +33,26 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def kernel_source_hash():
-    """Short hash of the grouped GEMM's source, stamped on traffic summaries so that a
-    summary taken on another version of the kernel is recognised as stale."""
+    """Short hash of the sources of the gate/up entry point's kernels (the grouped GEMM and
+    the bucketing launch before it), stamped on traffic summaries so that a summary taken on
+    another version of them is recognised as stale."""
     h = hashlib.sha256()
-    with open(os.path.join(_HERE, "csrc", "moe_w4a16.hip"), "rb") as f:
-        h.update(f.read())
+    for name in ("moe_w4a16.hip", "moe_route.hip"):
+        with open(os.path.join(_HERE, "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def _rows(path):
     with open(path, newline="") as f:
         return list(csv.DictReader(f))
+
+
+def _short(name, width=110):
+    """Kernel name without namespaces noise, cut to a readable width."""
+    name = name.replace("(anonymous namespace)::", "")
+    name = re.sub(r"rocprim::ROCPRIM_\w+::(detail::)?", "rocprim::", name)
+    return name if len(name) <= width else name[:width - 3] + "..."
 
 
 def stats(args):
@@ -52,7 +65,7 @@ def stats(args):
         out.append(f"{int(r['Calls']):>7} {float(r['TotalDurationNs']) / 1e3:>11.1f} "
                    f"{float(r['AverageNs']) / 1e3:>9.2f} {float(r['MinNs']) / 1e3:>9.2f} "
                    f"{float(r['MaxNs']) / 1e3:>9.2f} {100 * float(r['TotalDurationNs']) / total:>6.2f}"
-                   f"  {r['Name']}")
+                   f"  {_short(r['Name'])}")
     out.append(f"\nall kernels: {total / 1e3:.1f} us over {sum(int(r['Calls']) for r in rows)} calls")
     text = "\n".join(out) + "\n"
     with open(args.out, "w") as f:
@@ -73,6 +86,20 @@ def _per_dispatch(path, counter, patterns):
                 vals[p][r["Dispatch_Id"]] += float(r["Counter_Value"])
                 break
     return {p: (sum(d.values()) / len(d), len(d)) for p, d in vals.items()}
+
+
+_REQ = (("TCC_EA0_RDREQ_32B_sum", 32), ("TCC_EA0_RDREQ_64B_sum", 64),
+        ("TCC_EA0_RDREQ_128B_sum", 128))
+
+
+def _req_bytes(path, patterns):
+    """Read and write bytes per dispatch from the raw request counters."""
+    rd = {p: 0.0 for p in patterns}
+    for counter, size in _REQ:
+        for p, (v, _) in _per_dispatch(path, counter, patterns).items():
+            rd[p] += v * size
+    wr = {p: v * 64 for p, (v, _) in _per_dispatch(path, "TCC_EA0_WRREQ_64B_sum", patterns).items()}
+    return rd, wr
 
 
 def traffic(args):
@@ -99,6 +126,14 @@ def traffic(args):
                            "copy_write_kib_raw": round(w_kib, 1),
                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
            "kernels": kernels, "hbm_bytes_per_launch": int(total)}
+    if args.req and args.copy_req:
+        crd, cwr = _req_bytes(args.copy_req, ["copy"])
+        rd, wr = _req_bytes(args.req, args.kernel)
+        rec["request_counters"] = {
+            "copy_read_bytes": int(crd["copy"]), "copy_write_bytes": int(cwr.get("copy", 0)),
+            "per_kernel": {p: {"read_bytes": int(rd[p]), "write_bytes": int(wr.get(p, 0))}
+                           for p in args.kernel},
+            "bytes_per_launch": int(sum(rd.values()) + sum(wr.values()))}
     with open(args.out, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -116,6 +151,8 @@ def main():
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write", "command", "out", "entry"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
+    t.add_argument("--req")
+    t.add_argument("--copy-req")
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--kernel", action="append", required=True)
     args = ap.parse_args()
