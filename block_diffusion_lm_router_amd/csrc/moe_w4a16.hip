@@ -14,8 +14,9 @@
 // the block's rows crosses HBM once per item.
 //
 // Block order.  Consecutive block ids are dispatched round-robin over the 8 XCDs.  Block b
-// maps to XCD b % 8, and the blocks an XCD receives walk through all row tiles of one item
-// before the next, so the item's activation rows are fetched into that XCD's L2 once.
+// maps to XCD b % 8.  In the 128-row tile kernel the blocks an XCD receives walk through all
+// row tiles of one item before the next, so the item's activation rows are fetched into that
+// XCD's L2 once; the packed kernel orders its blocks for weight reuse instead (see there).
 //
 // Data movement.  The contraction dim is walked in stages of kSG 64-groups.  Packed weight
 // rows and activation rows go from HBM straight into a ring of LDS stage buffers with
@@ -601,11 +602,17 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
 template <bool GATED, int NSC>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kPkXSlot];
+  // XCD b % 8 owns a contiguous range of work items (the items of one expert are consecutive,
+  // so a hot expert's items mostly share an XCD) and walks it tile-major: the blocks of one
+  // tile of neighbouring items start together, and all but the first read the tile's stream
+  // from that XCD's L2.
   const int b = blockIdx.x;
+  const int n_items = a.items[0];
+  const int per = (n_items + kXcds - 1) / kXcds;
   const int local = b / kXcds;
-  const int item = (local / a.tiles) * kXcds + (b % kXcds);
-  const int tile = local % a.tiles;
-  if (item >= a.items[0]) return;
+  const int tile = local / per;
+  const int item = (b % kXcds) * per + local % per;
+  if (tile >= a.tiles || item >= n_items) return;
   const int e = a.items[1 + 3 * item];
   const int pos0 = a.items[2 + 3 * item];
   const int mcount = a.items[3 + 3 * item];
