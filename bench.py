@@ -9,7 +9,8 @@ steps.  All inputs are seeded synthetic tensors resident in HBM before timing st
 
 value = algorithmic bytes of the step (touched expert weights with their scales and
 zero-points, activations in and out, router logits, the unfrozen logits rows) / time,
-in GB/s; ms_per_step is the latency of one step.
+in GB/s; ms_per_step is the latency of one step; config.step_ms_p10_p50_p90 is the spread of
+the step latency over a second pass of the same length with an event between steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -161,7 +162,7 @@ def main():
                  for _ in range(args.steps)]
     gu_layer = [i % len(layers) for i in range(args.steps)]
     total = args.warmup + args.steps
-    n_acc = torch.zeros(total, dtype=torch.int32, device="cuda")
+    n_acc = torch.zeros(total + args.steps, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(i, events=None, ev_layer=-1):
@@ -191,6 +192,16 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+
+    # A second pass of the same number of steps, with an event between consecutive steps, gives
+    # the spread of the step latency without touching the timed region above.
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    step_ev[0].record(stream)
+    for i in range(total, total + args.steps):
+        step(i)
+        step_ev[i - total + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in zip(step_ev[:-1], step_ev[1:])])
 
     # Unfrozen rows seen by each timed step's sampler, from the device's acceptance counts.
     counts = n_acc.cpu().numpy()
@@ -233,6 +244,7 @@ def main():
                          f"fp32 [{P}, {V}] T=1 bound 2.0, 48-step frozen canvas"),
             "steps_per_block": workloads.STACK_STEPS,
             "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+            "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
             "step_algorithmic_bytes": int(step_bytes),
         },
         "roofline": {

@@ -281,3 +281,38 @@ def test_short_zipf_layer(bd, prepared):
     assert counts.max() > 32      # the hottest expert needs several 32-token items
     tokens = np.random.default_rng(1).choice(layer.shape.tokens, 6, replace=False)
     check_layer(layer, got, tokens=tokens)
+
+
+@pytest.mark.parametrize("layer_id", [0, 29])
+def test_stack_layer_bench_config(bd, layer_id):
+    """A layer of the benchmark stack in the benchmark's launch configuration (packed streams,
+    raw arrays released; 256 tokens, Zipf routing, the hottest expert split over several work
+    items): ids for every token, every expert-output row written, outputs on sampled tokens
+    that include tokens of the hottest expert."""
+    shape = workloads.STACK_LAYER
+    say("stack layer bench config", layer_id)
+    layer = Layer(bd, shape, layer=layer_id)
+    layer.w = bd.MoeWeights.from_numpy(layer.w_np, shape.top_k, prepare=True, drop_raw=True)
+    got = layer.run(bd, prepared=True)
+    ids, _, o, _ = got
+    assert not np.isnan(o).any(), "an expert-output row was not written"
+    counts = np.bincount(ids.ravel(), minlength=shape.experts)
+    hot = int(np.argmax(counts))
+    assert counts[hot] > 2 * 32        # several 32-token work items for one expert
+    rng = np.random.default_rng(layer_id)
+    hot_tokens = np.nonzero((ids == hot).any(axis=1))[0]
+    tokens = np.unique(np.concatenate([rng.choice(hot_tokens, 4, replace=False),
+                                       rng.choice(shape.tokens, 4, replace=False)]))
+    check_layer(layer, got, tokens=tokens)
+
+
+@pytest.mark.parametrize("prepared", [False, True], ids=["tile128", "packed256"])
+def test_widest_routing(bd, prepared):
+    """256 experts, top-16, 1500 tokens: the largest expert count and k the ABI accepts, and a
+    bucketing that takes two token passes; small expert matrices keep the oracle quick."""
+    shape = workloads.LayerShape(1500, 128, 64, 256, 16)
+    say("widest routing", prepared)
+    layer = Layer(bd, shape, layer=11)
+    got = layer.run(bd, prepared=prepared)
+    assert not np.isnan(got[2]).any()
+    check_layer(layer, got)
