@@ -66,6 +66,7 @@ SIGNATURES = {
     "diffusion_sample_step": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P, _P, _P,
                                    _SZ, _P]),
     "bd_hbm_copy": (_I, [_P, _P, _SZ, _P]),
+    "bd_hbm_read": (_I, [_P, _SZ, _P, _P]),
 }
 
 _lib = None
@@ -301,3 +302,16 @@ def hbm_copy(src, dst):
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst smaller than src")
     return _invoke("bd_hbm_copy", _ptr(src, None, "src"), _ptr(dst, None, "dst"), n, _stream())
+
+
+HBM_READ_WORDS = 2049
+
+
+def hbm_read(src, checksum):
+    """XOR of all 32-bit words of src into checksum[0]; checksum is an int32 device tensor of
+    at least HBM_READ_WORDS elements (the rest is scratch)."""
+    n = src.numel() * src.element_size()
+    if checksum.numel() < HBM_READ_WORDS:
+        raise ValueError(f"checksum needs {HBM_READ_WORDS} int32 elements")
+    return _invoke("bd_hbm_read", _ptr(src, None, "src"), n, _ptr(checksum, torch.int32, "checksum"),
+                   _stream())

@@ -259,4 +259,11 @@ int bd_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return to_status(bd::launch_copy(src, dst, bytes, as_stream(stream)));
 }
 
+int bd_hbm_read(const void* src, size_t bytes, uint32_t* checksum, void* stream) {
+  if (!checksum || (!src && bytes)) return BD_ERR_NULL;
+  if (bytes % 16 != 0) return BD_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(checksum)) return BD_ERR_ALIGN;
+  return to_status(bd::launch_read(src, bytes, checksum, as_stream(stream)));
+}
+
 }  // extern "C"

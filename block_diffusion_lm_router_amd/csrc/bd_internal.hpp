@@ -81,5 +81,6 @@ hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, flo
 
 // ---------------------------------------------------------------- measurement
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_read(const void* src, size_t bytes, uint32_t* checksum, hipStream_t stream);
 
 }  // namespace bd

@@ -51,6 +51,44 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const u32x4_t* __res
     __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Streaming read: XOR of every 32-bit word, one 16-byte load per thread per iteration over a
+// grid-stride sweep.  Each block folds its threads (wave shuffles, then LDS) and writes one
+// partial to part[blockIdx.x]; a one-block pass folds the partials into part[-1].  No two
+// blocks write the same word, so the read is not serialised behind same-address atomics.
+constexpr int kReadBlocks = 2048;
+
+__device__ __forceinline__ uint32_t block_xor(uint32_t v) {
+  __shared__ uint32_t w[kCopyThreads / 64];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v ^= (uint32_t)__shfl_xor((int)v, off, 64);
+  if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = 0;
+#pragma unroll
+  for (int i = 0; i < kCopyThreads / 64; ++i) v ^= w[i];
+  return v;
+}
+
+__global__ __launch_bounds__(kCopyThreads) void read_kernel(const u32x4_t* __restrict__ src, size_t n,
+                                                            uint32_t* __restrict__ part) {
+  const size_t stride = (size_t)gridDim.x * kCopyThreads;
+  uint32_t acc = 0;
+  for (size_t i = (size_t)blockIdx.x * kCopyThreads + threadIdx.x; i < n; i += stride) {
+    const u32x4_t v = src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  acc = block_xor(acc);
+  if (threadIdx.x == 0) part[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kCopyThreads) void read_finish_kernel(uint32_t* __restrict__ out,
+                                                                   int nparts) {
+  uint32_t acc = 0;
+  for (int i = threadIdx.x; i < nparts; i += kCopyThreads) acc ^= out[1 + i];
+  acc = block_xor(acc);
+  if (threadIdx.x == 0) out[0] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* expert_out, const float* topk_weights, int T, int k, int d,
@@ -69,6 +107,18 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t str
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream,
                      reinterpret_cast<const u32x4_t*>(src), reinterpret_cast<u32x4_t*>(dst), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_read(const void* src, size_t bytes, uint32_t* checksum, hipStream_t stream) {
+  const size_t n = bytes / 16;
+  size_t blocks = (n + kCopyThreads - 1) / kCopyThreads;
+  if (blocks > kReadBlocks) blocks = kReadBlocks;
+  if (blocks > 0)
+    hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream,
+                       reinterpret_cast<const u32x4_t*>(src), n, checksum + 1);
+  hipLaunchKernelGGL(read_finish_kernel, dim3(1), dim3(kCopyThreads), 0, stream, checksum,
+                     (int)blocks);
   return hipGetLastError();
 }
 

@@ -167,6 +167,57 @@ __device__ void expert_scan(int tot, int E, int Ep, int A, BucketShared& sh,
   }
 }
 
+constexpr int kIdCache = 4;                    // assignments per thread held in registers
+
+// The bucketing when all tokens fit one pass (T <= kPassTokens): each thread loads its
+// assignments' expert ids once, into registers, and the block takes four barriers (bitmasks
+// cleared / marked / counted and scanned / offsets published).
+__device__ void bucket_one_pass(const BucketArgs& g, BucketShared& sh) {
+  const int tid = threadIdx.x;
+  const int T = g.T, k = g.k, E = g.E, A = T * k;
+  const int Ep = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
+  const int W = (T + 63) / 64;
+  int eid[kIdCache];
+#pragma unroll
+  for (int i = 0; i < kIdCache; ++i) {
+    const int a = tid + i * kBucketThreads;
+    eid[i] = a < A ? g.ids[a] : 0;
+  }
+  for (int i = tid; i < E * kPassWords; i += kBucketThreads) sh.bits[i] = 0ull;
+  __syncthreads();
+  auto mark = [&](int e, int a) {
+    const int t = a / k;
+    atomicOr(&sh.bits[e * kPassWords + (t >> 6)], 1ull << (t & 63));
+  };
+#pragma unroll
+  for (int i = 0; i < kIdCache; ++i) {
+    const int a = tid + i * kBucketThreads;
+    if (a < A) mark(eid[i], a);
+  }
+  for (int a = tid + kIdCache * kBucketThreads; a < A; a += kBucketThreads) mark(g.ids[a], a);
+  __syncthreads();
+  int tot = 0;                                  // thread e < E: rank at each word's start
+  if (tid < E) {
+    for (int w = 0; w < W; ++w) {
+      sh.wpre[tid * kPassWords + w] = tot;
+      tot += __popcll(sh.bits[tid * kPassWords + w]);
+    }
+  }
+  expert_scan(tot, E, Ep, A, sh, g.offsets, g.items);   // publishes eoff behind a barrier
+  auto place = [&](int e, int a) {
+    const int t = a / k;
+    const int w = e * kPassWords + (t >> 6);
+    const int rank = sh.wpre[w] + __popcll(sh.bits[w] & ((1ull << (t & 63)) - 1ull));
+    g.perm[sh.eoff[e] + rank] = a;
+  };
+#pragma unroll
+  for (int i = 0; i < kIdCache; ++i) {
+    const int a = tid + i * kBucketThreads;
+    if (a < A) place(eid[i], a);
+  }
+  for (int a = tid + kIdCache * kBucketThreads; a < A; a += kBucketThreads) place(g.ids[a], a);
+}
+
 // Block 0: the bucketing.  Bucket position of assignment a = (t, j) routed to e is
 // offsets[e] + (tokens t' < t routed to e), so each bucket lists its assignments by
 // ascending token.  Tokens are taken in passes of kPassTokens: a bitmask per expert marks
@@ -181,6 +232,10 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_permute_kernel(BucketAr
     return;
   }
   __shared__ BucketShared sh;
+  if (g.T <= kPassTokens) {
+    bucket_one_pass(g, sh);
+    return;
+  }
   const int tid = threadIdx.x;
   const int T = g.T, k = g.k, E = g.E, A = T * k;
   const int Ep = E <= 64 ? 64 : (E <= 128 ? 128 : 256);

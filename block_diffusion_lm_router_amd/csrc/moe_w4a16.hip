@@ -622,11 +622,205 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
     packed_item<GATED, 1, NSC>(a, lds, e, pos0, mcount, tile);
 }
 
+// ------------------------------------------------------------------ down, resident rows
+//
+// The down GEMM over the packed stream when an item's activation rows fit LDS (K <= 1024:
+// 32 rows x K halves <= 64 KB).  The block loads its item's h rows into LDS once, one 8 KB
+// slot per stage in the same swizzled layout as the staged kernel, and then walks
+// kDownTilesPerBlock consecutive 256-row tiles of the expert.  Those tiles are one contiguous
+// run of the packed stream, so each wave streams its 1 KB runs and scale/zero pairs through
+// a register ring kPkDepth stages deep across tile boundaries, with no barrier after the
+// prologue.  A tile past the matrix end holds zero rows in the packed stream; they are
+// computed and not stored.
+#ifndef BD_DOWN_TILES_PER_BLOCK
+#define BD_DOWN_TILES_PER_BLOCK 2
+#endif
+constexpr int kDownTilesPerBlock = BD_DOWN_TILES_PER_BLOCK;
+constexpr int kResidentMaxStages = 8;
+
+struct PkW {
+  u32x4_t wa, wb, sz;
+};
+
+template <int NMT>
+__device__ __forceinline__ void down_resident_item(const GemmArgs& a, char* lds, int e, int pos0,
+                                                   int mcount, int tile0, int ntiles) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int kb = lane >> 4;
+  const int G = a.K >> 6;
+  const int NS = (G + 1) >> 1;
+  const int F = ntiles * NS;                           // stages the block streams
+  const DequantConsts dq = dequant_consts();
+  const char* pk = reinterpret_cast<const char*>(a.pk) +
+                   ((size_t)e * a.tiles + tile0) * (size_t)NS * kPkStage;
+  const uint32_t wa_off = ((wave * 2 + 0) * 64 + lane) * 16;
+  const uint32_t sz_off = kPkWBytes + (wave * 16 + n) * 16;
+  auto load = [&](int f) {
+    const char* st = pk + (size_t)min(f, F - 1) * kPkStage;
+    PkW r;
+    r.wa = *reinterpret_cast<const u32x4_t*>(st + wa_off);
+    r.wb = *reinterpret_cast<const u32x4_t*>(st + wa_off + 1024);
+    r.sz = *reinterpret_cast<const u32x4_t*>(st + sz_off);
+    return r;
+  };
+
+  // Output slots of the lane's tokens (D rows 4kb..4kb+3 of each 16-token tile), loaded first
+  // so that no later wait is for them.
+  int slot[NMT][4];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mt * 16 + kb * 4 + r;
+      slot[mt][r] = a.perm[pos0 + min(m, mcount - 1)];
+      if (m >= mcount) slot[mt][r] = -1;
+    }
+
+  // Prologue: rows 0..16*NMT-1 of the item (rows past mcount repeat the last one), stage s
+  // at slot s, 16-byte chunk ch of row m at (ch ^ xswz(m)).  Every thread issues the same
+  // loads (chunks past K or stages past NS read clamped, in-bounds addresses and are not
+  // written), then the first weight stages, then writes its rows to LDS.
+  constexpr int kRows = NMT * 16;
+  constexpr int kPer = kResidentMaxStages * kRows * 16 / kThreads;
+  constexpr int kStep = kThreads / (kRows * 16);        // stages between a thread's chunks
+  const int xm = (tid >> 4) % kRows;
+  const int xch = tid & 15;
+  const int xs0 = tid / (kRows * 16);
+  const char* xsrc = reinterpret_cast<const char*>(a.act) +
+                     (size_t)(pos0 + min(xm, mcount - 1)) * a.K * 2;
+  u32x4_t xv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int k0 = min((xs0 + i * kStep) * kStageK + xch * 8, a.K - 8);
+    xv[i] = *reinterpret_cast<const u32x4_t*>(xsrc + (size_t)k0 * 2);
+  }
+  // The issue order is kept (rows, then stage 0, 1, ...) so that each wait below and in the
+  // loop covers only the loads it needs.
+  __builtin_amdgcn_sched_barrier(0);
+  PkW buf[kPkDepth];
+#pragma unroll
+  for (int u = 0; u < kPkDepth; ++u) {
+    buf[u] = load(u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int st = xs0 + i * kStep;
+    if (st < NS && st * kStageK + xch * 8 < a.K)
+      *reinterpret_cast<u32x4_t*>(lds + st * kPkXSlot + xm * kXRowBytes + ((xch ^ xswz(xm)) << 4)) = xv[i];
+  }
+  lds_barrier();
+
+  float4_t totA[NMT], totB[NMT];
+  const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) totA[mt] = totB[mt] = zero4;
+
+  auto compute = [&](const PkW& r, int c) {
+    const char* xt = lds + c * kPkXSlot;
+    const half4_t szA = __builtin_bit_cast(half4_t, u32x2_t{r.sz[0], r.sz[1]});
+    const half4_t szB = __builtin_bit_cast(half4_t, u32x2_t{r.sz[2], r.sz[3]});
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (2 * c + j >= G) break;
+      const _Float16 zA = szA[2 + j], zB = szB[2 + j];
+      const _Float16 za1 = -((_Float16)1024.f + zA), za2 = -((_Float16)64.f + zA);
+      const _Float16 zb1 = -((_Float16)1024.f + zB), zb2 = -((_Float16)64.f + zB);
+      const float fsA = (float)szA[j], fsB = (float)szB[j];
+      const half8_t bA0 = dequant8(r.wa[2 * j], za1, za2, dq);
+      const half8_t bA1 = dequant8(r.wa[2 * j + 1], za1, za2, dq);
+      const half8_t bB0 = dequant8(r.wb[2 * j], zb1, zb2, dq);
+      const half8_t bB1 = dequant8(r.wb[2 * j + 1], zb1, zb2, dq);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int m = mt * 16 + n;
+        const char* xrow = xt + m * kXRowBytes;
+        const int c8 = j * 8 + kb * 2;
+        const half8_t a0 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 0) ^ xswz(m)) << 4)));
+        const half8_t a1 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 1) ^ xswz(m)) << 4)));
+        float4_t accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bA0, zero4, 0, 0, 0);
+        accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bA1, accA, 0, 0, 0);
+        float4_t accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bB0, zero4, 0, 0, 0);
+        accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bB1, accB, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          totA[mt][q] = fmaf(fsA, accA[q], totA[mt][q]);
+          totB[mt][q] = fmaf(fsB, accB[q], totB[mt][q]);
+        }
+      }
+    }
+  };
+  auto store = [&](int tile) {
+    const int row = tile * kPkRows + wave * 32 + n;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (slot[mt][r] < 0) continue;
+        float* o = a.o_out + (size_t)slot[mt][r] * a.out_ld;
+        if (row < a.R) o[row] = totA[mt][r];
+        if (row + 16 < a.R) o[row + 16] = totB[mt][r];
+      }
+      totA[mt] = totB[mt] = zero4;
+    }
+  };
+
+  // Rounds of kPkDepth stages; stage f of the run sits in buf[f % kPkDepth] and the load
+  // that refills it (stage f + kPkDepth, clamped to the run) is issued right after its use.
+  // A finished tile is stored before that load, so the waits for later stages never cover
+  // the stores.
+  int c = 0, tile = tile0;
+  for (int f0 = 0; f0 < F; f0 += kPkDepth) {
+#pragma unroll
+    for (int u = 0; u < kPkDepth; ++u) {
+      const bool live = f0 + u < F;
+      if (live) compute(buf[u], c);
+      if (live && ++c == NS) {
+        store(tile);
+        c = 0;
+        ++tile;
+      }
+      buf[u] = load(f0 + u + kPkDepth);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void w4a16_down_resident_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds_dyn[];
+  // Same XCD-aware order as the staged kernel, over (item, group of tiles).
+  const int b = blockIdx.x;
+  const int groups = (a.tiles + kDownTilesPerBlock - 1) / kDownTilesPerBlock;
+  const int n_items = a.items[0];
+  const int per = (n_items + kXcds - 1) / kXcds;
+  const int local = b / kXcds;
+  const int grp = local / per;
+  const int item = (b % kXcds) * per + local % per;
+  if (grp >= groups || item >= n_items) return;
+  const int e = a.items[1 + 3 * item];
+  const int pos0 = a.items[2 + 3 * item];
+  const int mcount = a.items[3 + 3 * item];
+  const int tile0 = grp * kDownTilesPerBlock;
+  const int ntiles = min(kDownTilesPerBlock, a.tiles - tile0);
+  if (mcount > 16)
+    down_resident_item<2>(a, lds_dyn, e, pos0, mcount, tile0, ntiles);
+  else
+    down_resident_item<1>(a, lds_dyn, e, pos0, mcount, tile0, ntiles);
+}
+
 // Stage counts with a fully unrolled kernel: the contraction dims 2816 (gate/up) and 704
 // (down) of the 26B-A4B expert shape.
 template <bool GATED>
 void launch_packed(const GemmArgs& a, int max_items, hipStream_t stream) {
   const int NS = (a.K / 64 + 1) / 2;
+  if (!GATED && NS <= kResidentMaxStages) {
+    const int groups = (a.tiles + kDownTilesPerBlock - 1) / kDownTilesPerBlock;
+    hipLaunchKernelGGL(w4a16_down_resident_kernel, dim3(grid_blocks(max_items, groups)),
+                       dim3(kThreads), NS * kPkXSlot, stream, a);
+    return;
+  }
   const dim3 grid(grid_blocks(max_items, a.tiles)), block(kThreads);
   if (NS == 22)
     hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 22>), grid, block, 0, stream, a);

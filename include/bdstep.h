@@ -290,6 +290,17 @@ int diffusion_sample_step(const float* logits, int P, int V, float temperature,
  */
 int bd_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/*
+ * Streaming read of `bytes` bytes at src (bytes % 16 == 0; src and checksum 16-byte aligned,
+ * both device memory): checksum points to BD_HBM_READ_WORDS uint32 words; word 0 receives
+ * the XOR of all 32-bit words of src (0 for bytes == 0) and the others are scratch.  The read
+ * cannot be optimised away and can be checked on the host.  The achievable read-only
+ * bandwidth beside the copy figure.  Two launches on `stream` (read, then a one-block fold of
+ * the per-block partials); the caller owns both buffers.  src may be NULL when bytes == 0.
+ */
+#define BD_HBM_READ_WORDS 2049
+int bd_hbm_read(const void* src, size_t bytes, uint32_t* checksum, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

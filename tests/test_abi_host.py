@@ -129,6 +129,10 @@ def test_sampler_validation(lib):
     assert step(P, 8, 100, 1.0, float("inf"), 0, 0, None, None, P, P, P, P, P, 1 << 20, None) == 2
     assert lib.bd_hbm_copy(P, P, 17, None) == 2
     assert lib.bd_hbm_copy(None, P, 16, None) == 1
+    assert lib.bd_hbm_read(P, 17, P, None) == 2
+    assert lib.bd_hbm_read(None, 16, P, None) == 1
+    assert lib.bd_hbm_read(P, 16, None, None) == 1
+    assert lib.bd_hbm_read(ctypes.c_void_p(0x1004), 16, P, None) == 3
 
 
 def test_prepare_sizes_and_validation(lib):
