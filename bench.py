@@ -248,7 +248,7 @@ def main():
             "step_algorithmic_bytes": int(step_bytes),
         },
         "roofline": {
-            "kernel": "moe_w4a16_gate_up (bucket_permute_kernel + w4a16_packed_kernel<true, 22>)",
+            "kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22>)",
             "bound": "hbm",
             "achieved": round(gu_gbs, 2),
             "peak": HBM_PEAK_GBS,

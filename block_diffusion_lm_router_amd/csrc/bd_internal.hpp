@@ -41,13 +41,13 @@ int moe_max_items(int T, int E, int k);
 size_t moe_workspace_bytes(int T, int E, int k, int d_model, int d_ff);
 MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_model, int d_ff);
 
-// Top-k ids and weights, the ids also into ws.ids.
+// Top-k ids and weights (the ids also into ws.ids), then the stable grouping of the
+// assignments by expert and the work list into ws (a second, one-block launch).
 hipError_t launch_route(const float* router_logits, int T, int E, int k, int32_t* topk_ids,
                         float* topk_weights, const MoeWorkspace& ws, hipStream_t stream);
-// Stable grouping of the assignments (ws.ids) by expert into ws, and x permuted into ws.xp,
-// in one launch.
-hipError_t launch_bucket(int T, int E, int k, const uint16_t* x, int d_model,
-                         const MoeWorkspace& ws, hipStream_t stream);
+// x permuted into ws.xp (the k-order of the dequantised nibbles), for the tile kernel.
+hipError_t launch_permute(int T, const uint16_t* x, int d_model, const MoeWorkspace& ws,
+                          hipStream_t stream);
 
 struct W4A16Matrix {
   const uint8_t* q;

@@ -1,6 +1,6 @@
 // Routing kernels of the MoE layer: per-token top-k with softmax weights, then a stable
-// bucketing of the T*k assignments by expert and the work list of touched experts (run at
-// the start of the gate/up GEMM, in the same launch as the activation permutation).
+// bucketing of the T*k assignments by expert and the work list of touched experts (one
+// block, in a second launch).
 //
 // Source: axe-diffusion-ksl-xe model card, "what the model is" (128 experts, top-8 per
 // token) and "the kernels we built" (one launch covers all experts instead of a
@@ -97,10 +97,13 @@ struct BucketArgs {
   int32_t* offsets;        // [E + 1]
   int32_t* items;          // [0] = count, then (expert, first position, tokens)
   int32_t* perm;           // [T * k]
-  const u32x4_t* x;        // [T * d_model / 8]
-  u32x4_t* xp;
-  int n8;
 };
+
+// Expert id of an assignment, clamped into [0, E) so that no value read can index past the
+// bucket tables (the routing only writes ids in range).
+__device__ __forceinline__ int expert_of(const int32_t* ids, int a, int E) {
+  return (int)min((uint32_t)ids[a], (uint32_t)(E - 1));
+}
 
 struct BucketShared {
   unsigned long long bits[kMaxE * kPassWords];   // token bitmask of each expert, one pass
@@ -181,7 +184,7 @@ __device__ void bucket_one_pass(const BucketArgs& g, BucketShared& sh) {
 #pragma unroll
   for (int i = 0; i < kIdCache; ++i) {
     const int a = tid + i * kBucketThreads;
-    eid[i] = a < A ? g.ids[a] : 0;
+    eid[i] = a < A ? expert_of(g.ids, a, E) : 0;
   }
   for (int i = tid; i < E * kPassWords; i += kBucketThreads) sh.bits[i] = 0ull;
   __syncthreads();
@@ -194,7 +197,8 @@ __device__ void bucket_one_pass(const BucketArgs& g, BucketShared& sh) {
     const int a = tid + i * kBucketThreads;
     if (a < A) mark(eid[i], a);
   }
-  for (int a = tid + kIdCache * kBucketThreads; a < A; a += kBucketThreads) mark(g.ids[a], a);
+  for (int a = tid + kIdCache * kBucketThreads; a < A; a += kBucketThreads)
+    mark(expert_of(g.ids, a, E), a);
   __syncthreads();
   int tot = 0;                                  // thread e < E: rank at each word's start
   if (tid < E) {
@@ -215,23 +219,17 @@ __device__ void bucket_one_pass(const BucketArgs& g, BucketShared& sh) {
     const int a = tid + i * kBucketThreads;
     if (a < A) place(eid[i], a);
   }
-  for (int a = tid + kIdCache * kBucketThreads; a < A; a += kBucketThreads) place(g.ids[a], a);
+  for (int a = tid + kIdCache * kBucketThreads; a < A; a += kBucketThreads)
+    place(expert_of(g.ids, a, E), a);
 }
 
-// Block 0: the bucketing.  Bucket position of assignment a = (t, j) routed to e is
-// offsets[e] + (tokens t' < t routed to e), so each bucket lists its assignments by
-// ascending token.  Tokens are taken in passes of kPassTokens: a bitmask per expert marks
-// the pass's tokens routed to it, popcounts of the words give the rank at each word's
-// start, and the rank of (t, j) adds the popcount of the bits below t in its word.  With
-// one pass the counts come from the bitmasks; with several, from a histogram first.
-// Blocks 1..: x -> xp with every 8 consecutive halves in the GEMMs' k-order.
-__global__ __launch_bounds__(kBucketThreads) void bucket_permute_kernel(BucketArgs g) {
-  if (blockIdx.x > 0) {
-    const int i = (blockIdx.x - 1) * kBucketThreads + threadIdx.x;
-    if (i < g.n8) g.xp[i] = permute8(g.x[i]);
-    return;
-  }
-  __shared__ BucketShared sh;
+// The bucketing, by one block of kBucketThreads.  Bucket position of assignment a = (t, j)
+// routed to e is offsets[e] + (tokens t' < t routed to e), so each bucket lists its
+// assignments by ascending token.  Tokens are taken in passes of kPassTokens: a bitmask per
+// expert marks the pass's tokens routed to it, popcounts of the words give the rank at each
+// word's start, and the rank of (t, j) adds the popcount of the bits below t in its word.
+// With one pass the counts come from the bitmasks; with several, from a histogram first.
+__device__ void bucket_all(const BucketArgs& g, BucketShared& sh) {
   if (g.T <= kPassTokens) {
     bucket_one_pass(g, sh);
     return;
@@ -244,7 +242,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_permute_kernel(BucketAr
   if (npass > 1) {
     if (tid < kMaxE) sh.cnt[tid] = 0;
     __syncthreads();
-    for (int a = tid; a < A; a += kBucketThreads) atomicAdd(&sh.cnt[g.ids[a]], 1);
+    for (int a = tid; a < A; a += kBucketThreads) atomicAdd(&sh.cnt[expert_of(g.ids, a, E)], 1);
     __syncthreads();
     expert_scan(tid < E ? sh.cnt[tid] : 0, E, Ep, A, sh, g.offsets, g.items);
   }
@@ -257,7 +255,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_permute_kernel(BucketAr
     const int a0 = t0 * k, a1 = (t0 + nt) * k;
     for (int a = a0 + tid; a < a1; a += kBucketThreads) {
       const int lt = a / k - t0;
-      atomicOr(&sh.bits[g.ids[a] * kPassWords + (lt >> 6)], 1ull << (lt & 63));
+      atomicOr(&sh.bits[expert_of(g.ids, a, E) * kPassWords + (lt >> 6)], 1ull << (lt & 63));
     }
     __syncthreads();
     if (tid < E) {
@@ -269,7 +267,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_permute_kernel(BucketAr
     if (npass == 1) expert_scan(tid < E ? run : 0, E, Ep, A, sh, g.offsets, g.items);
     __syncthreads();
     for (int a = a0 + tid; a < a1; a += kBucketThreads) {
-      const int e = g.ids[a];
+      const int e = expert_of(g.ids, a, E);
       const int lt = a / k - t0;
       const int w = e * kPassWords + (lt >> 6);
       const int rank = sh.wpre[w] + __popcll(sh.bits[w] & ((1ull << (lt & 63)) - 1ull));
@@ -277,6 +275,19 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_permute_kernel(BucketAr
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(BucketArgs g) {
+  __shared__ BucketShared sh;
+  bucket_all(g, sh);
+}
+
+// x -> xp with every 8 consecutive halves in the GEMMs' k-order (for the tile kernel, which
+// moves activations HBM -> LDS without passing through registers).
+__global__ __launch_bounds__(kBucketThreads) void permute_kernel(const u32x4_t* __restrict__ x,
+                                                                 u32x4_t* __restrict__ xp, int n8) {
+  const int i = blockIdx.x * kBucketThreads + threadIdx.x;
+  if (i < n8) xp[i] = permute8(x[i]);
 }
 
 }  // namespace
@@ -316,11 +327,6 @@ hipError_t launch_route(const float* router_logits, int T, int E, int k, int32_t
                         float* topk_weights, const MoeWorkspace& ws, hipStream_t stream) {
   hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(kTopkThreads), 0, stream, router_logits, T, E, k,
                      topk_ids, ws.ids, topk_weights);
-  return hipGetLastError();
-}
-
-hipError_t launch_bucket(int T, int E, int k, const uint16_t* x, int d_model,
-                         const MoeWorkspace& ws, hipStream_t stream) {
   BucketArgs g;
   g.ids = ws.ids;
   g.T = T;
@@ -329,11 +335,16 @@ hipError_t launch_bucket(int T, int E, int k, const uint16_t* x, int d_model,
   g.offsets = ws.offsets;
   g.items = ws.items;
   g.perm = ws.perm;
-  g.x = reinterpret_cast<const u32x4_t*>(x);
-  g.xp = reinterpret_cast<u32x4_t*>(ws.xp);
-  g.n8 = T * d_model / 8;
-  const int blocks = 1 + (g.n8 + kBucketThreads - 1) / kBucketThreads;
-  hipLaunchKernelGGL(bucket_permute_kernel, dim3(blocks), dim3(kBucketThreads), 0, stream, g);
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(int T, const uint16_t* x, int d_model, const MoeWorkspace& ws,
+                          hipStream_t stream) {
+  const int n8 = T * d_model / 8;
+  hipLaunchKernelGGL(permute_kernel, dim3((n8 + kBucketThreads - 1) / kBucketThreads),
+                     dim3(kBucketThreads), 0, stream, reinterpret_cast<const u32x4_t*>(x),
+                     reinterpret_cast<u32x4_t*>(ws.xp), n8);
   return hipGetLastError();
 }
 

@@ -458,20 +458,22 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
   const uint32_t wa_off = ((lw * 2 + 0) * 64 + lane) * 16;
   const uint32_t sz_off = kPkWBytes + (lw * 16 + n) * 16;
 
-  // Activation share: NMT = 2: rows 4w + lane/16, 16 bytes at chunk lane % 16 of the stage;
-  // NMT = 1: rows 2w + lane/32, 8 bytes (half lane % 2 of chunk (lane % 32) / 2).
-  const int xm = NMT == 2 ? wave * 4 + (lane >> 4) : wave * 2 + (lane >> 5);
-  const int xc = NMT == 2 ? (lane & 15) : ((lane & 31) >> 1);
-  const int xh = NMT == 2 ? 0 : (lane & 1);
+  // Activation share: thread tid loads the 16-byte chunk tid % 16 of row (tid / 16) mod
+  // 16*NMT of the stage; with NMT = 1 the upper 256 threads repeat the lower ones' loads and
+  // do not write.  Gate/up reads x as given and puts each chunk into the dequantised
+  // weights' k-order (permute8) on its way to LDS; down reads h, already in that order.
+  const int xm = (tid >> 4) & (NMT * 16 - 1);
+  const int xc = tid & 15;
+  const bool x_writer = tid < NMT * 256;
   uint32_t x_off;
   {
     const int mm = min(xm, mcount - 1);
     const int row = GATED ? a.perm[pos0 + mm] / a.top_k : pos0 + mm;
-    x_off = ((uint32_t)row * (uint32_t)a.K + xc * 8 + xh * 4) * 2;
+    x_off = ((uint32_t)row * (uint32_t)a.K + xc * 8) * 2;
   }
   const bool x_tail = xc * 8 >= (a.K & 127);             // chunk past K in a half stage
   const char* act = reinterpret_cast<const char*>(a.act);
-  const int xdst = xm * kXRowBytes + ((xc ^ xswz(xm)) << 4) + xh * 8;
+  const int xdst = xm * kXRowBytes + ((xc ^ xswz(xm)) << 4);
 
   auto load = [&](int c) {
     const int cl = min(c, NS - 1);
@@ -479,23 +481,15 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
     // the half stage past an odd G re-reads the row's first chunk (never used)
     const uint32_t xo = x_off + ((cl * kStageK * 2 + 256 > a.K * 2 && x_tail) ? 0u : (uint32_t)cl * kStageK * 2);
     PkStage r;
-    if (NMT == 2) {
-      r.x = *reinterpret_cast<const u32x4_t*>(act + xo);
-    } else {
-      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(act + xo);
-      r.x = u32x4_t{v[0], v[1], 0u, 0u};
-    }
+    r.x = *reinterpret_cast<const u32x4_t*>(act + xo);
     r.wa = *reinterpret_cast<const u32x4_t*>(st + wa_off);
     r.wb = *reinterpret_cast<const u32x4_t*>(st + wa_off + 1024);
     r.sz = *reinterpret_cast<const u32x4_t*>(st + sz_off);
     return r;
   };
   auto put_x = [&](const PkStage& r, int slot) {
-    char* d = lds + slot * kPkXSlot + xdst;
-    if (NMT == 2)
-      *reinterpret_cast<u32x4_t*>(d) = r.x;
-    else
-      *reinterpret_cast<u32x2_t*>(d) = u32x2_t{r.x[0], r.x[1]};
+    if (x_writer)
+      *reinterpret_cast<u32x4_t*>(lds + slot * kPkXSlot + xdst) = GATED ? permute8(r.x) : r.x;
   };
 
   float4_t totA[NMT], totB[NMT];
@@ -924,20 +918,23 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.d_ff = d_ff;
   a.top_k = top_k;
   a.tiles = d_ff / 64;
-  a.act = ws.xp;
+  a.act = x;
   a.perm = ws.perm;
   a.items = ws.items;
   a.pk = gu.pk;
   a.h_out = ws.h;
   a.o_out = nullptr;
   a.out_ld = d_ff;
-  // Group the assignments by expert and permute x (one launch), then the GEMM.
-  hipError_t err = launch_bucket(T, E, top_k, x, d_model, ws, stream);
-  if (err != hipSuccess) return err;
+  (void)E;
+  // The expert buckets and the work list are in ws from the routing launch.  The packed
+  // kernel reorders x in registers; the tile kernel needs a reordered copy first.
   if (gu.pk) {
     a.tiles = pk_tiles(true, d_model, d_ff);
     launch_packed<true>(a, ws.max_items, stream);
   } else {
+    hipError_t err = launch_permute(T, x, d_model, ws, stream);
+    if (err != hipSuccess) return err;
+    a.act = ws.xp;
     hipLaunchKernelGGL(w4a16_gemm_kernel<true>, dim3(grid_blocks(ws.max_items, a.tiles)),
                        dim3(kThreads), 0, stream, a);
   }

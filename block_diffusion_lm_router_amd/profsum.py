@@ -33,8 +33,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def kernel_source_hash():
-    """Short hash of the sources of the gate/up entry point's kernels (the grouped GEMM and
-    the bucketing launch before it), stamped on traffic summaries so that a summary taken on
+    """Short hash of the sources behind the gate/up launch (the grouped GEMM, and the routing
+    that builds its work list), stamped on traffic summaries so that a summary taken on
     another version of them is recognised as stale."""
     h = hashlib.sha256()
     for name in ("moe_w4a16.hip", "moe_route.hip"):

@@ -146,17 +146,17 @@ int moe_w4a16_prepare(const bd_moe_weights* w, uint8_t* gate_up_packed, uint8_t*
  * Device workspace bytes needed by the MoE entry points for T tokens.  The same
  * workspace carries the routing state from moe_route_topk to moe_w4a16_gate_up and
  * moe_w4a16_down (a copy of the top-k ids, the expert buckets, the work list, the
- * permuted activations and the fp16 GeGLU activations h [T*k][d_ff]).  Its contents
- * need no initialisation.  Returns 0 if the shape is invalid.
+ * permuted activations for raw weights and the fp16 GeGLU activations h [T*k][d_ff]).
+ * Its contents need no initialisation.  Returns 0 if the shape is invalid.
  */
 size_t bd_moe_workspace_size(int T, const bd_moe_weights* w);
 
 /*
  * Routing: per token, the top_k experts by descending router logit (the lower expert
  * id first on equal logits) and their weights = softmax over the k selected logits.
- * The ids are also kept in the workspace, from which moe_w4a16_gate_up forms the
- * stable bucketing of the T*k assignments by expert (ordered by token, then slot) and
- * the work list of touched experts.
+ * A second launch (one block) writes the stable bucketing of the T*k assignments by
+ * expert (ordered by token, then slot) and the work list of touched experts to the
+ * workspace, for moe_w4a16_gate_up and moe_w4a16_down.
  * Source: axe-diffusion-ksl-xe model card, "what the model is" (128 experts, top-8)
  * and "the kernels we built" (one launch over all experts, not a per-expert loop).
  *
@@ -176,8 +176,9 @@ int moe_route_topk(const bd_moe_weights* w, int T, const float* router_logits,
  * gelu_tanh(a) = a/2 (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))).  Packed nibbles are
  * streamed once per expert tile, dequantised in registers, contracted on MFMA with
  * fp32 accumulation per 64-group, scaled per group; h is kept in the workspace as fp16.
- * The launch is preceded by one that groups the assignments by expert (from the ids the
- * routing left in the workspace) and reorders x for the GEMM.
+ * The expert buckets and the work list come from the routing in the workspace.  With
+ * packed weights x is reordered in registers on its way to LDS; with raw weights a
+ * small launch first writes a reordered copy of x into the workspace.
  * Source: axe-diffusion-ksl-xe model card, "the kernels we built" (inline dequant of
  * packed nibbles, activation folded into the first GEMM's epilogue).
  * Requires a preceding moe_route_topk on the same workspace and stream.
