@@ -10,6 +10,10 @@ Passages followed (pages named in the package docstring):
 * DiffusionGemma block-diffusion page, "Samplers", entropy-bound: per-position
   entropy, positions sorted by ascending entropy, accepted while
   (cumsum - cummax) <= bound, at least one position always accepted.
+* same page, "Samplers", confidence-threshold: every unrevealed position whose
+  top-1 token probability is above the threshold (flag default 0.9, validated to
+  [0, 1]) is accepted; when none is, the single most confident unrevealed position
+  is accepted so that every step makes progress.
 
 Readings taken where the pages are silent or loose (each listed in the design doc):
 
@@ -39,6 +43,13 @@ Readings taken where the pages are silent or loose (each listed in the design doc):
   c <- S - H_i, accept while c <= bound.  cummax in ascending order is H_i
   itself.  If no candidate passes and candidates exist, the first is accepted.
   Candidates are the unfrozen positions whose entropy is not NaN.
+* The confidence of a position is the largest probability of softmax(x) at
+  temperature 1 (the same distribution as the entropy), 1 / sum_v exp(x_v - max x)
+  in float64; NaN for an invalid row, -1 for a frozen position.  "Above the
+  threshold" is strict (c > threshold), compared in float32 on the confidences
+  given.  Candidates are the unfrozen positions with a confidence that is not NaN
+  and not negative; the fallback takes the largest confidence, the lowest position
+  on ties, and accepts nothing when there is no candidate.
 
 Everything except the acceptance scan and the 24-bit uniforms is float64.
 Test infrastructure only.
@@ -97,6 +108,25 @@ def entropy(x):
     logp = (fin - m) - np.log(z)
     p = np.exp(logp)
     return float(-(p * logp).sum())
+
+
+def confidence(x):
+    """Top-1 probability max_v softmax(x)_v = 1 / sum_v exp(x_v - max x), in float64
+    (NaN if the row is invalid).  Entries at -inf contribute exp(-inf) = 0."""
+    x = np.asarray(x, dtype=np.float64)
+    if not row_is_valid(x):
+        return np.nan
+    fin = x[np.isfinite(x)]
+    return float(1.0 / np.exp(fin - fin.max()).sum())
+
+
+def confidence_rows(logits, frozen=None):
+    """Confidence of every row of ``logits`` [P, V]: -1 for frozen rows, NaN for invalid."""
+    logits = np.asarray(logits, dtype=np.float32)
+    out = np.empty(logits.shape[0])
+    for p in range(logits.shape[0]):
+        out[p] = -1.0 if (frozen is not None and frozen[p]) else confidence(logits[p])
+    return out
 
 
 def chunk_logmass(x, temperature):
@@ -169,5 +199,31 @@ def accept(entropy32, bound, frozen=None):
         n += 1
     if n == 0 and order:
         mask[order[0]] = 1
+        n = 1
+    return mask, n
+
+
+def accept_confidence(conf32, threshold, frozen=None):
+    """Confidence-threshold acceptance on float32 confidences.  Returns (mask uint8 [P], count).
+
+    Accepted: every candidate with c > threshold; if there is none, the candidate with the
+    largest c (lowest position on ties).  Candidates: unfrozen, c not NaN, c >= 0.
+    """
+    c = np.asarray(conf32, dtype=np.float32)
+    P = c.shape[0]
+    frozen = np.zeros(P, dtype=bool) if frozen is None else np.asarray(frozen, dtype=bool)
+    thr = np.float32(threshold)
+    cand = [p for p in range(P) if not frozen[p] and not np.isnan(c[p]) and c[p] >= 0]
+    mask = np.zeros(P, dtype=np.uint8)
+    for p in cand:
+        if c[p] > thr:
+            mask[p] = 1
+    n = int(mask.sum())
+    if n == 0 and cand:
+        best = cand[0]
+        for p in cand[1:]:
+            if c[p] > c[best]:
+                best = p
+        mask[best] = 1
         n = 1
     return mask, n

@@ -198,3 +198,83 @@ def test_accept_invariants(hs, bound, fro):
     assert not np.any(mask[frozen])
     assert sorted(np.nonzero(mask)[0].tolist()) == sorted(p for _, p in cand[:n])
     assert n <= sampler.accept(H, bound + 1.0, frozen)[1]
+
+
+# ---------------------------------------------------------------- confidence-threshold
+
+def test_confidence_uniform_row():
+    for V in (1, 2, 7, 4096):
+        assert abs(sampler.confidence(np.full(V, -1.5, dtype=np.float32)) - 1.0 / V) < 1e-15
+
+
+@pytest.mark.parametrize("n,V,a,b", [(1, 4096, 12.0, 0.0), (3, 100, 2.0, -1.0), (2, 2, 0.5, 0.5),
+                                     (1, 262144, 26.0, 0.0)])
+def test_confidence_two_level_closed_form(n, V, a, b):
+    x = np.full(V, b, dtype=np.float32)
+    x[:n] = a
+    top = max(a, b)
+    Z = n * math.exp(a - top) + (V - n) * math.exp(b - top)
+    assert abs(sampler.confidence(x) - 1.0 / Z) <= 1e-12 / Z
+
+
+def test_confidence_is_softmax_max_and_bounds_entropy():
+    """The library softmax's largest entry; and since the min-entropy -ln p_max never exceeds
+    the entropy, exp(-H) <= p_max <= 1, with p_max >= 1/V."""
+    rng = np.random.default_rng(7)
+    for scale in (0.1, 1.0, 6.0):
+        x = (rng.standard_normal(5000) * scale).astype(np.float32)
+        c = sampler.confidence(x)
+        assert abs(c - special.softmax(x.astype(np.float64)).max()) < 1e-14
+        assert math.exp(-sampler.entropy(x)) <= c * (1 + 1e-12) and c <= 1.0
+        assert c >= 1.0 / x.size
+
+
+def test_confidence_minus_inf_invalid_and_frozen():
+    assert sampler.confidence(np.array([-np.inf, 3.0], dtype=np.float32)) == 1.0
+    assert abs(sampler.confidence(np.array([0, -np.inf, 0], dtype=np.float32)) - 0.5) < 1e-15
+    for bad in ([0.0, np.nan], [np.inf, 0.0], [-np.inf, -np.inf]):
+        assert math.isnan(sampler.confidence(np.array(bad, dtype=np.float32)))
+    logits = np.zeros((3, 8), dtype=np.float32)
+    logits[2, 0] = np.nan
+    c = sampler.confidence_rows(logits, frozen=np.array([0, 1, 0], dtype=np.uint8))
+    assert c[0] == 0.125 and c[1] == -1.0 and math.isnan(c[2])
+
+
+def _accept_by_sorting(c, thr, frozen):
+    """The page's rule, written another way: candidates above the threshold, else the head
+    of the candidates ordered by descending confidence then ascending position."""
+    cand = [p for p in range(len(c)) if not frozen[p] and c[p] == c[p] and c[p] >= 0]
+    above = [p for p in cand if c[p] > np.float32(thr)]
+    if above:
+        return set(above)
+    if not cand:
+        return set()
+    return {sorted(cand, key=lambda p: (-float(c[p]), p))[0]}
+
+
+def test_accept_confidence_brute_force():
+    values = np.array([0.0, 0.25, 0.5, 0.9, np.float32(0.9) + np.float32(1e-7), 1.0, np.nan, -1.0],
+                      dtype=np.float32)
+    rng = np.random.default_rng(3)
+    for P in range(1, 6):
+        for _ in range(300):
+            c = values[rng.integers(0, values.size, P)]
+            frozen = rng.integers(0, 2, P).astype(np.uint8) if rng.random() < 0.5 else np.zeros(P, np.uint8)
+            thr = float(rng.choice([0.0, 0.5, 0.9, 1.0]))
+            mask, n = sampler.accept_confidence(c, thr, frozen)
+            want = _accept_by_sorting(c, thr, frozen)
+            assert set(np.nonzero(mask)[0].tolist()) == want and n == len(want)
+
+
+def test_accept_confidence_edges():
+    c = np.array([0.9, 0.3, 0.95, 0.95], dtype=np.float32)
+    mask, n = sampler.accept_confidence(c, 0.9)
+    assert mask.tolist() == [0, 0, 1, 1] and n == 2            # equal to the threshold: not above
+    mask, n = sampler.accept_confidence(c, 1.0)
+    assert mask.tolist() == [0, 0, 1, 0] and n == 1            # fallback: first of the tied maxima
+    mask, n = sampler.accept_confidence(c, 0.5, frozen=np.array([0, 0, 1, 1]))
+    assert mask.tolist() == [1, 0, 0, 0] and n == 1            # frozen never accepted
+    mask, n = sampler.accept_confidence(c, 0.5, frozen=np.ones(4))
+    assert n == 0 and mask.sum() == 0                          # nothing to accept
+    mask, n = sampler.accept_confidence(np.array([np.nan, -1.0, 0.1], dtype=np.float32), 0.9)
+    assert mask.tolist() == [0, 0, 1] and n == 1               # NaN and frozen markers skipped
