@@ -65,6 +65,11 @@ SIGNATURES = {
     "diffusion_accept_entropy_bound": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
     "diffusion_sample_step": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P, _P, _P,
                                    _SZ, _P]),
+    "diffusion_sample_confidence": (_I, [_P, _I, _I, _F, _U64, _U32, _P, _P, _P, _P, _P, _SZ,
+                                         _P]),
+    "diffusion_accept_confidence": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
+    "diffusion_sample_step_confidence": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P,
+                                              _P, _P, _SZ, _P]),
     "bd_hbm_copy": (_I, [_P, _P, _SZ, _P]),
     "bd_hbm_read": (_I, [_P, _SZ, _P, _P]),
 }
@@ -292,6 +297,41 @@ def diffusion_sample_step(logits, temperature, entropy_bound, seed, step, frozen
                    _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
                    _ptr(tokens_out, torch.int32, "tokens_out"),
                    _ptr(entropy_out, torch.float32, "entropy_out"),
+                   _ptr(accept_out, torch.uint8, "accept_out"),
+                   _ptr(num_accepted, torch.int32, "num_accepted"),
+                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+
+
+def diffusion_sample_confidence(logits, temperature, seed, step, frozen, tokens_out, entropy_out,
+                                confidence_out, workspace):
+    P, V = logits.shape
+    return _invoke("diffusion_sample_confidence", _ptr(logits, torch.float32, "logits"), P, V,
+                   float(temperature), int(seed), int(step), _ptr(frozen, torch.uint8, "frozen"),
+                   _ptr(tokens_out, torch.int32, "tokens_out"),
+                   _ptr(entropy_out, torch.float32, "entropy_out"),
+                   _ptr(confidence_out, torch.float32, "confidence_out"),
+                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+
+
+def diffusion_accept_confidence(confidence, tokens, threshold, frozen, canvas, accept_out,
+                                num_accepted):
+    P = confidence.shape[0]
+    return _invoke("diffusion_accept_confidence", _ptr(confidence, torch.float32, "confidence"),
+                   _ptr(tokens, torch.int32, "tokens"), P, float(threshold),
+                   _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
+                   _ptr(accept_out, torch.uint8, "accept_out"),
+                   _ptr(num_accepted, torch.int32, "num_accepted"), _stream())
+
+
+def diffusion_sample_step_confidence(logits, temperature, threshold, seed, step, frozen, canvas,
+                                     tokens_out, confidence_out, accept_out, num_accepted,
+                                     workspace):
+    P, V = logits.shape
+    return _invoke("diffusion_sample_step_confidence", _ptr(logits, torch.float32, "logits"), P,
+                   V, float(temperature), float(threshold), int(seed), int(step),
+                   _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
+                   _ptr(tokens_out, torch.int32, "tokens_out"),
+                   _ptr(confidence_out, torch.float32, "confidence_out"),
                    _ptr(accept_out, torch.uint8, "accept_out"),
                    _ptr(num_accepted, torch.int32, "num_accepted"),
                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())

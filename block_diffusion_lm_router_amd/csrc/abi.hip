@@ -213,7 +213,7 @@ int diffusion_sample_entropy(const float* logits, int P, int V, float temperatur
   st = check_workspace(workspace, workspace_bytes, bd::sample_workspace_bytes(P, V));
   if (st != BD_OK) return st;
   return to_status(bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
-                                             tokens_out, entropy_out, workspace,
+                                             tokens_out, entropy_out, nullptr, workspace,
                                              as_stream(stream)));
 }
 
@@ -245,10 +245,66 @@ int diffusion_sample_step(const float* logits, int P, int V, float temperature,
   if (st != BD_OK) return st;
   hipStream_t s = as_stream(stream);
   hipError_t err = bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
-                                             tokens_out, entropy_out, workspace, s);
+                                             tokens_out, entropy_out, nullptr, workspace, s);
   if (err == hipSuccess)
     err = bd::launch_accept(entropy_out, tokens_out, P, entropy_bound, frozen, canvas, accept_out,
                             num_accepted, s);
+  return to_status(err);
+}
+
+static bool threshold_ok(float threshold) { return threshold >= 0.f && threshold <= 1.f; }
+
+int diffusion_sample_confidence(const float* logits, int P, int V, float temperature,
+                                uint64_t seed, uint32_t step, const uint8_t* frozen,
+                                int32_t* tokens_out, float* entropy_out, float* confidence_out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_sample_shape(P, V, temperature);
+  if (st != BD_OK) return st;
+  if (!logits || !tokens_out || !confidence_out) return BD_ERR_NULL;
+  if (!aligned16(logits) || !aligned4(tokens_out) || !aligned4(confidence_out) ||
+      (entropy_out && !aligned4(entropy_out)))
+    return BD_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, bd::sample_workspace_bytes(P, V));
+  if (st != BD_OK) return st;
+  return to_status(bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
+                                             tokens_out, entropy_out, confidence_out, workspace,
+                                             as_stream(stream)));
+}
+
+int diffusion_accept_confidence(const float* confidence, const int32_t* tokens, int P,
+                                float threshold, uint8_t* frozen, int32_t* canvas,
+                                uint8_t* accept_out, int32_t* num_accepted, void* stream) {
+  if (P < 1 || P > BD_MAX_POSITIONS || !threshold_ok(threshold)) return BD_ERR_SHAPE;
+  if (!confidence || !tokens || !accept_out || !num_accepted) return BD_ERR_NULL;
+  if (!aligned4(confidence) || !aligned4(tokens) || !aligned4(num_accepted) ||
+      (canvas && !aligned4(canvas)))
+    return BD_ERR_ALIGN;
+  return to_status(bd::launch_accept_confidence(confidence, tokens, P, threshold, frozen, canvas,
+                                                accept_out, num_accepted, as_stream(stream)));
+}
+
+int diffusion_sample_step_confidence(const float* logits, int P, int V, float temperature,
+                                     float threshold, uint64_t seed, uint32_t step,
+                                     uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                                     float* confidence_out, uint8_t* accept_out,
+                                     int32_t* num_accepted, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  int st = check_sample_shape(P, V, temperature);
+  if (st != BD_OK) return st;
+  if (!threshold_ok(threshold)) return BD_ERR_SHAPE;
+  if (!logits || !tokens_out || !confidence_out || !accept_out || !num_accepted)
+    return BD_ERR_NULL;
+  if (!aligned16(logits) || !aligned4(tokens_out) || !aligned4(confidence_out) ||
+      !aligned4(num_accepted) || (canvas && !aligned4(canvas)))
+    return BD_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, bd::sample_workspace_bytes(P, V));
+  if (st != BD_OK) return st;
+  hipStream_t s = as_stream(stream);
+  hipError_t err = bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
+                                             tokens_out, nullptr, confidence_out, workspace, s);
+  if (err == hipSuccess)
+    err = bd::launch_accept_confidence(confidence_out, tokens_out, P, threshold, frozen, canvas,
+                                       accept_out, num_accepted, s);
   return to_status(err);
 }
 

@@ -73,11 +73,15 @@ int sample_split_count(int P, int V);
 size_t sample_workspace_bytes(int P, int V);
 hipError_t launch_sample_entropy(const float* logits, int P, int V, float temperature,
                                  uint64_t seed, uint32_t step, const uint8_t* frozen,
-                                 int32_t* tokens_out, float* entropy_out, void* workspace,
-                                 hipStream_t stream);
+                                 int32_t* tokens_out, float* entropy_out, float* conf_out,
+                                 void* workspace, hipStream_t stream);
 hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, float bound,
                          uint8_t* frozen, int32_t* canvas, uint8_t* accept_out,
                          int32_t* num_accepted, hipStream_t stream);
+hipError_t launch_accept_confidence(const float* conf, const int32_t* tokens, int P,
+                                    float threshold, uint8_t* frozen, int32_t* canvas,
+                                    uint8_t* accept_out, int32_t* num_accepted,
+                                    hipStream_t stream);
 
 // ---------------------------------------------------------------- measurement
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);

@@ -258,47 +258,45 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     const float* __restrict__ logits, int V, int nC, int S, float temperature, uint32_t k0,
     uint32_t k1, uint32_t step, const uint8_t* __restrict__ frozen,
     const PartState* __restrict__ part, const float* __restrict__ lmass,
-    int32_t* __restrict__ tokens_out, float* __restrict__ entropy_out) {
+    int32_t* __restrict__ tokens_out, float* __restrict__ entropy_out,
+    float* __restrict__ conf_out) {
   const int p = blockIdx.x;
   const int tid = threadIdx.x;
   if (frozen != nullptr && frozen[p]) {
     if (tid == 0) {
       tokens_out[p] = -1;
-      entropy_out[p] = INFINITY;
+      if (entropy_out != nullptr) entropy_out[p] = INFINITY;
+      if (conf_out != nullptr) conf_out[p] = -1.f;
     }
     return;
   }
-  __shared__ float sH;
   __shared__ int sValid, sArg;
   __shared__ double skey[kFinishThreads];
   __shared__ int sidx[kFinishThreads];
   if (tid == 0) {
     PartState acc = part[(size_t)p * S];
     for (int s = 1; s < S; ++s) merge_state(acc, part[(size_t)p * S + s]);
-    float H = NAN;
+    float H = NAN, conf = NAN;
     bool valid = !acc.nan && acc.m != -INFINITY;
     if (valid) {
+      // Z = sum exp(x - m); the top-1 probability is exp(0) / Z.
       const float Z = acc.n + acc.s;
       H = log1pf((acc.n - 1.f) + acc.s) - acc.t / Z;
+      conf = 1.f / Z;
       valid = !(H != H);
     }
-    sH = valid ? H : NAN;
     sValid = valid ? 1 : 0;
     sArg = acc.best_i;
+    if (entropy_out != nullptr) entropy_out[p] = valid ? H : NAN;
+    if (conf_out != nullptr) conf_out[p] = valid ? conf : NAN;
   }
   __syncthreads();
   if (!sValid) {
-    if (tid == 0) {
-      tokens_out[p] = -1;
-      entropy_out[p] = NAN;
-    }
+    if (tid == 0) tokens_out[p] = -1;
     return;
   }
   if (temperature == 0.f) {
-    if (tid == 0) {
-      tokens_out[p] = sArg;
-      entropy_out[p] = sH;
-    }
+    if (tid == 0) tokens_out[p] = sArg;
     return;
   }
   // Level 1: chunk keys K_c = L_c + G_c, G_c from counter (c, p, step, 1) word 0.
@@ -337,10 +335,7 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     }
   }
   block_argmax(sbest, sv, skey, sidx);
-  if (tid == 0) {
-    tokens_out[p] = sv;
-    entropy_out[p] = sH;
-  }
+  if (tid == 0) tokens_out[p] = sv;
 }
 
 // ---------------------------------------------------------------- acceptance (one block)
@@ -435,6 +430,56 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
   }
 }
 
+// Confidence-threshold acceptance on one workgroup.  Candidates: not frozen, confidence
+// not NaN and >= 0 (frozen rows carry -1).  Every candidate with confidence > threshold is
+// accepted; if none is, the candidate with the largest confidence (lowest position on ties)
+// is.  The fallback key orders by confidence, then by inverted position, so one max
+// reduction picks it.
+__global__ __launch_bounds__(kAcceptThreads) void accept_conf_kernel(
+    const float* __restrict__ conf, const int32_t* __restrict__ tokens, int P, float threshold,
+    uint8_t* __restrict__ frozen, int32_t* __restrict__ canvas, uint8_t* __restrict__ accept_out,
+    int32_t* __restrict__ num_accepted) {
+  __shared__ uint64_t wbest[kAcceptThreads / kWave];
+  __shared__ int sPick;
+  const int tid = threadIdx.x;
+  bool cand = false, pass = false;
+  uint64_t key = 0;
+  if (tid < P) {
+    const float c = conf[tid];
+    const bool is_frozen = frozen != nullptr && frozen[tid];
+    cand = !is_frozen && c >= 0.f;  // false for NaN
+    pass = cand && c > threshold;
+    if (cand) key = ((uint64_t)float_order_key(c) << 32) | (uint32_t)(0xffffffffu - (uint32_t)tid);
+  }
+  const int n_pass = __syncthreads_count(pass);
+  bool take = pass;
+  int count = n_pass;
+  if (n_pass == 0) {
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint64_t o = __shfl_xor(key, off);
+      key = o > key ? o : key;
+    }
+    if (lane_id() == 0) wbest[tid / kWave] = key;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t b = 0;
+      for (int w = 0; w < kAcceptThreads / kWave; ++w) b = wbest[w] > b ? wbest[w] : b;
+      sPick = b == 0 ? -1 : (int)(0xffffffffu - (uint32_t)b);
+    }
+    __syncthreads();
+    take = tid == sPick;
+    count = sPick >= 0 ? 1 : 0;
+  }
+  if (tid < P) {
+    accept_out[tid] = take ? 1 : 0;
+    if (take) {
+      if (canvas != nullptr) canvas[tid] = tokens[tid];
+      if (frozen != nullptr) frozen[tid] = 1;
+    }
+  }
+  if (tid == 0) *num_accepted = count;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- host-side launchers
@@ -448,8 +493,8 @@ int sample_split_count(int P, int V) {
 
 hipError_t launch_sample_entropy(const float* logits, int P, int V, float temperature,
                                  uint64_t seed, uint32_t step, const uint8_t* frozen,
-                                 int32_t* tokens_out, float* entropy_out, void* workspace,
-                                 hipStream_t stream) {
+                                 int32_t* tokens_out, float* entropy_out, float* conf_out,
+                                 void* workspace, hipStream_t stream) {
   const int nC = (V + kChunk - 1) / kChunk;
   const int S = sample_split_count(P, V);
   PartState* part = reinterpret_cast<PartState*>(workspace);
@@ -470,7 +515,7 @@ hipError_t launch_sample_entropy(const float* logits, int P, int V, float temper
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(sample_finish_kernel, dim3(P), dim3(kFinishThreads), 0, stream, logits, V, nC,
                      S, temperature, (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32), step,
-                     frozen, part, lmass, tokens_out, entropy_out);
+                     frozen, part, lmass, tokens_out, entropy_out, conf_out);
   return hipGetLastError();
 }
 
@@ -485,6 +530,15 @@ hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, flo
                          int32_t* num_accepted, hipStream_t stream) {
   hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kAcceptThreads), 0, stream, entropy, tokens, P,
                      bound, frozen, canvas, accept_out, num_accepted);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_confidence(const float* conf, const int32_t* tokens, int P,
+                                    float threshold, uint8_t* frozen, int32_t* canvas,
+                                    uint8_t* accept_out, int32_t* num_accepted,
+                                    hipStream_t stream) {
+  hipLaunchKernelGGL(accept_conf_kernel, dim3(1), dim3(kAcceptThreads), 0, stream, conf, tokens,
+                     P, threshold, frozen, canvas, accept_out, num_accepted);
   return hipGetLastError();
 }
 

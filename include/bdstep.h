@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 3
+#define BD_ABI_VERSION 4
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -281,6 +281,53 @@ int diffusion_sample_step(const float* logits, int P, int V, float temperature,
                           uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
                           float* entropy_out, uint8_t* accept_out, int32_t* num_accepted,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Confidence-threshold variant of the sampler.  The same single streaming pass as
+ * diffusion_sample_entropy (same tokens, same entropies), which also writes the top-1
+ * probability of every position that is not frozen:
+ *   confidence_out[p] = max_v softmax(x_p)_v = 1 / sum_v exp(x_pv - max_v x_pv)
+ * (temperature 1, whatever the sampling temperature), evaluated in fp32 from the pass's
+ * running sums.  Frozen rows get -1 (and token -1, entropy +inf); invalid rows (NaN, +inf,
+ * or only -inf) get NaN.  entropy_out may be NULL.
+ * Source: DiffusionGemma block-diffusion page, "Samplers" (confidence-threshold: the top-1
+ * token probability of each unrevealed position).
+ */
+int diffusion_sample_confidence(const float* logits, int P, int V, float temperature,
+                                uint64_t seed, uint32_t step, const uint8_t* frozen,
+                                int32_t* tokens_out, float* entropy_out, float* confidence_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Confidence-threshold acceptance on one workgroup.  Candidates are the positions that
+ * are not frozen and whose confidence is neither NaN nor negative.  Every candidate with
+ * confidence > threshold (strict, fp32) is accepted; if candidates exist and none
+ * qualifies, the candidate with the largest confidence (lowest position on ties) is
+ * accepted alone, so each call makes progress.  Each accepted p gets accept_out[p] = 1,
+ * canvas[p] = tokens[p] and frozen[p] = 1; every other accept_out entry is 0.
+ * Source: DiffusionGemma block-diffusion page, "Samplers" (confidence-threshold) and its
+ * options table (threshold default 0.9, validated to [0, 1]).
+ *
+ *   confidence    fp32  [P]      (the device's own confidences, e.g. from above)
+ *   tokens        int32 [P]
+ *   frozen        uint8 [P] in/out, or NULL (none frozen, nothing recorded)
+ *   canvas        int32 [P] in/out, or NULL (not updated)
+ *   accept_out    uint8 [P] out
+ *   num_accepted  int32 [1] out
+ *   threshold     in [0, 1], else BD_ERR_SHAPE
+ */
+int diffusion_accept_confidence(const float* confidence, const int32_t* tokens, int P,
+                                float threshold, uint8_t* frozen, int32_t* canvas,
+                                uint8_t* accept_out, int32_t* num_accepted, void* stream);
+
+/* diffusion_sample_confidence (no entropy output) then diffusion_accept_confidence on the
+ * same stream. */
+int diffusion_sample_step_confidence(const float* logits, int P, int V, float temperature,
+                                     float threshold, uint64_t seed, uint32_t step,
+                                     uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                                     float* confidence_out, uint8_t* accept_out,
+                                     int32_t* num_accepted, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ measurement */
 

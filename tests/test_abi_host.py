@@ -135,6 +135,26 @@ def test_sampler_validation(lib):
     assert lib.bd_hbm_read(ctypes.c_void_p(0x1004), 16, P, None) == 3
 
 
+def test_confidence_sampler_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    n = lib.bd_sample_workspace_size(256, 262144)
+    call = lib.diffusion_sample_confidence
+    assert call(P, 256, 262144, -1.0, 0, 0, None, P, None, P, P, n, None) == 2
+    assert call(P, 256, 262144, 1.0, 0, 0, None, P, None, None, P, n, None) == 1
+    assert call(P, 256, 262144, 1.0, 0, 0, None, P, None, P, P, n - 1, None) == 4
+    assert call(P, 256, 262144, 1.0, 0, 0, None, P, ctypes.c_void_p(0x1002), P, P, n, None) == 3
+    acc = lib.diffusion_accept_confidence
+    for bad in (-0.01, 1.01, float("nan"), float("inf")):
+        assert acc(P, P, 8, bad, None, None, P, P, None) == 2
+    assert acc(P, P, 0, 0.9, None, None, P, P, None) == 2
+    assert acc(P, P, 1025, 0.9, None, None, P, P, None) == 2
+    assert acc(None, P, 8, 0.9, None, None, P, P, None) == 1
+    assert acc(P, P, 8, 0.9, None, ctypes.c_void_p(0x1001), P, P, None) == 3
+    step = lib.diffusion_sample_step_confidence
+    assert step(P, 8, 100, 1.0, 1.5, 0, 0, None, None, P, P, P, P, P, 1 << 20, None) == 2
+    assert step(P, 8, 100, 1.0, 0.9, 0, 0, None, None, P, None, P, P, P, 1 << 20, None) == 1
+
+
 def test_prepare_sizes_and_validation(lib):
     w = _weights()
     ref = ctypes.byref(w)

@@ -1,8 +1,9 @@
-"""GPU parity of the sampler (diffusion_sample_entropy / _accept_entropy_bound / _step)
-against the CPU oracle, through the C ABI.
+"""GPU parity of the sampler (diffusion_sample_entropy / _accept_entropy_bound / _step and
+the confidence-threshold variant diffusion_sample_confidence / _accept_confidence /
+_step_confidence) against the CPU oracle, through the C ABI.
 
 Bars: tokens at temperature 0 and acceptance masks bit-exact (the mask fed the GPU's
-entropies); entropies within 1e-4 relative; tokens at T > 0 bit-exact except where the
+entropies or confidences); entropies within 1e-4 relative, confidences within 1e-5; tokens at T > 0 bit-exact except where the
 oracle's own decision margin is below the rounding of the chunk log-masses.
 """
 
@@ -13,7 +14,7 @@ import pytest
 
 from block_diffusion_lm_router_amd import workloads
 from oracle import sampler as osamp
-from gpu_common import (H_REL, L1_MARGIN, L2_MARGIN, requires_gpu, say, top2_margin)
+from gpu_common import (C_REL, H_REL, L1_MARGIN, L2_MARGIN, requires_gpu, say, top2_margin)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -235,3 +236,148 @@ def test_full_size_step(bd, which):
         assert np.array_equal(canvas.cpu().numpy(), np.where(ref_mask == 1, tok_np, -7))
         if which == "sampler_wide":
             assert ref_n > 1        # the wide-boost variant exercises multi-accept
+
+
+# ---------------------------------------------------------------- confidence-threshold
+
+
+def run_confidence(bd, logits_np, temperature, seed=0, step=0, frozen_np=None):
+    import torch
+    P, V = logits_np.shape
+    logits = torch.from_numpy(np.ascontiguousarray(logits_np)).cuda()
+    frozen = None if frozen_np is None else torch.from_numpy(frozen_np.astype(np.uint8)).cuda()
+    tok = torch.empty(P, dtype=torch.int32, device="cuda")
+    H = torch.empty(P, dtype=torch.float32, device="cuda")
+    C = torch.empty(P, dtype=torch.float32, device="cuda")
+    ws = bd.sample_workspace(P, V)
+    bd.diffusion_sample_confidence(logits, temperature, seed, step, frozen, tok, H, C, ws)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), H.cpu().numpy(), C.cpu().numpy()
+
+
+def check_confidence(C_gpu, C_ref):
+    for p, (g, r) in enumerate(zip(C_gpu.astype(np.float64), C_ref)):
+        if math.isnan(r):
+            assert math.isnan(g), f"row {p}: expected NaN, got {g}"
+        elif r < 0:
+            assert g == -1.0, f"row {p}: frozen row must carry -1, got {g}"
+        else:
+            assert abs(g - r) <= C_REL * r, f"row {p}: confidence {g} vs {r} (rel {abs(g - r) / r:.3g})"
+
+
+@pytest.mark.parametrize("temperature", [0.0, 1.0])
+def test_confidence_pass(bd, temperature):
+    """Same pass as the entropy entry point: identical tokens and entropies, plus the top-1
+    probability against the oracle, on ragged shapes and the special rows."""
+    rng = np.random.default_rng(42)
+    cases = [special_rows(), workloads.make_logits(workloads.TINY_SAMPLER),
+             (rng.standard_normal((5, 5003)) * 3).astype(np.float32),
+             (rng.standard_normal((3, 7)) * 3).astype(np.float32)]
+    for x in cases:
+        say("confidence pass", x.shape, temperature)
+        tok, H, C = run_confidence(bd, x, temperature, seed=7, step=2)
+        tok_e, H_e = run_entropy(bd, x, temperature, seed=7, step=2)
+        assert np.array_equal(tok, tok_e)
+        assert np.array_equal(H.view(np.uint32), H_e.view(np.uint32))
+        check_confidence(C, osamp.confidence_rows(x))
+    x = special_rows()
+    _, _, C = run_confidence(bd, x, 1.0)
+    assert C[3] == 1.0                                   # one live entry
+    assert abs(C[7] - 1.0 / x.shape[1]) <= C_REL / x.shape[1]   # uniform row: 1 / V
+
+
+def test_confidence_frozen_rows(bd):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((9, 2048)).astype(np.float32)
+    frozen = np.array([0, 1, 1, 0, 0, 1, 0, 0, 1], dtype=np.uint8)
+    x[frozen == 1] = np.nan                              # must not be read
+    say("confidence frozen rows")
+    tok, H, C = run_confidence(bd, x, 1.0, seed=1, frozen_np=frozen)
+    assert np.all(tok[frozen == 1] == -1) and np.all(np.isposinf(H[frozen == 1]))
+    check_confidence(C, osamp.confidence_rows(x, frozen))
+
+
+def run_accept_conf(bd, C_np, tokens_np, threshold, frozen_np=None, canvas_np=None):
+    import torch
+    P = C_np.shape[0]
+    C = torch.from_numpy(C_np.astype(np.float32)).cuda()
+    tok = torch.from_numpy(tokens_np.astype(np.int32)).cuda()
+    frozen = None if frozen_np is None else torch.from_numpy(frozen_np.astype(np.uint8)).cuda()
+    canvas = None if canvas_np is None else torch.from_numpy(canvas_np.astype(np.int32)).cuda()
+    acc = torch.full((P,), 7, dtype=torch.uint8, device="cuda")
+    cnt = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    bd.diffusion_accept_confidence(C, tok, threshold, frozen, canvas, acc, cnt)
+    torch.cuda.synchronize()
+    return (acc.cpu().numpy(), int(cnt.item()),
+            None if frozen is None else frozen.cpu().numpy(),
+            None if canvas is None else canvas.cpu().numpy())
+
+
+@pytest.mark.parametrize("P", [1, 2, 5, 64, 256, 1000, 1024])
+def test_accept_confidence_matches_oracle(bd, P):
+    rng = np.random.default_rng(1000 + P)
+    for trial in range(7):
+        C = rng.beta(0.5, 0.5, P).astype(np.float32)
+        C[rng.random(P) < 0.05] = np.nan
+        if trial == 1:
+            C[:] = 0.5                                   # all tied: lowest position wins
+        if trial == 2:
+            C = np.minimum(C, np.float32(0.9))           # nobody above: the fallback
+            C[rng.integers(0, P)] = np.float32(0.9)      # exactly at the threshold is not above
+        frozen = (rng.random(P) < 0.3).astype(np.uint8)
+        if trial == 3:
+            frozen[:] = 1                                # no candidate: count 0
+        tokens = rng.integers(0, 1000, P).astype(np.int32)
+        canvas = rng.integers(0, 1000, P).astype(np.int32)
+        thr = [0.9, 0.9, 0.9, 0.9, 0.0, 1.0, 0.5][trial]
+        say("accept confidence", P, trial, thr)
+        acc, cnt, fr, cv = run_accept_conf(bd, C, tokens, thr, frozen, canvas)
+        ref_mask, ref_n = osamp.accept_confidence(C, thr, frozen)
+        assert cnt == ref_n and np.array_equal(acc, ref_mask), f"P={P} trial={trial}"
+        assert np.array_equal(fr, np.maximum(frozen, ref_mask))
+        assert np.array_equal(cv, np.where(ref_mask == 1, tokens, canvas))
+        if trial == 3:
+            assert cnt == 0
+
+
+def test_accept_confidence_without_frozen_or_canvas(bd):
+    C = np.array([0.3, 0.95, -1.0, 0.91, np.nan, 0.9], dtype=np.float32)
+    acc, cnt, _, _ = run_accept_conf(bd, C, np.arange(6), 0.9)
+    ref_mask, ref_n = osamp.accept_confidence(C, 0.9)
+    assert cnt == ref_n == 2 and np.array_equal(acc, ref_mask)
+
+
+@pytest.mark.parametrize("which", ["sampler", "sampler_wide"])
+def test_full_size_step_confidence(bd, which):
+    import torch
+    shape = workloads.SAMPLER if which == "sampler" else workloads.SAMPLER_WIDE
+    x = workloads.make_logits(shape)
+    P, V = x.shape
+    say("full-size confidence", which, x.shape)
+    C_ref = osamp.confidence_rows(x)
+    for temperature, step in ((0.0, 0), (1.0, 6)):
+        logits = torch.from_numpy(x).cuda()
+        frozen = torch.zeros(P, dtype=torch.uint8, device="cuda")
+        frozen[::5] = 1
+        frozen_np = frozen.cpu().numpy()
+        canvas = torch.full((P,), -7, dtype=torch.int32, device="cuda")
+        tok = torch.empty(P, dtype=torch.int32, device="cuda")
+        C = torch.empty(P, dtype=torch.float32, device="cuda")
+        acc = torch.empty(P, dtype=torch.uint8, device="cuda")
+        cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+        ws = bd.sample_workspace(P, V)
+        bd.diffusion_sample_step_confidence(logits, temperature, 0.9, shape.seed, step, frozen,
+                                            canvas, tok, C, acc, cnt, ws)
+        torch.cuda.synchronize()
+        tok_np, C_np = tok.cpu().numpy(), C.cpu().numpy()
+        check_confidence(C_np, np.where(frozen_np == 1, -1.0, C_ref))
+        rows = [p for p in range(P) if not frozen_np[p]]
+        assert check_tokens_sampled(x, tok_np, temperature, shape.seed, step, rows=rows) <= 3
+        assert np.all(tok_np[frozen_np == 1] == -1)
+        ref_mask, ref_n = osamp.accept_confidence(C_np, 0.9, frozen_np)
+        assert int(cnt.item()) == ref_n
+        assert np.array_equal(acc.cpu().numpy(), ref_mask)
+        assert np.array_equal(frozen.cpu().numpy(), np.maximum(frozen_np, ref_mask))
+        assert np.array_equal(canvas.cpu().numpy(), np.where(ref_mask == 1, tok_np, -7))
+        if which == "sampler_wide":
+            assert ref_n > 1        # near-zero entropies put many rows above 0.9
