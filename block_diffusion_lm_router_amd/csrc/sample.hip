@@ -28,8 +28,21 @@ namespace bd {
 namespace {
 
 constexpr int kChunk = 1024;
-constexpr int kStreamThreads = 256;
+#ifndef BD_SAMPLE_THREADS
+#define BD_SAMPLE_THREADS 256
+#endif
+#ifndef BD_SAMPLE_RING
+#define BD_SAMPLE_RING 2
+#endif
+#ifndef BD_SAMPLE_BLOCKS
+#define BD_SAMPLE_BLOCKS 1024
+#endif
+#ifndef BD_SAMPLE_NT
+#define BD_SAMPLE_NT 1
+#endif
+constexpr int kStreamThreads = BD_SAMPLE_THREADS;
 constexpr int kStreamWaves = kStreamThreads / kWave;
+constexpr int kRing = BD_SAMPLE_RING;  // chunks in flight per wave
 
 // Loads chunk c of a row: entry e(j, q) = c*1024 + (j*64 + lane)*4 + q lands in x[4j + q].
 // Entries past V read as -inf (they carry no probability mass).
@@ -42,7 +55,11 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int V,
     for (int j = 0; j < 4; ++j) {
       const int idx = base + (j * kWave + lane) * 4;
       if (idx < V) {
+#if BD_SAMPLE_NT
         const float4_t v = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(row + idx));
+#else
+        const float4_t v = *reinterpret_cast<const float4_t*>(row + idx);
+#endif
         x[4 * j + 0] = v[0];
         x[4 * j + 1] = v[1];
         x[4 * j + 2] = v[2];
@@ -195,18 +212,23 @@ __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
   st.best_i = 0x7fffffff;
   st.nan = false;
 
-  float xa[16], xb[16];
-  int c = c_begin + wave;
-  if (c < c_end) load_chunk(row, V, c, vec, xa);
-  while (c < c_end) {
-    const int c2 = c + kStreamWaves;
-    if (c2 < c_end) load_chunk(row, V, c2, vec, xb);
-    process_chunk<MODE>(xa, c, invT, st, lmass_row);
-    if (c2 >= c_end) break;
-    const int c3 = c2 + kStreamWaves;
-    if (c3 < c_end) load_chunk(row, V, c3, vec, xa);
-    process_chunk<MODE>(xb, c2, invT, st, lmass_row);
-    c = c3;
+  // Ring of kRing chunks in registers per wave: chunk i of the wave's sequence sits in slot
+  // i % kRing and is refilled with chunk i + kRing right after it has been folded in.
+  float x[kRing][16];
+  const int c0 = c_begin + wave;
+#pragma unroll
+  for (int r = 0; r < kRing; ++r)
+    if (c0 + r * kStreamWaves < c_end) load_chunk(row, V, c0 + r * kStreamWaves, vec, x[r]);
+  for (int base = c0; base < c_end; base += kRing * kStreamWaves) {
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      const int c = base + r * kStreamWaves;
+      if (c < c_end) {
+        process_chunk<MODE>(x[r], c, invT, st, lmass_row);
+        const int cn = c + kRing * kStreamWaves;
+        if (cn < c_end) load_chunk(row, V, cn, vec, x[r]);
+      }
+    }
   }
 
   // Lanes share the reference maximum: the wave state is a plain sum.
@@ -232,28 +254,44 @@ __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
 // ---------------------------------------------------------------- finish (one block per row)
 
 constexpr int kFinishThreads = 256;
+constexpr int kFinishWaves = kFinishThreads / kWave;
+constexpr int kMaxSplits = BD_SAMPLE_BLOCKS;  // sample_split_count never exceeds this
 
 __device__ __forceinline__ bool better_key(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-__device__ void block_argmax(double& key, int& idx, double* skey, int* sidx) {
-  const int tid = threadIdx.x;
-  skey[tid] = key;
-  sidx[tid] = idx;
-  __syncthreads();
-  for (int off = kFinishThreads / 2; off > 0; off >>= 1) {
-    if (tid < off && better_key(skey[tid + off], sidx[tid + off], skey[tid], sidx[tid])) {
-      skey[tid] = skey[tid + off];
-      sidx[tid] = sidx[tid + off];
+// Block-wide argmax of (key, index): larger key, then lower index.  The order is total, so
+// the result does not depend on the reduction order.  Uniform result; one barrier.
+__device__ __forceinline__ void block_argmax(double& key, int& idx, double* wkey, int* widx) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const double ok = __shfl_xor(key, off);
+    const int oi = __shfl_xor(idx, off);
+    if (better_key(ok, oi, key, idx)) {
+      key = ok;
+      idx = oi;
     }
-    __syncthreads();
   }
-  key = skey[0];
-  idx = sidx[0];
+  const int wave = threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    wkey[wave] = key;
+    widx[wave] = idx;
+  }
   __syncthreads();
+  key = wkey[0];
+  idx = widx[0];
+#pragma unroll
+  for (int w = 1; w < kFinishWaves; ++w)
+    if (better_key(wkey[w], widx[w], key, idx)) {
+      key = wkey[w];
+      idx = widx[w];
+    }
 }
 
+// One block per row.  Every load the row needs before its level-2 draw is issued at entry:
+// the V-split states (merged by one lane in split order) and the chunk log-masses with their
+// level-1 noise.  Level 2 then re-reads the winning chunk only.
 __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     const float* __restrict__ logits, int V, int nC, int S, float temperature, uint32_t k0,
     uint32_t k1, uint32_t step, const uint8_t* __restrict__ frozen,
@@ -270,12 +308,31 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     }
     return;
   }
+  __shared__ PartState sp[kMaxSplits];
+  __shared__ double wkey[2][kFinishWaves];
+  __shared__ int widx[2][kFinishWaves];
   __shared__ int sValid, sArg;
-  __shared__ double skey[kFinishThreads];
-  __shared__ int sidx[kFinishThreads];
+  for (int s = tid; s < S; s += kFinishThreads) sp[s] = part[(size_t)p * S + s];
+  const bool sampled = temperature != 0.f;
+  // Level 1: chunk keys K_c = L_c + G_c, G_c from counter (c, p, step, 1) word 0.
+  double best = -INFINITY;
+  int bestc = 0x7fffffff;
+  if (sampled) {
+    for (int c = tid; c < nC; c += kFinishThreads) {
+      const float L = lmass[(size_t)p * nC + c];
+      if (L == -INFINITY) continue;
+      const Philox4 r = philox4x32_10((uint32_t)c, (uint32_t)p, step, 1u, k0, k1);
+      const double key = (double)L + gumbel_from_word(r.w[0]);
+      if (better_key(key, c, best, bestc)) {
+        best = key;
+        bestc = c;
+      }
+    }
+  }
+  __syncthreads();
   if (tid == 0) {
-    PartState acc = part[(size_t)p * S];
-    for (int s = 1; s < S; ++s) merge_state(acc, part[(size_t)p * S + s]);
+    PartState acc = sp[0];
+    for (int s = 1; s < S; ++s) merge_state(acc, sp[s]);
     float H = NAN, conf = NAN;
     bool valid = !acc.nan && acc.m != -INFINITY;
     if (valid) {
@@ -289,44 +346,29 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     sArg = acc.best_i;
     if (entropy_out != nullptr) entropy_out[p] = valid ? H : NAN;
     if (conf_out != nullptr) conf_out[p] = valid ? conf : NAN;
+    if (!valid) tokens_out[p] = -1;
+    else if (!sampled) tokens_out[p] = acc.best_i;
   }
-  __syncthreads();
-  if (!sValid) {
-    if (tid == 0) tokens_out[p] = -1;
-    return;
-  }
-  if (temperature == 0.f) {
-    if (tid == 0) tokens_out[p] = sArg;
-    return;
-  }
-  // Level 1: chunk keys K_c = L_c + G_c, G_c from counter (c, p, step, 1) word 0.
-  double best = -INFINITY;
-  int bestc = 0x7fffffff;
-  for (int c = tid; c < nC; c += kFinishThreads) {
-    const float L = lmass[(size_t)p * nC + c];
-    if (L == -INFINITY) continue;
-    const Philox4 r = philox4x32_10((uint32_t)c, (uint32_t)p, step, 1u, k0, k1);
-    const double key = (double)L + gumbel_from_word(r.w[0]);
-    if (better_key(key, c, best, bestc)) {
-      best = key;
-      bestc = c;
-    }
-  }
-  block_argmax(best, bestc, skey, sidx);
+  if (!sampled) return;
+  block_argmax(best, bestc, wkey[0], widx[0]);  // its barrier also publishes sValid
+  if (!sValid) return;
   // Level 2: inside chunk bestc, maximise x_v / T + g_v, g_v from (v >> 2, p, step, 0).
   const int v0 = bestc * kChunk + 4 * tid;
   const int vend = min(V, (bestc + 1) * kChunk);
   double sbest = -INFINITY;
   int sv = 0x7fffffff;
   if (v0 < vend) {
-    const Philox4 r = philox4x32_10((uint32_t)(v0 >> 2), (uint32_t)p, step, 0u, k0, k1);
     const float* row = logits + (size_t)p * V;
+    float xv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[q] = v0 + q < vend ? row[v0 + q] : -INFINITY;
+    const Philox4 r = philox4x32_10((uint32_t)(v0 >> 2), (uint32_t)p, step, 0u, k0, k1);
     const double T = (double)temperature;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int v = v0 + q;
       if (v < vend) {
-        const double sc = (double)row[v] / T + gumbel_from_word(r.w[q]);
+        const double sc = (double)xv[q] / T + gumbel_from_word(r.w[q]);
         if (better_key(sc, v, sbest, sv)) {
           sbest = sc;
           sv = v;
@@ -334,7 +376,7 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
       }
     }
   }
-  block_argmax(sbest, sv, skey, sidx);
+  block_argmax(sbest, sv, wkey[1], widx[1]);
   if (tid == 0) tokens_out[p] = sv;
 }
 
@@ -360,37 +402,36 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     int32_t* __restrict__ num_accepted) {
   __shared__ uint64_t keys[kAcceptThreads];
   __shared__ int sCount;
+  // The block has n threads, n the smallest power of two >= max(P, 64); thread i holds key i.
   const int tid = threadIdx.x;
-  int n = 1;
-  while (n < P) n <<= 1;
-  if (tid < n) {
-    uint64_t key = ~0ull;  // non-candidates sort last
-    if (tid < P) {
-      const float h = entropy[tid];
-      const bool is_frozen = frozen != nullptr && frozen[tid];
-      if (!is_frozen && !(h != h)) key = ((uint64_t)float_order_key(h) << 32) | (uint32_t)tid;
-      accept_out[tid] = 0;
-    }
-    keys[tid] = key;
+  const int n = blockDim.x;
+  unsigned long long key = ~0ull;  // non-candidates sort last
+  if (tid < P) {
+    const float h = entropy[tid];
+    const bool is_frozen = frozen != nullptr && frozen[tid];
+    if (!is_frozen && !(h != h)) key = ((uint64_t)float_order_key(h) << 32) | (uint32_t)tid;
+    accept_out[tid] = 0;
   }
-  __syncthreads();
-  // Bitonic sort, ascending, of n keys (n a power of two, n <= 1024).
+  // Bitonic sort, ascending, of the n keys held one per thread.  Exchanges with a partner in
+  // the same wave (j < 64) go through cross-lane shuffles; wider ones through LDS.
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      if (tid < n) {
-        const int partner = tid ^ j;
-        if (partner > tid) {
-          const uint64_t a = keys[tid], b = keys[partner];
-          const bool up = (tid & k) == 0;
-          if ((a > b) == up) {
-            keys[tid] = b;
-            keys[partner] = a;
-          }
-        }
+      unsigned long long other;
+      if (j < kWave) {
+        other = __shfl_xor(key, j);
+      } else {
+        keys[tid] = key;
+        __syncthreads();
+        other = keys[tid ^ j];
+        __syncthreads();
       }
-      __syncthreads();
+      const bool up = (tid & k) == 0;
+      const bool lower = (tid & j) == 0;  // this thread holds the lower index of the pair
+      key = (lower == up) ? (key < other ? key : other) : (key < other ? other : key);
     }
   }
+  keys[tid] = key;
+  __syncthreads();
   // One lane: the sequential fp32 scan in sorted order.
   if (tid == 0) {
     float S = 0.f;
@@ -486,7 +527,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_conf_kernel(
 
 int sample_split_count(int P, int V) {
   const int nC = (V + kChunk - 1) / kChunk;
-  int S = (2048 + P - 1) / P;
+  int S = (BD_SAMPLE_BLOCKS + P - 1) / P;
   S = min(S, nC / 8);
   return S < 1 ? 1 : S;
 }
@@ -528,8 +569,10 @@ size_t sample_workspace_bytes(int P, int V) {
 hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, float bound,
                          uint8_t* frozen, int32_t* canvas, uint8_t* accept_out,
                          int32_t* num_accepted, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kAcceptThreads), 0, stream, entropy, tokens, P,
-                     bound, frozen, canvas, accept_out, num_accepted);
+  int n = kWave;
+  while (n < P) n <<= 1;
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(n), 0, stream, entropy, tokens, P, bound, frozen,
+                     canvas, accept_out, num_accepted);
   return hipGetLastError();
 }
 
