@@ -74,6 +74,8 @@ SEED_PERM = 3
 SEED_TINY_LOGITS = 4
 SEED_LOGITS = 5
 SEED_WEIGHTS = 100
+SEED_HIDDEN = 6
+SEED_NORM_ROUTER = 200
 
 
 def _rng(seed):
@@ -136,6 +138,21 @@ def make_router_logits(shape: LayerShape, layer: int = 0):
 def make_layer(shape: LayerShape, layer: int = 0):
     """(x, router_logits, weights) of one layer."""
     return make_activations(shape), make_router_logits(shape, layer), make_weights(shape, layer)
+
+
+def make_norm_router(shape: LayerShape, layer: int = 0):
+    """Inputs of the RMS norm and router projection of one layer.
+
+    hidden h ~ 3 N(0, 1) fp16 [T, d] (seed 6); norm weight 1 + 0.1 N(0, 1) fp16 [d] and router
+    matrix N(0, 1) / sqrt(d) fp16 [E, d] (seed 200 + layer), so that the logits of a normed
+    row are about N(0, 1), as the router logits of the other workloads.
+    """
+    T, d, E = shape.tokens, shape.d_model, shape.experts
+    h = (3.0 * _rng(SEED_HIDDEN).standard_normal((T, d), dtype=np.float32)).astype(np.float16)
+    rng = _rng(SEED_NORM_ROUTER + layer)
+    w_norm = (1.0 + 0.1 * rng.standard_normal(d, dtype=np.float32)).astype(np.float16)
+    w_router = (rng.standard_normal((E, d), dtype=np.float32) / np.float32(np.sqrt(d))).astype(np.float16)
+    return h, w_norm, w_router
 
 
 def make_logits(shape: SamplerShape, seed: int = None):

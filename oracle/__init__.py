@@ -19,12 +19,13 @@ Modules
 -------
 philox   Philox4x32-10 counter-based generator (Salmon et al., SC'11).
 moe      uint4 dequantisation, top-k routing, GeGLU expert FFN, fixed-order combine.
-sampler  per-position entropy, temperature-0 argmax, two-level gumbel-max token,
-         entropy-bound acceptance.
+layer    the RMS norm before the FFN and the router projection that feeds the top-k.
+sampler  per-position entropy and top-1 probability, temperature-0 argmax, two-level
+         gumbel-max token, entropy-bound and confidence-threshold acceptance.
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against closed forms,
 brute force, library routines or published known-answer values.  None is
 "parity unpinned".
 """
 
-from . import philox, moe, sampler  # noqa: F401
+from . import philox, moe, layer, sampler  # noqa: F401
