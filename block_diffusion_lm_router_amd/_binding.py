@@ -60,6 +60,8 @@ SIGNATURES = {
     "moe_w4a16_down": (_I, [_W, _I, _P, _P, _SZ, _P]),
     "moe_w4a16_ffn": (_I, [_W, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine_fixed_order": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "moe_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P, _P]),
+    "moe_router_logits": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "bd_sample_workspace_size": (_SZ, [_I, _I]),
     "diffusion_sample_entropy": (_I, [_P, _I, _I, _F, _U64, _U32, _P, _P, _P, _P, _SZ, _P]),
     "diffusion_accept_entropy_bound": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
@@ -256,6 +258,24 @@ def moe_combine_fixed_order(expert_out, topk_weights, y):
     return _invoke("moe_combine_fixed_order", _ptr(expert_out, torch.float32, "expert_out"),
                    _ptr(topk_weights, torch.float32, "topk_weights"), T, k, d,
                    _ptr(y, torch.float16, "y"), _stream())
+
+
+def moe_rmsnorm(h, weight, y, eps=1e-6):
+    T, d = h.shape
+    if weight.numel() != d or tuple(y.shape) != (T, d):
+        raise ValueError("moe_rmsnorm: weight must be [d] and y [T, d]")
+    return _invoke("moe_rmsnorm", _ptr(h, torch.float16, "h"), _ptr(weight, torch.float16, "weight"),
+                   T, d, float(eps), _ptr(y, torch.float16, "y"), _stream())
+
+
+def moe_router_logits(x, w_router, logits):
+    T, d = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != d or tuple(logits.shape) != (T, E):
+        raise ValueError("moe_router_logits: w_router must be [E, d] and logits [T, E]")
+    return _invoke("moe_router_logits", _ptr(x, torch.float16, "x"),
+                   _ptr(w_router, torch.float16, "w_router"), T, d, E,
+                   _ptr(logits, torch.float32, "logits"), _stream())
 
 
 def sample_workspace_size(P, V):

@@ -197,6 +197,26 @@ int moe_combine_fixed_order(const float* expert_out, const float* topk_weights, 
   return to_status(bd::launch_combine(expert_out, topk_weights, T, k, d, y, as_stream(stream)));
 }
 
+int moe_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps, uint16_t* y,
+                void* stream) {
+  if (T < 1 || T > BD_MAX_TOKENS || d < 8 || d > BD_MAX_FEATURES || d % 8 != 0 ||
+      !isfinite(eps) || eps < 0.f)
+    return BD_ERR_SHAPE;
+  if (!h || !weight || !y) return BD_ERR_NULL;
+  if (!aligned16(h) || !aligned16(weight) || !aligned16(y)) return BD_ERR_ALIGN;
+  return to_status(bd::launch_rmsnorm(h, weight, T, d, eps, y, as_stream(stream)));
+}
+
+int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                      float* logits, void* stream) {
+  if (T < 1 || T > BD_MAX_TOKENS || E < 1 || E > BD_MAX_EXPERTS || d < 128 ||
+      d > BD_MAX_FEATURES || d % 128 != 0)
+    return BD_ERR_SHAPE;
+  if (!x || !w_router || !logits) return BD_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(logits)) return BD_ERR_ALIGN;
+  return to_status(bd::launch_router(x, w_router, T, d, E, logits, as_stream(stream)));
+}
+
 size_t bd_sample_workspace_size(int P, int V) {
   if (check_sample_shape(P, V, 0.f) != BD_OK) return 0;
   return bd::sample_workspace_bytes(P, V);

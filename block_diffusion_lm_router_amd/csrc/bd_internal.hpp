@@ -68,6 +68,12 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
 hipError_t launch_combine(const float* expert_out, const float* topk_weights, int T, int k, int d,
                           uint16_t* y, hipStream_t stream);
 
+// RMS norm of fp16 rows (one wave per row) and the router projection (MFMA, split-K).
+hipError_t launch_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps,
+                          uint16_t* y, hipStream_t stream);
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                         float* logits, hipStream_t stream);
+
 // ---------------------------------------------------------------- sampler
 int sample_split_count(int P, int V);
 size_t sample_workspace_bytes(int P, int V);

@@ -1,0 +1,145 @@
+// The two steps either side of the expert FFN's routing: the fused RMS norm that produces the
+// FFN input, and the router projection whose fp32 logits feed the top-k.
+//
+// Sources: axe-diffusion-ksl-xe model card, "the kernels we built" (the RMS norm as one
+// launch instead of about six elementwise ones, 180 times per forward pass); "what the model
+// is" (128 experts scored per token, top-8 kept).
+//
+// RMS norm.  One wave per row, four rows per 256-thread block.  A row of d <= 4096 halves is
+// at most eight 16-byte vectors per lane: the wave loads the row once into registers, sums
+// the squares in fp32 (each square of an fp16 value is exact in fp32; lanes sum in element
+// order, then one fixed-order wave reduction), loading its share of w alongside, and writes
+//     y = fp16_rne(x * (1 / sqrt(sum / d + eps)) * w)
+// from the same registers.  HBM traffic is the row in and the row out, plus w from L2.
+//
+// Router projection.  logits[t][e] = sum_k x[t][k] W_r[e][k] on v_mfma_f32_16x16x32_f16:
+// fp16 products are exact and accumulate in fp32.  A block owns one 16-token x 16-expert tile
+// and its four waves split the contraction dim into quarters; the quarters' 16 x 16 sums meet
+// in LDS and are added in wave order, so the result is reproducible.  Each lane streams its
+// 16-byte fragments of x and W_r straight from memory (both stay in L2: 1.4 MB and 0.7 MB at
+// the layer's shape).  Fragment layout as in the expert GEMMs: lane (m, kb) = (lane % 16,
+// lane / 16) supplies row m at k-slots 8kb..8kb+7 of A (tokens) and of B (experts), and
+// receives D for tokens 4kb..4kb+3 of expert m.
+
+#include "bd_device.hpp"
+#include "bd_internal.hpp"
+
+namespace bd {
+
+namespace {
+
+constexpr int kNormThreads = 256;
+constexpr int kNormRows = kNormThreads / kWave;
+constexpr int kNormMaxVec = 8;  // 8 vectors x 8 halves x 64 lanes = 4096 features
+
+__device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
+__device__ __forceinline__ u32x4_t as_u32x4(half8_t v) { return __builtin_bit_cast(u32x4_t, v); }
+
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w, int T, int d, float eps,
+    uint16_t* __restrict__ y) {
+  const int row = blockIdx.x * kNormRows + (int)(threadIdx.x / kWave);
+  if (row >= T) return;  // wave-uniform
+  const int lane = lane_id();
+  const int nv = d / 8;
+  const u32x4_t* __restrict__ src = reinterpret_cast<const u32x4_t*>(h + (size_t)row * d);
+  const u32x4_t* __restrict__ wv = reinterpret_cast<const u32x4_t*>(w);
+  u32x4_t v[kNormMaxVec], g[kNormMaxVec];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormMaxVec; ++i) {
+    const int j = lane + i * kWave;
+    if (j < nv) {
+      v[i] = __builtin_nontemporal_load(src + j);
+      g[i] = wv[j];
+      const half8_t x = as_half8(v[i]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float f = (float)x[q];
+        ss = fmaf(f, f, ss);
+      }
+    }
+  }
+  const float total = wave_sum(ss);
+  const float r = 1.f / sqrtf(total / (float)d + eps);
+  u32x4_t* __restrict__ dst = reinterpret_cast<u32x4_t*>(y + (size_t)row * d);
+#pragma unroll
+  for (int i = 0; i < kNormMaxVec; ++i) {
+    const int j = lane + i * kWave;
+    if (j < nv) {
+      const half8_t x = as_half8(v[i]);
+      const half8_t gw = as_half8(g[i]);
+      half8_t o;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = (_Float16)(((float)x[q] * r) * (float)gw[q]);
+      dst[j] = as_u32x4(o);
+    }
+  }
+}
+
+constexpr int kRouterThreads = 256;
+constexpr int kRouterWaves = kRouterThreads / kWave;  // contraction quarters
+
+__global__ __launch_bounds__(kRouterThreads) void router_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int E, int d,
+    float* __restrict__ logits) {
+  __shared__ float4_t part[kRouterWaves][kWave];
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int m = lane & 15;
+  const int kb = lane >> 4;
+  const int t0 = blockIdx.x * 16;
+  const int e0 = blockIdx.y * 16;
+  // Rows past the ends are clamped onto the last row: their sums are computed and dropped.
+  const int t = min(t0 + m, T - 1);
+  const int e = min(e0 + m, E - 1);
+  const int kq = d / kRouterWaves;
+  const int steps = kq / 32;
+  const half8_t* __restrict__ xa =
+      reinterpret_cast<const half8_t*>(x + (size_t)t * d + wave * kq + kb * 8);
+  const half8_t* __restrict__ wb =
+      reinterpret_cast<const half8_t*>(wr + (size_t)e * d + wave * kq + kb * 8);
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = 0; s < steps; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s * 4], wb[s * 4], acc, 0, 0, 0);
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  float4_t sum = part[0][lane];
+#pragma unroll
+  for (int q = 1; q < kRouterWaves; ++q) {
+    const float4_t p = part[q][lane];
+    sum[0] += p[0];
+    sum[1] += p[1];
+    sum[2] += p[2];
+    sum[3] += p[3];
+  }
+  const int ee = e0 + m;
+  if (ee >= E) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tt = t0 + 4 * kb + i;
+    if (tt < T) logits[(size_t)tt * E + ee] = sum[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps,
+                          uint16_t* y, hipStream_t stream) {
+  const int blocks = (T + kNormRows - 1) / kNormRows;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(blocks), dim3(kNormThreads), 0, stream, h, weight, T,
+                     d, eps, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                         float* logits, hipStream_t stream) {
+  const dim3 grid((T + 15) / 16, (E + 15) / 16);
+  hipLaunchKernelGGL(router_kernel, grid, dim3(kRouterThreads), 0, stream, x, w_router, T, E, d,
+                     logits);
+  return hipGetLastError();
+}
+
+}  // namespace bd

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 4
+#define BD_ABI_VERSION 5
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -52,6 +52,7 @@ extern "C" {
 #define BD_MAX_TOKENS 65536
 #define BD_MAX_POSITIONS 1024
 #define BD_MAX_VOCAB (1 << 24)
+#define BD_MAX_FEATURES 4096
 
 typedef enum {
   BD_OK = 0,
@@ -217,6 +218,36 @@ int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x,
  */
 int moe_combine_fixed_order(const float* expert_out, const float* topk_weights,
                             int T, int k, int d, uint16_t* y, void* stream);
+
+/* ------------------------------------------------------------------ layer neighbours */
+
+/*
+ * Fused RMS norm of fp16 rows, one launch:
+ *   y[t][i] = fp16_rne( h[t][i] / sqrt(mean_i(h[t][i]^2) + eps) * weight[i] )
+ * evaluated in fp32 (squares exact, fixed summation order).  The FFN input of a layer.
+ * Source: axe-diffusion-ksl-xe model card, "the kernels we built" (RMS norm as one launch
+ * instead of about six elementwise ones).  No bias, no mean subtraction, weight as stored.
+ *
+ *   h       fp16 [T][d], 16-byte aligned        weight  fp16 [d], 16-byte aligned
+ *   y       fp16 [T][d] out, 16-byte aligned (may not overlap h)
+ *   T in 1..BD_MAX_TOKENS; d in 8..BD_MAX_FEATURES with d % 8 == 0; eps finite, >= 0.
+ */
+int moe_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps, uint16_t* y,
+                void* stream);
+
+/*
+ * Router projection: logits[t][e] = sum_i x[t][i] * w_router[e][i], fp16 operands (exact
+ * products), fp32 accumulation (MFMA), fp32 out; the input of moe_route_topk.
+ * Source: axe-diffusion-ksl-xe model card, "what the model is" (every token scores the 128
+ * experts and keeps the top 8).
+ *
+ *   x         fp16 [T][d], 16-byte aligned (e.g. the output of moe_rmsnorm)
+ *   w_router  fp16 [E][d], expert-major, 16-byte aligned
+ *   logits    fp32 [T][E] out
+ *   T in 1..BD_MAX_TOKENS; E in 1..BD_MAX_EXPERTS; d in 128..BD_MAX_FEATURES, d % 128 == 0.
+ */
+int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                      float* logits, void* stream);
 
 /* ------------------------------------------------------------------ sampler */
 

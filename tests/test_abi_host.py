@@ -155,6 +155,25 @@ def test_confidence_sampler_validation(lib):
     assert step(P, 8, 100, 1.0, 0.9, 0, 0, None, None, P, None, P, P, P, 1 << 20, None) == 1
 
 
+def test_norm_router_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    norm = lib.moe_rmsnorm
+    assert norm(P, P, 0, 2816, 1e-6, P, None) == 2
+    assert norm(P, P, 4, 2820, 1e-6, P, None) == 2
+    assert norm(P, P, 4, 4104, 1e-6, P, None) == 2
+    assert norm(P, P, 4, 2816, -1.0, P, None) == 2
+    assert norm(P, P, 4, 2816, float("nan"), P, None) == 2
+    assert norm(None, P, 4, 2816, 1e-6, P, None) == 1
+    assert norm(P, ctypes.c_void_p(0x1008), 4, 2816, 1e-6, P, None) == 3
+    rt = lib.moe_router_logits
+    assert rt(P, P, 4, 2880, 128, P, None) == 2
+    assert rt(P, P, 4, 2816, 0, P, None) == 2
+    assert rt(P, P, 4, 2816, 257, P, None) == 2
+    assert rt(P, P, 65537, 2816, 128, P, None) == 2
+    assert rt(P, None, 4, 2816, 128, P, None) == 1
+    assert rt(ctypes.c_void_p(0x1002), P, 4, 2816, 128, P, None) == 3
+
+
 def test_prepare_sizes_and_validation(lib):
     w = _weights()
     ref = ctypes.byref(w)
