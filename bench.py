@@ -95,6 +95,90 @@ def cpu_baseline(shape, layer_inputs, logits, sampler_shape):
     }
 
 
+def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=20):
+    """Live per-launch timings of the path's parts beside the step: each call bracketed by its
+    own pair of events on the launch stream, inputs alternating between two copies (or two
+    layers) so the 256 MB last-level cache cannot serve a repeat; median over n calls.
+
+    * ffn_layer_uniform: one whole FFN layer (route, gate/up, down, combine) at the 256-token
+      canvas with uniform N(0, 1) router logits (every expert touched);
+    * sampler_entropy_bound / sampler_confidence: one sampler step over all rows unfrozen;
+    * rmsnorm / router: the layer neighbours at the same shape.
+    """
+    import torch
+    from block_diffusion_lm_router_amd import _binding  # noqa: F401
+    stream = torch.cuda.current_stream()
+    shape = workloads.LAYER
+    T, d, f, E, k = shape.tokens, shape.d_model, shape.d_ff, shape.experts, shape.top_k
+    gu_b, dn_b = workloads.expert_bytes(shape)
+    P, V = logits.shape
+    out = {}
+
+    def timed(name, fns, alg_bytes, pre=None):
+        evs = []
+        for i in range(n + 3):
+            if pre is not None:
+                pre()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fns[i % len(fns)]()
+            b.record(stream)
+            if i >= 3:
+                evs.append((a, b))
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+        gbs = alg_bytes / (us * 1e-6) / 1e9
+        out[name] = {"us_p50": round(us, 2), "alg_bytes": int(alg_bytes), "GB/s": round(gbs, 1),
+                     "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    router = torch.from_numpy(workloads.make_router_logits(shape)).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    o = torch.empty((T, k, d), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    bd.moe_route_topk(layers[0][0], router, ids, tw, ws)
+    touched = int(torch.unique(ids).numel())
+
+    def layer_fn(w):
+        launches = (bd.bind(bd.moe_route_topk, w, router, ids, tw, ws),
+                    bd.bind(bd.moe_w4a16_gate_up, w, x, ws),
+                    bd.bind(bd.moe_w4a16_down, w, T, o, ws),
+                    bd.bind(bd.moe_combine_fixed_order, o, tw, y))
+        return lambda: [fn() for fn in launches]
+
+    timed("ffn_layer_uniform", [layer_fn(layers[0][0]), layer_fn(layers[1 % len(layers)][0])],
+          touched * (gu_b + dn_b) + 2 * T * d * 2 + T * E * 4 + 2 * T * k * 4)
+    out["ffn_layer_uniform"]["experts_touched"] = touched
+
+    logits2 = logits.clone()
+    frozen = torch.zeros(P, dtype=torch.uint8, device="cuda")
+    canvas = torch.zeros(P, dtype=torch.int32, device="cuda")
+    tok = torch.empty(P, dtype=torch.int32, device="cuda")
+    H = torch.empty(P, dtype=torch.float32, device="cuda")
+    acc = torch.empty(P, dtype=torch.uint8, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    samp_bytes = P * V * 4 + P * (4 + 4 + 1 + 1 + 4)
+    timed("sampler_entropy_bound",
+          [bd.bind(bd.diffusion_sample_step, lg, sshape.temperature, sshape.bound, sshape.seed, 0,
+                   frozen, canvas, tok, H, acc, cnt, sws) for lg in (logits, logits2)],
+          samp_bytes, pre=frozen.zero_)
+    timed("sampler_confidence",
+          [bd.bind(bd.diffusion_sample_step_confidence, lg, sshape.temperature, 0.9, sshape.seed,
+                   0, frozen, canvas, tok, H, acc, cnt, sws) for lg in (logits, logits2)],
+          samp_bytes, pre=frozen.zero_)
+    del logits2
+
+    h_np, wn_np, wr_np = workloads.make_norm_router(shape)
+    hs = [torch.from_numpy(h_np).cuda() for _ in range(2)]
+    wn = torch.from_numpy(wn_np).cuda()
+    wr = torch.from_numpy(wr_np).cuda()
+    xn = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    rl = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    timed("rmsnorm", [bd.bind(bd.moe_rmsnorm, hh, wn, xn) for hh in hs], 2 * T * d * 2 + d * 2)
+    timed("router", [bd.bind(bd.moe_router_logits, xn, wr, rl)], T * d * 2 + E * d * 2 + T * E * 4)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -224,6 +308,8 @@ def main():
                       dtype=np.float64)
     gu_gbs = gu_alg.sum() / (gu_ms.sum() * 1e-3) / 1e9
     traffic = measured_traffic(float(gu_alg.mean()))
+    log("timing the parts one launch at a time")
+    parts = components(bd, workloads, layers, x, logits, sshape, ws, sws)
 
     result = {
         "metric": "denoising-step MoE+sampler latency (ms) and achieved HBM GB/s vs peak, 1 GPU",
@@ -246,6 +332,7 @@ def main():
             "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
             "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
             "step_algorithmic_bytes": int(step_bytes),
+            "components": parts,
         },
         "roofline": {
             "kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22>)",
