@@ -20,6 +20,7 @@ Modules
 philox   Philox4x32-10 counter-based generator (Salmon et al., SC'11).
 moe      uint4 dequantisation, top-k routing, GeGLU expert FFN, fixed-order combine.
 layer    the RMS norm before the FFN and the router projection that feeds the top-k.
+loop     the denoising-loop driver: canvas length, random initial canvas, stability update.
 sampler  per-position entropy and top-1 probability, temperature-0 argmax, two-level
          gumbel-max token, entropy-bound and confidence-threshold acceptance.
 
@@ -28,4 +29,4 @@ brute force, library routines or published known-answer values.  None is
 "parity unpinned".
 """
 
-from . import philox, moe, layer, sampler  # noqa: F401
+from . import philox, moe, layer, loop, sampler  # noqa: F401
