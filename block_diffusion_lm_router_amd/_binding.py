@@ -72,6 +72,9 @@ SIGNATURES = {
     "diffusion_accept_confidence": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
     "diffusion_sample_step_confidence": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P,
                                               _P, _P, _SZ, _P]),
+    "bd_canvas_length": (_I, [_I, _I, _I, _I]),
+    "diffusion_canvas_init": (_I, [_P, _P, _P, _P, _I, _I, _U64, _U32, _P]),
+    "diffusion_loop_update": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "bd_hbm_copy": (_I, [_P, _P, _SZ, _P]),
     "bd_hbm_read": (_I, [_P, _SZ, _P, _P]),
 }
@@ -355,6 +358,35 @@ def diffusion_sample_step_confidence(logits, temperature, threshold, seed, step,
                    _ptr(accept_out, torch.uint8, "accept_out"),
                    _ptr(num_accepted, torch.int32, "num_accepted"),
                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+
+
+def canvas_length(max_canvas, min_canvas, remaining, full_canvas=False):
+    n = load().bd_canvas_length(int(max_canvas), int(min_canvas), int(remaining),
+                                1 if full_canvas else 0)
+    if n == 0:
+        raise BdError("bd_canvas_length: invalid arguments")
+    return n
+
+
+def diffusion_canvas_init(canvas, prev_canvas, frozen, loop_state, vocab, seed, block):
+    P = canvas.shape[0]
+    if loop_state.numel() < 4:
+        raise ValueError("loop_state needs 4 int32 elements")
+    return _invoke("diffusion_canvas_init", _ptr(canvas, torch.int32, "canvas"),
+                   _ptr(prev_canvas, torch.int32, "prev_canvas"), _ptr(frozen, torch.uint8, "frozen"),
+                   _ptr(loop_state, torch.int32, "loop_state"), P, int(vocab), int(seed), int(block),
+                   _stream())
+
+
+def diffusion_loop_update(tokens, canvas, prev_canvas, frozen, loop_state, stability_threshold,
+                          max_steps, write_drafts=True):
+    P = canvas.shape[0]
+    if loop_state.numel() < 4:
+        raise ValueError("loop_state needs 4 int32 elements")
+    return _invoke("diffusion_loop_update", _ptr(tokens, torch.int32, "tokens"),
+                   _ptr(canvas, torch.int32, "canvas"), _ptr(prev_canvas, torch.int32, "prev_canvas"),
+                   _ptr(frozen, torch.uint8, "frozen"), _ptr(loop_state, torch.int32, "loop_state"),
+                   P, int(stability_threshold), int(max_steps), 1 if write_drafts else 0, _stream())
 
 
 def hbm_copy(src, dst):

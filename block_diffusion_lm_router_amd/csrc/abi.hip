@@ -328,6 +328,39 @@ int diffusion_sample_step_confidence(const float* logits, int P, int V, float te
   return to_status(err);
 }
 
+int bd_canvas_length(int max_canvas, int min_canvas, int remaining, int full_canvas) {
+  if (max_canvas < 1 || min_canvas < 1 || remaining < 0) return 0;
+  if (full_canvas) return max_canvas;
+  const int want = remaining > min_canvas ? remaining : min_canvas;
+  return want < max_canvas ? want : max_canvas;
+}
+
+int diffusion_canvas_init(int32_t* canvas, int32_t* prev_canvas, uint8_t* frozen,
+                          int32_t* loop_state, int P, int vocab, uint64_t seed, uint32_t block,
+                          void* stream) {
+  if (P < 1 || P > BD_MAX_POSITIONS || vocab < 1 || vocab > BD_MAX_VOCAB) return BD_ERR_SHAPE;
+  if (!canvas || !prev_canvas || !frozen || !loop_state) return BD_ERR_NULL;
+  if (!aligned4(canvas) || !aligned4(prev_canvas) || !aligned4(loop_state)) return BD_ERR_ALIGN;
+  return to_status(bd::launch_canvas_init(canvas, prev_canvas, frozen, loop_state, P, vocab, seed,
+                                          block, as_stream(stream)));
+}
+
+int diffusion_loop_update(const int32_t* tokens, int32_t* canvas, int32_t* prev_canvas,
+                          const uint8_t* frozen, int32_t* loop_state, int P,
+                          int stability_threshold, int max_steps, int write_drafts,
+                          void* stream) {
+  if (P < 1 || P > BD_MAX_POSITIONS || stability_threshold < 1 || max_steps < 1)
+    return BD_ERR_SHAPE;
+  if (!canvas || !prev_canvas || !frozen || !loop_state || (write_drafts && !tokens))
+    return BD_ERR_NULL;
+  if ((tokens && !aligned4(tokens)) || !aligned4(canvas) || !aligned4(prev_canvas) ||
+      !aligned4(loop_state))
+    return BD_ERR_ALIGN;
+  return to_status(bd::launch_loop_update(tokens, canvas, prev_canvas, frozen, loop_state, P,
+                                          stability_threshold, max_steps, write_drafts ? 1 : 0,
+                                          as_stream(stream)));
+}
+
 int bd_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (!src || !dst) return BD_ERR_NULL;
   if (bytes % 16 != 0) return BD_ERR_SHAPE;

@@ -89,6 +89,14 @@ hipError_t launch_accept_confidence(const float* conf, const int32_t* tokens, in
                                     uint8_t* accept_out, int32_t* num_accepted,
                                     hipStream_t stream);
 
+// ---------------------------------------------------------------- denoising-loop driver
+hipError_t launch_canvas_init(int32_t* canvas, int32_t* prev, uint8_t* frozen, int32_t* state,
+                              int P, int vocab, uint64_t seed, uint32_t block,
+                              hipStream_t stream);
+hipError_t launch_loop_update(const int32_t* tokens, int32_t* canvas, int32_t* prev,
+                              const uint8_t* frozen, int32_t* state, int P, int threshold,
+                              int max_steps, int write_drafts, hipStream_t stream);
+
 // ---------------------------------------------------------------- measurement
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_read(const void* src, size_t bytes, uint32_t* checksum, hipStream_t stream);

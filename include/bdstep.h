@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 5
+#define BD_ABI_VERSION 6
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -359,6 +359,50 @@ int diffusion_sample_step_confidence(const float* logits, int P, int V, float te
                                      float* confidence_out, uint8_t* accept_out,
                                      int32_t* num_accepted, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ denoising-loop driver */
+
+/*
+ * Canvas length of the next block (host only, no device work):
+ *   full_canvas ? max_canvas : min(max_canvas, max(remaining, min_canvas)).
+ * Returns 0 if max_canvas < 1, min_canvas < 1 or remaining < 0.
+ * Source: DiffusionGemma block-diffusion page, "How it works" (length rule) and "CLI flags"
+ * (minimum 64, maximum the model's canvas length, the full-canvas option).
+ */
+int bd_canvas_length(int max_canvas, int min_canvas, int remaining, int full_canvas);
+
+/*
+ * Start of a block: canvas[p] = prev_canvas[p] = floor(w_p * vocab / 2^32) with w_p word 0 of
+ * Philox4x32-10 (key = seed low word, high word) at counter (p, block, 0, 2); frozen[p] = 0;
+ * loop_state[0..3] = 0.  loop_state is int32 [4]: steps run, consecutive unchanged steps,
+ * done flag, frozen count.
+ * Source: DiffusionGemma block-diffusion page, "How it works" (canvas of uniformly random
+ * token ids) and "Reproducibility" (the seed fixes the initial canvas).
+ *   P in 1..BD_MAX_POSITIONS; vocab in 1..BD_MAX_VOCAB; all pointers device memory.
+ */
+int diffusion_canvas_init(int32_t* canvas, int32_t* prev_canvas, uint8_t* frozen,
+                          int32_t* loop_state, int P, int vocab, uint64_t seed, uint32_t block,
+                          void* stream);
+
+/*
+ * The driver's update after one step's sampler call (one workgroup).  Unless loop_state
+ * says the block is done (then nothing changes): if write_drafts, every position the step
+ * sampled (tokens[p] >= 0) takes its draft, canvas[p] = tokens[p] (frozen positions keep
+ * their token, tokens = -1 there); the canvas is compared with prev_canvas, which then
+ * takes the canvas; steps += 1; the unchanged count is reset on any change, else
+ * incremented; done = unchanged >= stability_threshold, or every position frozen, or
+ * steps >= max_steps.
+ * Source: DiffusionGemma block-diffusion page, "How it works" (the model refines the whole
+ * block each step; the stable-and-confident early stop after stability_threshold unchanged
+ * steps; the step budget).
+ *   tokens  int32 [P] (may be NULL if write_drafts == 0); canvas, prev_canvas int32 [P];
+ *   frozen  uint8 [P] (after the step's acceptance); loop_state int32 [4] in/out.
+ *   P in 1..BD_MAX_POSITIONS; stability_threshold >= 1; max_steps >= 1.
+ */
+int diffusion_loop_update(const int32_t* tokens, int32_t* canvas, int32_t* prev_canvas,
+                          const uint8_t* frozen, int32_t* loop_state, int P,
+                          int stability_threshold, int max_steps, int write_drafts,
+                          void* stream);
 
 /* ------------------------------------------------------------------ measurement */
 

@@ -174,6 +174,30 @@ def test_norm_router_validation(lib):
     assert rt(ctypes.c_void_p(0x1002), P, 4, 2816, 128, P, None) == 3
 
 
+def test_loop_driver_validation(lib):
+    from oracle import loop
+    for args in [(256, 64, 0, 0), (256, 64, 12, 0), (256, 64, 100, 0), (256, 64, 999, 0),
+                 (256, 64, 12, 1), (32, 64, 5, 0), (1, 1, 0, 0)]:
+        assert lib.bd_canvas_length(*args) == loop.canvas_length(*args[:3], bool(args[3]))
+    assert lib.bd_canvas_length(0, 64, 5, 0) == 0
+    assert lib.bd_canvas_length(256, 0, 5, 0) == 0
+    assert lib.bd_canvas_length(256, 64, -1, 0) == 0
+    P = ctypes.c_void_p(0x1000)
+    init = lib.diffusion_canvas_init
+    assert init(P, P, P, P, 0, 100, 0, 0, None) == 2
+    assert init(P, P, P, P, 1025, 100, 0, 0, None) == 2
+    assert init(P, P, P, P, 8, 0, 0, 0, None) == 2
+    assert init(P, P, P, P, 8, (1 << 24) + 1, 0, 0, None) == 2
+    assert init(P, None, P, P, 8, 100, 0, 0, None) == 1
+    assert init(P, P, P, ctypes.c_void_p(0x1002), 8, 100, 0, 0, None) == 3
+    upd = lib.diffusion_loop_update
+    assert upd(P, P, P, P, P, 8, 0, 48, 1, None) == 2
+    assert upd(P, P, P, P, P, 8, 3, 0, 1, None) == 2
+    assert upd(None, P, P, P, P, 8, 3, 48, 1, None) == 1
+    assert upd(P, P, P, P, None, 8, 3, 48, 1, None) == 1
+    assert upd(ctypes.c_void_p(0x1001), P, P, P, P, 8, 3, 48, 1, None) == 3
+
+
 def test_prepare_sizes_and_validation(lib):
     w = _weights()
     ref = ctypes.byref(w)
