@@ -103,7 +103,8 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=20):
     * ffn_layer_uniform: one whole FFN layer (route, gate/up, down, combine) at the 256-token
       canvas with uniform N(0, 1) router logits (every expert touched);
     * sampler_entropy_bound / sampler_confidence: one sampler step over all rows unfrozen;
-    * rmsnorm / router: the layer neighbours at the same shape.
+    * rmsnorm / router: the layer neighbours at the same shape;
+    * canvas_init / loop_update: the denoising-loop driver's two launches at the canvas size.
     """
     import torch
     from block_diffusion_lm_router_amd import _binding  # noqa: F401
@@ -176,6 +177,15 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=20):
     rl = torch.empty((T, E), dtype=torch.float32, device="cuda")
     timed("rmsnorm", [bd.bind(bd.moe_rmsnorm, hh, wn, xn) for hh in hs], 2 * T * d * 2 + d * 2)
     timed("router", [bd.bind(bd.moe_router_logits, xn, wr, rl)], T * d * 2 + E * d * 2 + T * E * 4)
+
+    prev = torch.empty(P, dtype=torch.int32, device="cuda")
+    state = torch.zeros(4, dtype=torch.int32, device="cuda")
+    timed("canvas_init", [bd.bind(bd.diffusion_canvas_init, canvas, prev, frozen, state, V, 0, 0)],
+          P * (4 + 4 + 1) + 16)
+    # a block that never ends inside the timed calls (threshold and budget out of reach)
+    timed("loop_update", [bd.bind(bd.diffusion_loop_update, tok, canvas, prev, frozen, state,
+                                  1 << 30, 1 << 30)], P * (4 + 4 + 4 + 4 + 1) + 32,
+          pre=frozen.zero_)
     return out
 
 
