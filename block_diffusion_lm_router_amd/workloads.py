@@ -97,22 +97,26 @@ def _zeros(rng, shape):
     return (_random_bytes(rng, shape) & 0x0F).astype(np.float16)
 
 
-def make_weights(shape: LayerShape, layer: int = 0):
+def make_weights(shape: LayerShape, layer: int = 0, gate_up_group: int = None,
+                 down_group: int = None):
     """Packed uint4 expert weights of one layer (seed 100 + layer).
 
     Layout (see include/bdstep.h): gate_up_q [E][2f][d/2] (gate rows first),
     gate_up_scale / gate_up_zero fp16 [E][2f][d/g]; down_q [E][d][f/2],
-    down_scale / down_zero fp16 [E][d][f/g].
+    down_scale / down_zero fp16 [E][d][f/g_down].  The group sizes default to shape.group;
+    gate_up_group=128 with down_group=64 is the format of the model card's checkpoint.
     """
-    E, d, f, g = shape.experts, shape.d_model, shape.d_ff, shape.group
+    E, d, f = shape.experts, shape.d_model, shape.d_ff
+    g = gate_up_group or shape.group
+    gd = down_group or shape.group
     rng = _rng(SEED_WEIGHTS + layer)
     return {
         "gate_up_q": _random_bytes(rng, (E, 2 * f, d // 2)),
         "gate_up_scale": _scales(rng, (E, 2 * f, d // g)),
         "gate_up_zero": _zeros(rng, (E, 2 * f, d // g)),
         "down_q": _random_bytes(rng, (E, d, f // 2)),
-        "down_scale": _scales(rng, (E, d, f // g)),
-        "down_zero": _zeros(rng, (E, d, f // g)),
+        "down_scale": _scales(rng, (E, d, f // gd)),
+        "down_zero": _zeros(rng, (E, d, f // gd)),
     }
 
 

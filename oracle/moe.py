@@ -80,18 +80,20 @@ def gelu_tanh(a):
     return 0.5 * a * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (a + 0.044715 * a ** 3)))
 
 
-def expert_matrices(weights, e, group=GROUP):
+def expert_matrices(weights, e, group=GROUP, down_group=None):
     """Dense float64 gate, up and down matrices of expert ``e``.
 
     ``weights`` maps the names gate_up_q, gate_up_scale, gate_up_zero, down_q,
     down_scale, down_zero to arrays laid out [E][rows][...] as in the C header.
-    Returns (W_gate [f, d], W_up [f, d], W_down [d, f]).
+    ``group`` is the gate/up group size, ``down_group`` the down one (None: the same);
+    the checkpoint format on the model card's "requirements" groups gate_up at 128 and
+    down at 64.  Returns (W_gate [f, d], W_up [f, d], W_down [d, f]).
     """
     gu = dequant(weights["gate_up_q"][e], weights["gate_up_scale"][e],
                  weights["gate_up_zero"][e], group)
     f = gu.shape[0] // 2
     wd = dequant(weights["down_q"][e], weights["down_scale"][e],
-                 weights["down_zero"][e], group)
+                 weights["down_zero"][e], group if down_group is None else down_group)
     return gu[:f], gu[f:], wd
 
 
@@ -103,7 +105,7 @@ def expert_ffn(x_rows, w_gate, w_up, w_down):
     return (gelu_tanh(a) * u) @ w_down.T
 
 
-def moe_expert_outputs(x, ids, weights, group=GROUP, tokens=None):
+def moe_expert_outputs(x, ids, weights, group=GROUP, tokens=None, down_group=None):
     """Per-assignment expert outputs o[t, j] = FFN_{ids[t, j]}(x[t]).
 
     ``x`` fp16 [T, d]; returns float64 [T, k, d].  With ``tokens`` given, only
@@ -118,7 +120,7 @@ def moe_expert_outputs(x, ids, weights, group=GROUP, tokens=None):
     mask[rows] = True
     for e in np.unique(ids[rows]):
         tt, jj = np.nonzero((ids == e) & mask[:, None])
-        w_gate, w_up, w_down = expert_matrices(weights, int(e), group)
+        w_gate, w_up, w_down = expert_matrices(weights, int(e), group, down_group)
         out[tt, jj] = expert_ffn(x64[tt], w_gate, w_up, w_down)
     return out
 
@@ -133,11 +135,11 @@ def combine(expert_out, topk_weights):
     return y
 
 
-def moe_ffn(x, router_logits, weights, k, group=GROUP, tokens=None):
+def moe_ffn(x, router_logits, weights, k, group=GROUP, tokens=None, down_group=None):
     """The whole layer: route, run the selected experts, combine.
 
     Returns (ids, topk_weights, expert_out [T, k, d], y [T, d]) in float64.
     """
     ids, tw = route_topk(router_logits, k)
-    o = moe_expert_outputs(x, ids, weights, group, tokens)
+    o = moe_expert_outputs(x, ids, weights, group, tokens, down_group)
     return ids, tw, o, combine(o, tw)

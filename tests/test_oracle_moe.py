@@ -196,3 +196,41 @@ def test_page_memory_figures(golden_dir):
     gu, dn = workloads.expert_bytes(workloads.LAYER)
     assert gu == 2 * f * d // 2 + 2 * 2 * (2 * f * d // 64)
     assert dn == d * f // 2 + 2 * 2 * (d * f // 64)
+
+
+# ---------------------------------------------------------------- checkpoint format groups
+
+
+def test_group_128_equals_group_64_with_each_pair_sharing_scale_and_zero():
+    """A 128-group is two 64-groups with the same scale and zero-point."""
+    rng = np.random.default_rng(31)
+    N, K = 6, 512
+    packed = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    s128 = rng.uniform(0.005, 0.02, (N, K // 128)).astype(np.float16)
+    z128 = rng.integers(0, 16, (N, K // 128)).astype(np.float16)
+    w128 = moe.dequant(packed, s128, z128, 128)
+    w64 = moe.dequant(packed, np.repeat(s128, 2, axis=1), np.repeat(z128, 2, axis=1), 64)
+    assert np.array_equal(w128, w64)
+    q = moe.unpack_nibbles(packed)
+    k = np.arange(K)
+    assert np.array_equal(w128, (q - z128.astype(np.float64)[:, k // 128]) * s128.astype(np.float64)[:, k // 128])
+
+
+def test_checkpoint_format_groups_per_matrix():
+    """gate_up at g = 128 and down at g = 64 (the model card's checkpoint format): the
+    expert matrices come from each matrix's own group size, checked against scalar loops."""
+    from block_diffusion_lm_router_amd import workloads
+    shape = workloads.LayerShape(4, 256, 128, 3, 2)
+    w = workloads.make_weights(shape, 0, gate_up_group=128, down_group=64)
+    assert w["gate_up_scale"].shape == (3, 256, 2) and w["down_scale"].shape == (3, 256, 2)
+    wg, wu, wd = moe.expert_matrices(w, 1, 128, 64)
+    q = moe.unpack_nibbles(w["gate_up_q"][1])
+    for n, col in ((0, 5), (130, 200), (255, 255)):
+        g = col // 128
+        ref = (q[n, col] - float(w["gate_up_zero"][1, n, g])) * float(w["gate_up_scale"][1, n, g])
+        got = wg[n, col] if n < 128 else wu[n - 128, col]
+        assert got == ref
+    qd = moe.unpack_nibbles(w["down_q"][1])
+    for n, col in ((0, 0), (77, 127), (255, 64)):
+        g = col // 64
+        assert wd[n, col] == (qd[n, col] - float(w["down_zero"][1, n, g])) * float(w["down_scale"][1, n, g])
