@@ -44,6 +44,7 @@ class MoeWeightsC(ctypes.Structure):
         ("down_zero", _P),
         ("gate_up_packed", _P),
         ("down_packed", _P),
+        ("down_group_size", ctypes.c_int32),
     ]
 
 
@@ -160,16 +161,22 @@ class MoeWeights:
 
     KEYS = ("gate_up_q", "gate_up_scale", "gate_up_zero", "down_q", "down_scale", "down_zero")
 
-    def __init__(self, tensors, top_k, group_size=64):
+    def __init__(self, tensors, top_k, group_size=None, down_group_size=None):
+        """Group sizes default to what the scale arrays' shapes imply (d_model / groups of
+        gate/up, d_ff / groups of down)."""
         self.tensors = tensors
         gq = tensors["gate_up_q"]
         E, two_f, half_d = gq.shape
         self.num_experts, self.d_ff, self.d_model = E, two_f // 2, half_d * 2
-        self.top_k, self.group_size = top_k, group_size
+        if group_size is None:
+            group_size = self.d_model // tensors["gate_up_scale"].shape[-1]
+        if down_group_size is None:
+            down_group_size = self.d_ff // tensors["down_scale"].shape[-1]
+        self.top_k, self.group_size, self.down_group_size = top_k, group_size, down_group_size
         dtypes = {"gate_up_q": torch.uint8, "down_q": torch.uint8}
         ptrs = {k: _ptr(tensors[k], dtypes.get(k, torch.float16), k) for k in self.KEYS}
         self.c = MoeWeightsC(E, top_k, self.d_model, self.d_ff, group_size,
-                             *[ptrs[k] for k in self.KEYS], None, None)
+                             *[ptrs[k] for k in self.KEYS], None, None, down_group_size)
         self.packed = None
 
     def prepare(self, drop_raw=False):
@@ -203,10 +210,10 @@ class MoeWeights:
         return self
 
     @classmethod
-    def from_numpy(cls, arrays, top_k, device="cuda", group_size=64, prepare=False,
-                   drop_raw=False):
+    def from_numpy(cls, arrays, top_k, device="cuda", group_size=None, prepare=False,
+                   drop_raw=False, down_group_size=None):
         t = {k: torch.from_numpy(arrays[k]).to(device) for k in cls.KEYS}
-        w = cls(t, top_k, group_size)
+        w = cls(t, top_k, group_size, down_group_size)
         return w.prepare(drop_raw=drop_raw) if prepare else w
 
     def ref(self):

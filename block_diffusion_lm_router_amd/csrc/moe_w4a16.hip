@@ -825,12 +825,13 @@ void launch_packed(const GemmArgs& a, int max_items, hipStream_t stream) {
 }
 
 // Repacking into the packed stream (layout above).  One thread per 16-byte chunk of the output;
-// rows past the matrix and the group past an odd G are written as zeros.
+// rows past the matrix and the group past an odd G are written as zeros.  With source groups of
+// 128 (gshift 1) each 64-group slot takes the scale and zero-point of the 128-group holding it.
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ q,
                                                    const uint16_t* __restrict__ scale,
                                                    const uint16_t* __restrict__ zero, int R, int K,
-                                                   int tiles, int gated, int d_ff, size_t chunks,
-                                                   u32x4_t* __restrict__ out) {
+                                                   int tiles, int gated, int d_ff, int gshift,
+                                                   size_t chunks, u32x4_t* __restrict__ out) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= chunks) return;
   const int G = K / 64, NS = (G + 1) / 2;
@@ -873,9 +874,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ q
     for (int set = 0; set < 2; ++set) {
       const int row = mrow(tile_row(w, set, nn));
       if (row < 0) continue;
-      const size_t base = ((size_t)e * R + row) * G;
-      const uint32_t s0 = scale[base + g0], z0 = zero[base + g0];
-      const uint32_t s1 = g1 < G ? scale[base + g1] : 0u, z1 = g1 < G ? zero[base + g1] : 0u;
+      const size_t base = ((size_t)e * R + row) * (G >> gshift);
+      const uint32_t s0 = scale[base + (g0 >> gshift)], z0 = zero[base + (g0 >> gshift)];
+      const uint32_t s1 = g1 < G ? scale[base + (g1 >> gshift)] : 0u;
+      const uint32_t z1 = g1 < G ? zero[base + (g1 >> gshift)] : 0u;
       v[2 * set] = s0 | (s1 << 16);
       v[2 * set + 1] = z0 | (z1 << 16);
     }
@@ -903,7 +905,7 @@ hipError_t launch_pack(const W4A16Matrix& m, bool gated, int E, int d_model, int
   const size_t chunks = pk_bytes(gated, E, d_model, d_ff) / 16;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
                      m.q, m.scale, m.zero, R, K, pk_tiles(gated, d_model, d_ff), gated ? 1 : 0,
-                     d_ff, chunks, reinterpret_cast<u32x4_t*>(out));
+                     d_ff, m.group == 128 ? 1 : 0, chunks, reinterpret_cast<u32x4_t*>(out));
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 6
+#define BD_ABI_VERSION 7
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -71,18 +71,23 @@ typedef enum {
  * groups along the contraction dimension.
  *
  *   gate_up_q      uint8 [E][2*d_ff][d_model/2]   rows 0..d_ff-1 = gate, d_ff..2*d_ff-1 = up
- *   gate_up_scale  fp16  [E][2*d_ff][d_model/g]
+ *   gate_up_scale  fp16  [E][2*d_ff][d_model/g]      g  = group_size
  *   gate_up_zero   fp16  [E][2*d_ff][d_model/g]
  *   down_q         uint8 [E][d_model][d_ff/2]
- *   down_scale     fp16  [E][d_model][d_ff/g]
- *   down_zero      fp16  [E][d_model][d_ff/g]
+ *   down_scale     fp16  [E][d_model][d_ff/gd]      gd = down_group_size (0: gd = g)
+ *   down_zero      fp16  [E][d_model][d_ff/gd]
  *
  * Byte i of a packed row holds element 2i in its low nibble and element 2i+1 in its
  * high nibble.  The dequantised weight is w[n][k] = (q[n][k] - zero[n][k/g]) *
  * scale[n][k/g].  Zero-points are the uint4 code of the zero (an integer 0..15 held
  * in fp16); the GEMM subtracts them exactly in fp16, a non-integer zero-point is
  * rounded to the nearest integer first.
- * Supported: group_size == 64, d_model % 128 == 0, d_ff % 64 == 0, d_model and d_ff <= 4096.
+ * Supported: d_model % 128 == 0, d_ff % 64 == 0, d_model and d_ff <= 4096; g and gd each 64
+ * or 128 and dividing that matrix's contraction dim (d_model for gate/up, d_ff for down).
+ * A group of 128 is used through the packed stream only (moe_w4a16_prepare spreads its
+ * scale and zero-point over the stream's two 64-group slots); a GEMM over raw arrays with a
+ * group of 128 returns BD_ERR_UNSUPPORTED.  The model card's checkpoint format
+ * ("requirements") is g = 128, gd = 64.
  *
  * gate_up_packed / down_packed (optional, NULL when absent): the matrix repacked once by
  * moe_w4a16_prepare into the stream the 256-row GEMM tiles consume.  A GEMM whose packed
@@ -96,7 +101,7 @@ typedef struct bd_moe_weights {
   int32_t top_k;       /* k, 1..min(E, 16)   */
   int32_t d_model;     /* d                  */
   int32_t d_ff;        /* f                  */
-  int32_t group_size;  /* g, must be 64      */
+  int32_t group_size;  /* g of gate/up: 64 or 128 (128 via the packed stream only) */
   const uint8_t* gate_up_q;
   const uint16_t* gate_up_scale;
   const uint16_t* gate_up_zero;
@@ -105,6 +110,7 @@ typedef struct bd_moe_weights {
   const uint16_t* down_zero;
   const uint8_t* gate_up_packed;  /* optional, bd_moe_packed_size(w, 0) bytes, 16-byte aligned */
   const uint8_t* down_packed;     /* optional, bd_moe_packed_size(w, 1) bytes, 16-byte aligned */
+  int32_t down_group_size;        /* gd of down: 0 (= g), 64 or 128 (128 via the packed stream) */
 } bd_moe_weights;
 
 /* Library ABI version (BD_ABI_VERSION of the build). */

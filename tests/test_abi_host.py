@@ -55,10 +55,10 @@ def test_version_and_status_strings(lib):
     assert lib.bd_status_string(99) == b"unknown status"
 
 
-def _weights(E=128, k=8, d=2816, f=704, g=64, ptr=0x1000):
+def _weights(E=128, k=8, d=2816, f=704, g=64, ptr=0x1000, gd=0):
     from block_diffusion_lm_router_amd._binding import MoeWeightsC
     p = ctypes.c_void_p(ptr)
-    return MoeWeightsC(E, k, d, f, g, p, p, p, p, p, p, None, None)
+    return MoeWeightsC(E, k, d, f, g, p, p, p, p, p, p, None, None, gd)
 
 
 def test_moe_workspace_size(lib):
@@ -75,7 +75,8 @@ def test_moe_workspace_size(lib):
 @pytest.mark.parametrize("kw,T,code", [
     (dict(), 0, 2), (dict(), 65537, 2), (dict(E=0), 4, 2), (dict(E=257), 4, 2),
     (dict(k=0), 4, 2), (dict(k=17), 4, 2), (dict(E=4, k=5), 4, 2),
-    (dict(g=128), 4, 5), (dict(d=2880), 4, 5), (dict(f=700), 4, 5),
+    (dict(g=32), 4, 5), (dict(g=128, gd=256), 4, 5), (dict(d=2880), 4, 5), (dict(f=700), 4, 5),
+    (dict(g=128, d=2880 - 64), 4, 2), (dict(gd=128), 4, 2),
 ])
 def test_moe_shape_validation(lib, kw, T, code):
     w = _weights(**kw)
@@ -209,8 +210,19 @@ def test_prepare_sizes_and_validation(lib):
     p = ctypes.c_void_p(0x1000)
     assert lib.moe_w4a16_prepare(ref, None, p, None) == 1              # BD_ERR_NULL
     assert lib.moe_w4a16_prepare(ref, ctypes.c_void_p(0x1008), p, None) == 3   # BD_ERR_ALIGN
-    bad = _weights(g=128)
+    bad = _weights(g=32)
     assert lib.moe_w4a16_prepare(ctypes.byref(bad), p, p, None) == 5   # BD_ERR_UNSUPPORTED
+    bad = _weights(g=128)                                              # down at 128: 704 % 128
+    assert lib.moe_w4a16_prepare(ctypes.byref(bad), p, p, None) == 2   # BD_ERR_SHAPE
+    # the checkpoint format (gate/up 128, down 64) packs into the same stream sizes
+    ck = _weights(g=128, gd=64)
+    assert lib.bd_moe_packed_size(ctypes.byref(ck), 0) == 128 * 6 * 22 * 18432
+    assert lib.bd_moe_packed_size(ctypes.byref(ck), 1) == 128 * 11 * 6 * 18432
+    # a 128-group over raw arrays is refused by the GEMMs; with the packed stream it is not
+    ws = ctypes.c_void_p(0x10000)
+    assert lib.moe_w4a16_gate_up(ctypes.byref(ck), 256, p, ws, 1 << 30, None) == 5
+    assert lib.moe_w4a16_down(ctypes.byref(_weights(g=64, gd=128, f=768)), 256, p, ws, 1 << 30,
+                              None) == 5
     # a misaligned packed stream is rejected by the GEMM entry points before any launch
     w.gate_up_packed = 0x1008
     ws = ctypes.c_void_p(0x10000)

@@ -33,6 +33,9 @@ class Layer:
         self.x = workloads.make_activations(shape) if x is None else x
         self.logits = workloads.make_router_logits(shape, layer) if logits is None else logits
         self.w_np = workloads.make_weights(shape, layer) if weights is None else weights
+        # group sizes as the scale arrays' shapes imply (gate/up, down)
+        self.groups = (shape.d_model // self.w_np["gate_up_scale"].shape[-1],
+                       shape.d_ff // self.w_np["down_scale"].shape[-1])
         self.w = bd.MoeWeights.from_numpy(self.w_np, shape.top_k)
         self.x_d = torch.from_numpy(self.x).cuda()
         self.logits_d = torch.from_numpy(self.logits).cuda()
@@ -74,7 +77,7 @@ def outputs_and_h_rounding_bound(layer, ids, rows):
     x64 = layer.x.astype(np.float64)
     for e in np.unique(ids[rows]):
         tt, jj = np.nonzero((ids == e) & mask[:, None])
-        wg, wu, wd = omoe.expert_matrices(layer.w_np, int(e))
+        wg, wu, wd = omoe.expert_matrices(layer.w_np, int(e), *layer.groups)
         o[tt, jj] = omoe.expert_ffn(x64[tt], wg, wu, wd)
         h = omoe.gelu_tanh(x64[tt] @ wg.T) * (x64[tt] @ wu.T)
         bound[tt, jj] = (np.abs(h) @ np.abs(wd.T)) * 2.0 ** -11
@@ -316,3 +319,41 @@ def test_widest_routing(bd, prepared):
     got = layer.run(bd, prepared=prepared)
     assert not np.isnan(got[2]).any()
     check_layer(layer, got)
+
+
+# ---------------------------------------------------------------- checkpoint format groups
+
+
+def test_group128_packs_to_the_same_stream_as_duplicated_group64(bd):
+    """Repacking 128-groups gives the stream of the same weights written as 64-groups whose
+    pairs share a scale and zero-point (byte for byte), so the GEMMs need no other path."""
+    shape = workloads.LayerShape(8, 512, 256, 3, 2)
+    w128 = workloads.make_weights(shape, 3, gate_up_group=128, down_group=128)
+    w64 = dict(w128)
+    for k in ("gate_up_scale", "gate_up_zero", "down_scale", "down_zero"):
+        w64[k] = np.ascontiguousarray(np.repeat(w128[k], 2, axis=-1))
+    say("group-128 packing")
+    a = bd.MoeWeights.from_numpy(w128, 2, prepare=True)
+    b = bd.MoeWeights.from_numpy(w64, 2, prepare=True)
+    assert (a.group_size, a.down_group_size, b.group_size) == (128, 128, 64)
+    import torch
+    torch.cuda.synchronize()
+    for pa, pb in zip(a.packed, b.packed):
+        assert torch.equal(pa, pb)
+
+
+@pytest.mark.parametrize("which", ["tiny", "layer"])
+def test_checkpoint_format_layer(bd, which):
+    """gate/up grouped at 128, down at 64 (the checkpoint format) through the packed streams:
+    ids bit-exact, outputs within the FFN bar (all tokens on the tiny shape, sampled tokens at
+    the full shape); the raw-array GEMM refuses the 128-groups."""
+    shape = workloads.TINY_LAYER if which == "tiny" else workloads.LAYER
+    w_np = workloads.make_weights(shape, 5, gate_up_group=128, down_group=64)
+    say("checkpoint format", which)
+    layer = Layer(bd, shape, weights=w_np)
+    assert layer.groups == (128, 64)
+    tokens = None if which == "tiny" else np.random.default_rng(1).choice(shape.tokens, 6, replace=False)
+    check_layer(layer, layer.run(bd, prepared=True), tokens=tokens)
+    layer.w.unprepare()
+    with pytest.raises(bd.BdError):
+        layer.run(bd, prepared=False)
