@@ -12,7 +12,15 @@ zero-points, activations in and out, router logits, the unfrozen logits rows) / 
 in GB/s; ms_per_step is the latency of one step; config.step_ms_p10_p50_p90 is the spread of
 the step latency over a second pass of the same length with an event between steps.
 
+Two more workloads time the parts on their own configurations (--workload):
+  layer    one MoE FFN layer (route, gate/up, down, combine) at the 256-token canvas with uniform
+           N(0, 1) router logits (every expert touched), two independently seeded layers in turn;
+  sampler  the sampler step alone over fp32 logits [256, 262144] (every row unfrozen), two copies
+           of the logits in turn.
+Each reports the same fields; its roofline covers its dominant launch.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--workload stack|layer|sampler]
 """
 
 import argparse
@@ -36,6 +44,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=None, help="MoE layers per step (default 30)")
+    ap.add_argument("--workload", choices=("stack", "layer", "sampler"), default="stack",
+                    help="stack (default): the whole denoising step; layer: one FFN layer at the "
+                         "256-token canvas with uniform routing; sampler: the sampler alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -189,12 +200,179 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=20):
     return out
 
 
+def timed_loop(fn, steps, warmup):
+    """ms per call of fn over `steps` calls after `warmup`, bracketed by synchronisation."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(warmup, warmup + steps):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def base_record(args, value, ms, workload, extra_config):
+    cfg = {"workload": workload}
+    cfg.update(extra_config)
+    cfg["hbm_frac_of_peak"] = round(value / HBM_PEAK_GBS, 4)
+    return {
+        "metric": "denoising-step MoE+sampler latency (ms) and achieved HBM GB/s vs peak, 1 GPU",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16-mfma/f32", "data": "synthetic",
+        "config": cfg,
+    }
+
+
+def main_layer(args):
+    """One FFN layer at the 256-token canvas, uniform routing; roofline of the gate/up launch."""
+    import torch
+    from block_diffusion_lm_router_amd import _binding as bd, workloads
+    torch.cuda.set_device(0)
+    shape = workloads.LAYER
+    T, d, f, E, k = shape.tokens, shape.d_model, shape.d_ff, shape.experts, shape.top_k
+    gu_b, dn_b = workloads.expert_bytes(shape)
+    x_np = workloads.make_activations(shape)
+    r_np = workloads.make_router_logits(shape)
+    x, router = torch.from_numpy(x_np).cuda(), torch.from_numpy(r_np).cuda()
+    w0_np = workloads.make_weights(shape, 0)
+    layers = [bd.MoeWeights.from_numpy(w0_np, k, prepare=True, drop_raw=True),
+              bd.MoeWeights.from_numpy(workloads.make_weights(shape, 1), k, prepare=True,
+                                       drop_raw=True)]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    o = torch.empty((T, k, d), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    ws = bd.moe_workspace(T, layers[0])
+    bd.moe_route_topk(layers[0], router, ids, tw, ws)
+    touched = int(torch.unique(ids).numel())
+    launches = [(bd.bind(bd.moe_route_topk, w, router, ids, tw, ws),
+                 bd.bind(bd.moe_w4a16_gate_up, w, x, ws),
+                 bd.bind(bd.moe_w4a16_down, w, T, o, ws),
+                 bd.bind(bd.moe_combine_fixed_order, o, tw, y)) for w in layers]
+
+    def step(i):
+        for fn in launches[i % 2]:
+            fn()
+
+    log(f"timing {args.steps} layer passes")
+    ms = timed_loop(step, args.steps, args.warmup)
+    alg = touched * (gu_b + dn_b) + 2 * T * d * 2 + T * E * 4 + 2 * T * k * 4
+    value = alg / (ms * 1e-3) / 1e9
+    # the gate/up launch alone, each bracketed by its own events (a separate pass)
+    stream = torch.cuda.current_stream()
+    evs = []
+    for i in range(args.steps):
+        route, gate_up, down, combine = launches[i % 2]
+        route()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        gate_up()
+        b.record(stream)
+        down()
+        combine()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    gu_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    gu_alg = touched * gu_b + T * d * 2 + T * k * f * 2
+    gu_gbs = gu_alg / (gu_us * 1e-6) / 1e9
+    rec = base_record(args, value, ms,
+                      f"layer: one MoE FFN layer (canvas {T}, d_model {d}, expert ffn {f}, {E} experts "
+                      f"top-{k}, W4A16 asym g64, uniform N(0,1) router logits), route + gate/up + "
+                      f"down + combine", {"experts_touched": touched, "step_algorithmic_bytes": int(alg)})
+    rec["roofline"] = {"kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22>)", "bound": "hbm",
+                       "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                       "avg_launch_us": round(gu_us, 2), "alg_bytes_per_launch": int(gu_alg)}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        from threadpoolctl import threadpool_limits
+        from oracle import moe as omoe
+        threads = min(os.cpu_count() or 1, 16)
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            omoe.moe_ffn(x_np, r_np, w0_np, k)
+            secs = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(alg / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"numpy fp64 oracle: one whole layer ({T} tokens, {touched} "
+                                         f"experts) in {secs:.2f} s; same byte accounting"}
+    print(json.dumps(rec), flush=True)
+
+
+def main_sampler(args):
+    """The sampler step alone on [256, 262144] fp32 logits; roofline of the whole call."""
+    import torch
+    from block_diffusion_lm_router_amd import _binding as bd, workloads
+    torch.cuda.set_device(0)
+    sshape = workloads.SAMPLER
+    P, V = sshape.positions, sshape.vocab
+    lg_np = workloads.make_logits(sshape)
+    lgs = [torch.from_numpy(lg_np).cuda() for _ in range(2)]
+    tok = torch.empty(P, dtype=torch.int32, device="cuda")
+    H = torch.empty(P, dtype=torch.float32, device="cuda")
+    acc = torch.empty(P, dtype=torch.uint8, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    sws = bd.sample_workspace(P, V)
+    calls = [[bd.bind(bd.diffusion_sample_step, lg, sshape.temperature, sshape.bound, sshape.seed,
+                      s, None, None, tok, H, acc, cnt, sws) for lg in lgs] for s in range(2)]
+
+    def step(i):
+        calls[(i // 2) % 2][i % 2]()
+
+    log(f"timing {args.steps} sampler steps")
+    ms = timed_loop(step, args.steps, args.warmup)
+    alg = P * V * 4 + P * (4 + 4 + 1) + 4
+    value = alg / (ms * 1e-3) / 1e9
+    stream = torch.cuda.current_stream()
+    evs = []
+    for i in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(i)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    gbs = alg / (us * 1e-6) / 1e9
+    rec = base_record(args, value, ms,
+                      f"sampler: fp32 logits [{P}, {V}] (N(0,1) + one entry boosted U[0,12]), "
+                      f"entropy + two-level gumbel-max at T=1, entropy-bound acceptance at 2.0, "
+                      f"every row unfrozen", {"step_algorithmic_bytes": int(alg)})
+    rec["roofline"] = {"kernel": "diffusion_sample_step (sample_stream_kernel + sample_finish_kernel "
+                                 "+ accept_kernel)", "bound": "hbm", "achieved": round(gbs, 2),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                       "traffic": None, "avg_launch_us": round(us, 2), "alg_bytes_per_launch": int(alg)}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        from oracle import sampler as osamp
+        t0 = time.perf_counter()
+        H_ref, _ = osamp.sample_rows(lg_np, sshape.temperature, sshape.seed, 0)
+        osamp.accept(H_ref.astype(np.float32), sshape.bound)
+        secs = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(alg / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"numpy fp64 oracle: one whole sampler step over all {P} rows "
+                                         f"in {secs:.2f} s (numpy element-wise, one thread); same byte "
+                                         f"accounting"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "layer":
+        return main_layer(args)
+    if args.workload == "sampler":
+        return main_sampler(args)
     import torch
     from block_diffusion_lm_router_amd import _binding as bd, workloads
 
