@@ -381,3 +381,43 @@ def test_full_size_step_confidence(bd, which):
         assert np.array_equal(canvas.cpu().numpy(), np.where(ref_mask == 1, tok_np, -7))
         if which == "sampler_wide":
             assert ref_n > 1        # near-zero entropies put many rows above 0.9
+
+
+@pytest.mark.parametrize("P", [1, 63, 256, 257, 1024])
+@pytest.mark.parametrize("rule", ["entropy", "confidence"])
+def test_step_both_acceptance_launch_shapes(bd, P, rule):
+    """Whole sampler steps across the acceptance block sizes (64 .. 1024 threads): the oracle's
+    mask on the GPU's own statistics, call after call on one workspace, with frozen rows and
+    the canvas carried from call to call."""
+    import torch
+    rng = np.random.default_rng(P * 3 + len(rule))
+    V = 1500
+    x = rng.standard_normal((P, V)).astype(np.float32)
+    x[np.arange(P), rng.integers(0, V, P)] += rng.uniform(0, 25, P).astype(np.float32)
+    ws = bd.sample_workspace(P, V)
+    frozen = torch.from_numpy((rng.random(P) < 0.2).astype(np.uint8)).cuda()
+    canvas = torch.full((P,), -3, dtype=torch.int32, device="cuda")
+    tok = torch.empty(P, dtype=torch.int32, device="cuda")
+    stat = torch.empty(P, dtype=torch.float32, device="cuda")
+    acc = torch.empty(P, dtype=torch.uint8, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    lg = torch.from_numpy(x).cuda()
+    for call in range(3):
+        say("step launch shapes", P, rule, call)
+        fr_before = frozen.cpu().numpy()
+        cv_before = canvas.cpu().numpy()
+        if rule == "entropy":
+            bd.diffusion_sample_step(lg, 1.0, 1.5, 4, call, frozen, canvas, tok, stat, acc, cnt, ws)
+        else:
+            bd.diffusion_sample_step_confidence(lg, 1.0, 0.9, 4, call, frozen, canvas, tok, stat,
+                                                acc, cnt, ws)
+        torch.cuda.synchronize()
+        st = stat.cpu().numpy()
+        tk = tok.cpu().numpy()
+        if rule == "entropy":
+            mask, n = osamp.accept(st, 1.5, fr_before)
+        else:
+            mask, n = osamp.accept_confidence(st, 0.9, fr_before)
+        assert int(cnt.item()) == n and np.array_equal(acc.cpu().numpy(), mask), f"call {call}"
+        assert np.array_equal(frozen.cpu().numpy(), np.maximum(fr_before, mask))
+        assert np.array_equal(canvas.cpu().numpy(), np.where(mask == 1, tk, cv_before))
