@@ -396,11 +396,30 @@ __device__ __forceinline__ float float_from_order_key(uint32_t k) {
   return __builtin_bit_cast(float, u);
 }
 
+// Block-wide minimum of one 64-bit key per thread (uniform result, one barrier; wmin is an
+// LDS slot of blockDim.x / 64 entries that no other thread reads before the next barrier).
+__device__ __forceinline__ unsigned long long block_min_u64(unsigned long long k,
+                                                            unsigned long long* wmin) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(k, off);
+    k = o < k ? o : k;
+  }
+  if (lane_id() == 0) wmin[threadIdx.x / kWave] = k;
+  __syncthreads();
+  unsigned long long m = wmin[0];
+  for (int w = 1; w < (int)(blockDim.x / kWave); ++w) m = wmin[w] < m ? wmin[w] : m;
+  return m;
+}
+
+constexpr int kSelectSteps = 8;  // positions taken by selection before the full sort
+
 __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const float* __restrict__ entropy, const int32_t* __restrict__ tokens, int P, float bound,
     uint8_t* __restrict__ frozen, int32_t* __restrict__ canvas, uint8_t* __restrict__ accept_out,
     int32_t* __restrict__ num_accepted) {
   __shared__ uint64_t keys[kAcceptThreads];
+  __shared__ unsigned long long wmin[2][kAcceptThreads / kWave];
   __shared__ int sCount;
   // The block has n threads, n the smallest power of two >= max(P, 64); thread i holds key i.
   const int tid = threadIdx.x;
@@ -412,63 +431,90 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     if (!is_frozen && !(h != h)) key = ((uint64_t)float_order_key(h) << 32) | (uint32_t)tid;
     accept_out[tid] = 0;
   }
-  // Bitonic sort, ascending, of the n keys held one per thread.  Exchanges with a partner in
-  // the same wave (j < 64) go through cross-lane shuffles; wider ones through LDS.
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      unsigned long long other;
-      if (j < kWave) {
-        other = __shfl_xor(key, j);
-      } else {
-        keys[tid] = key;
-        __syncthreads();
-        other = keys[tid ^ j];
-        __syncthreads();
-      }
-      const bool up = (tid & k) == 0;
-      const bool lower = (tid & j) == 0;  // this thread holds the lower index of the pair
-      key = (lower == up) ? (key < other ? key : other) : (key < other ? other : key);
-    }
-  }
-  keys[tid] = key;
-  __syncthreads();
-  // One lane: the sequential fp32 scan in sorted order.
-  if (tid == 0) {
-    float S = 0.f;
-    int cnt = 0;
-    bool stop = false;
-    for (int base = 0; base < n && !stop; base += 8) {
-      uint64_t kk[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) kk[q] = (base + q < n) ? keys[base + q] : ~0ull;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (stop) break;
-        if (kk[q] == ~0ull) {
-          stop = true;
-          break;
-        }
-        const float h = float_from_order_key((uint32_t)(kk[q] >> 32));
-        S = __fadd_rn(S, h);
-        const float c = __fsub_rn(S, h);
-        if (!(c <= bound)) {
-          stop = true;
-          break;
-        }
-        ++cnt;
-      }
-    }
-    if (cnt == 0 && keys[0] != ~0ull) cnt = 1;
-    sCount = cnt;
-    *num_accepted = cnt;
-  }
-  __syncthreads();
-  if (tid < sCount) {
-    const int pos = (int)(uint32_t)keys[tid];
+  auto take = [&](int pos) {  // run by the thread that holds position pos
     accept_out[pos] = 1;
     if (canvas != nullptr) canvas[pos] = tokens[pos];
     if (frozen != nullptr) frozen[pos] = 1;
+  };
+  // Selection: the smallest remaining key, block-wide, one at a time; every thread runs the
+  // same fp32 scan on the same uniform values.  Most steps end here, after a few positions.
+  float S = 0.f;
+  int cnt = 0;
+  bool stop = false;
+  for (int it = 0; it < kSelectSteps && !stop; ++it) {
+    const unsigned long long m = block_min_u64(key, wmin[it & 1]);
+    if (m == ~0ull) {
+      stop = true;  // no candidate left
+      break;
+    }
+    const float h = float_from_order_key((uint32_t)(m >> 32));
+    const float S2 = __fadd_rn(S, h);
+    const float c = __fsub_rn(S2, h);
+    const bool pass = c <= bound;
+    if (pass || cnt == 0) {  // the first candidate is accepted whatever the bound
+      if (key == m) {
+        take(tid);
+        key = ~0ull;
+      }
+      ++cnt;
+      S = S2;
+    }
+    if (!pass) stop = true;
   }
+  if (!stop) {
+    // Still accepting: sort the remaining keys (the taken ones sort last) and continue the scan.
+    // Bitonic sort, ascending, of the n keys held one per thread.  Exchanges with a partner
+    // in the same wave (j < 64) go through cross-lane shuffles; wider ones through LDS.
+    for (int k = 2; k <= n; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        unsigned long long other;
+        if (j < kWave) {
+          other = __shfl_xor(key, j);
+        } else {
+          keys[tid] = key;
+          __syncthreads();
+          other = keys[tid ^ j];
+          __syncthreads();
+        }
+        const bool up = (tid & k) == 0;
+        const bool lower = (tid & j) == 0;  // this thread holds the lower index of the pair
+        key = (lower == up) ? (key < other ? key : other) : (key < other ? other : key);
+      }
+    }
+    keys[tid] = key;
+    __syncthreads();
+    // One lane: the sequential fp32 scan over the sorted remainder.
+    if (tid == 0) {
+      int more = 0;
+      bool done = false;
+      for (int base = 0; base < n && !done; base += 8) {
+        uint64_t kk[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) kk[q] = (base + q < n) ? keys[base + q] : ~0ull;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (done) break;
+          if (kk[q] == ~0ull) {
+            done = true;
+            break;
+          }
+          const float h = float_from_order_key((uint32_t)(kk[q] >> 32));
+          S = __fadd_rn(S, h);
+          const float c = __fsub_rn(S, h);
+          if (!(c <= bound)) {
+            done = true;
+            break;
+          }
+          ++more;
+        }
+      }
+      sCount = more;
+    }
+    __syncthreads();
+    if (tid < sCount) take((int)(uint32_t)keys[tid]);
+    cnt += sCount;
+  }
+  if (tid == 0) *num_accepted = cnt;
 }
 
 // Confidence-threshold acceptance on one workgroup.  Candidates: not frozen, confidence

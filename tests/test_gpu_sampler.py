@@ -421,3 +421,24 @@ def test_step_both_acceptance_launch_shapes(bd, P, rule):
         assert int(cnt.item()) == n and np.array_equal(acc.cpu().numpy(), mask), f"call {call}"
         assert np.array_equal(frozen.cpu().numpy(), np.maximum(fr_before, mask))
         assert np.array_equal(canvas.cpu().numpy(), np.where(mask == 1, tk, cv_before))
+
+
+@pytest.mark.parametrize("bound,expect", [(0.75, 7), (0.875, 8), (1.0, 9), (2.0, 17), (1e30, 40),
+                                          (-0.5, 1)])
+def test_accept_counts_around_the_selection_steps(bd, bound, expect):
+    """The acceptance takes its first positions by selection and sorts only when more pass; the
+    counts on either side of that switch (dyadic entropies: the exclusive sums are exact)."""
+    P = 40
+    rng = np.random.default_rng(int(expect))
+    H = np.full(P, 0.125, dtype=np.float32)
+    perm = rng.permutation(P)
+    H = H[perm]
+    H[perm[:3]] = np.float32(0.125)                  # ties everywhere: position order decides
+    tokens = np.arange(P, dtype=np.int32) + 100
+    say("accept around selection", bound, expect)
+    acc, cnt, fr, cv = run_accept(bd, H, tokens, bound, np.zeros(P, np.uint8),
+                                  np.zeros(P, np.int32))
+    ref_mask, ref_n = osamp.accept(H, bound)
+    assert ref_n == expect and cnt == expect and np.array_equal(acc, ref_mask)
+    assert np.array_equal(acc, (np.arange(P) < expect).astype(np.uint8))
+    assert np.array_equal(fr, ref_mask) and np.array_equal(cv, np.where(ref_mask == 1, tokens, 0))
