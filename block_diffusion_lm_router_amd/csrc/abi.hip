@@ -74,6 +74,7 @@ int check_sample_shape(int P, int V, float temperature) {
   if (P < 1 || P > BD_MAX_POSITIONS) return BD_ERR_SHAPE;
   if (V < 1 || V > BD_MAX_VOCAB) return BD_ERR_SHAPE;
   if (!(temperature >= 0.f) || !isfinite(temperature)) return BD_ERR_SHAPE;
+  if (temperature > 0.f && !isfinite(1.f / temperature)) return BD_ERR_SHAPE;  // 1/T overflows
   return BD_OK;
 }
 

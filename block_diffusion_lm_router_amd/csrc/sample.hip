@@ -14,11 +14,12 @@
 //     t  = sum of exp(x - m) (x - m).
 // With Z = n + s the entropy is H = ln Z - t / Z = log1p((n - 1) + s) - t / Z; keeping
 // the maximal entries out of s keeps H accurate when it is near zero.  The temperature-0
-// argmax needs only the chunk maxima.  For T > 0 the pass also stores each chunk's
-// log-mass L_c = ln sum exp(x / T), the input of the level-1 gumbel-max.  Partial states
-// of the V-splits of a row are merged in split order by the finish kernel, which also
-// draws the level-1 and level-2 gumbel noise (Philox, fp64) and re-reads the one winning
-// chunk (1024 entries) of the row.
+// argmax needs only the chunk maxima.  For T > 0 the pass also forms each chunk's log-mass
+// L_c = ln sum exp(x / T) and draws the level-1 key L_c + G_c (Philox, fp64): lane b of a wave
+// keeps the b-th chunk's L_c, and every 64 chunks (and at the end) the lanes draw their keys
+// at once and the wave keeps the best.  Partial states of the V-splits of a row are merged in
+// split order by the finish kernel, which re-reads the one winning chunk (1024 entries) for
+// the level-2 draw.
 
 #include "bd_device.hpp"
 #include "bd_internal.hpp"
@@ -85,10 +86,30 @@ struct LaneState {
   bool nan;      // NaN seen in a chunk with no finite entry (wave-uniform)
 };
 
-// MODE 0: temperature 0 (argmax); 1: temperature 1; 2: any other temperature.
+// Larger key first, then the lower index: a total order, so every reduction by it gives the
+// same result whatever its order.
+__device__ __forceinline__ bool better_key(double ka, int ia, double kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Wave-wide best (key, index) by better_key; the result is uniform.
+__device__ __forceinline__ void wave_argmax(double& key, int& idx) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const double ok = __shfl_xor(key, off);
+    const int oi = __shfl_xor(idx, off);
+    if (better_key(ok, oi, key, idx)) {
+      key = ok;
+      idx = oi;
+    }
+  }
+}
+
+// MODE 0: temperature 0 (argmax); 1: temperature 1; 2: any other temperature.  Returns the
+// chunk's log-mass L_c for MODE > 0 (-inf for a chunk without a finite entry).
 template <int MODE>
-__device__ __forceinline__ void process_chunk(const float (&x)[16], int c, float invT,
-                                              LaneState& st, float* __restrict__ lmass_row) {
+__device__ __forceinline__ float process_chunk(const float (&x)[16], int c, float invT,
+                                               LaneState& st) {
   const int lane = lane_id();
   float lm = x[0];
 #pragma unroll
@@ -99,8 +120,7 @@ __device__ __forceinline__ void process_chunk(const float (&x)[16], int c, float
 #pragma unroll
     for (int i = 0; i < 16; ++i) bad |= (x[i] != x[i]);
     if (wave_any(bad)) st.nan = true;
-    if (MODE != 0 && lane == 0) lmass_row[c] = -INFINITY;
-    return;
+    return -INFINITY;
   }
   float nc = 0.f, sc = 0.f, tc = 0.f, zt = 0.f;
   const float scaleT = kLog2e * invT;
@@ -149,16 +169,19 @@ __device__ __forceinline__ void process_chunk(const float (&x)[16], int c, float
       st.best_i = wave_min_i32(idx);
       st.best_v = mc;
     }
-  } else {
-    const float z = wave_sum(MODE == 1 ? nc + sc : zt);
-    const float L = (MODE == 1 ? mc : mc * invT) + __builtin_amdgcn_logf(z) * kLn2;
-    if (lane == 0) lmass_row[c] = L;
+    return 0.f;
   }
+  const float z = wave_sum(MODE == 1 ? nc + sc : zt);
+  return (MODE == 1 ? mc : mc * invT) + __builtin_amdgcn_logf(z) * kLn2;
 }
 
 // Merge entropy state b into a (a's maximum is the reference when larger).
 __device__ __forceinline__ void merge_state(PartState& a, const PartState& b) {
   a.nan |= b.nan;
+  if (better_key(b.best_key, b.best_c, a.best_key, a.best_c)) {
+    a.best_key = b.best_key;
+    a.best_c = b.best_c;
+  }
   if (b.best_v > a.best_v || (b.best_v == a.best_v && b.best_i < a.best_i)) {
     a.best_v = b.best_v;
     a.best_i = b.best_i;
@@ -193,17 +216,49 @@ __device__ __forceinline__ void merge_state(PartState& a, const PartState& b) {
 
 template <int MODE>
 __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
-    const float* __restrict__ logits, int V, int nC, int S, float invT,
-    const uint8_t* __restrict__ frozen, PartState* __restrict__ part, float* __restrict__ lmass) {
+    const float* __restrict__ logits, int V, int nC, int S, float invT, uint32_t k0,
+    uint32_t k1, uint32_t step, const uint8_t* __restrict__ frozen,
+    PartState* __restrict__ part) {
   const int p = blockIdx.y;
   const int s = blockIdx.x;
   if (frozen != nullptr && frozen[p]) return;
   const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
   const int c_begin = (int)((int64_t)s * nC / S);
   const int c_end = (int)((int64_t)(s + 1) * nC / S);
   const float* __restrict__ row = logits + (size_t)p * V;
-  float* __restrict__ lmass_row = lmass + (size_t)p * nC;
   const bool vec = (V & 3) == 0;
+
+  // Level-1 batch: lane b holds the log-mass of the b-th chunk since the last draw.  A draw
+  // gives each held chunk its key L_c + G_c, G_c from counter (c, p, step, 1) word 0.
+  float bL = -INFINITY;
+  int bC = 0;
+  int nb = 0;
+  double wkey = -INFINITY;
+  int wc = 0x7fffffff;
+  auto draw = [&]() {
+    double key = -INFINITY;
+    int kc = 0x7fffffff;
+    if (lane < nb && bL != -INFINITY) {
+      const Philox4 r = philox4x32_10((uint32_t)bC, (uint32_t)p, step, 1u, k0, k1);
+      key = (double)bL + gumbel_from_word(r.w[0]);
+      kc = bC;
+    }
+    wave_argmax(key, kc);
+    if (better_key(key, kc, wkey, wc)) {
+      wkey = key;
+      wc = kc;
+    }
+    nb = 0;
+  };
+  auto fold = [&](float L, int c) {
+    if (MODE == 0) return;
+    if (lane == nb) {
+      bL = L;
+      bC = c;
+    }
+    if (++nb == kWave) draw();
+  };
 
   LaneState st;
   st.m = -INFINITY;
@@ -224,15 +279,19 @@ __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
     for (int r = 0; r < kRing; ++r) {
       const int c = base + r * kStreamWaves;
       if (c < c_end) {
-        process_chunk<MODE>(x[r], c, invT, st, lmass_row);
+        fold(process_chunk<MODE>(x[r], c, invT, st), c);
         const int cn = c + kRing * kStreamWaves;
         if (cn < c_end) load_chunk(row, V, cn, vec, x[r]);
       }
     }
   }
 
+  if (MODE != 0 && nb > 0) draw();
+
   // Lanes share the reference maximum: the wave state is a plain sum.
   PartState ws;
+  ws.best_key = wkey;
+  ws.best_c = wc;
   ws.m = st.m;
   ws.n = wave_sum(st.n);
   ws.s = wave_sum(st.s);
@@ -257,22 +316,9 @@ constexpr int kFinishThreads = 256;
 constexpr int kFinishWaves = kFinishThreads / kWave;
 constexpr int kMaxSplits = BD_SAMPLE_BLOCKS;  // sample_split_count never exceeds this
 
-__device__ __forceinline__ bool better_key(double ka, int ia, double kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
-}
-
-// Block-wide argmax of (key, index): larger key, then lower index.  The order is total, so
-// the result does not depend on the reduction order.  Uniform result; one barrier.
+// Block-wide argmax of (key, index) by better_key; uniform result, one barrier.
 __device__ __forceinline__ void block_argmax(double& key, int& idx, double* wkey, int* widx) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const double ok = __shfl_xor(key, off);
-    const int oi = __shfl_xor(idx, off);
-    if (better_key(ok, oi, key, idx)) {
-      key = ok;
-      idx = oi;
-    }
-  }
+  wave_argmax(key, idx);
   const int wave = threadIdx.x / kWave;
   if (lane_id() == 0) {
     wkey[wave] = key;
@@ -289,13 +335,32 @@ __device__ __forceinline__ void block_argmax(double& key, int& idx, double* wkey
     }
 }
 
-// One block per row.  Every load the row needs before its level-2 draw is issued at entry:
-// the V-split states (merged by one lane in split order) and the chunk log-masses with their
-// level-1 noise.  Level 2 then re-reads the winning chunk only.
+// Standard Gumbel draw from one Philox word in fp32, for the level-2 pre-selection only.
+// u = ((r >> 8) + 0.5) 2^-24; w = -ln u is formed without cancellation: from u itself when
+// u < 1/2 (exact in fp32), else as -log1p(-(1 - u)) with 1 - u = (2^24 - 1 - (r >> 8) + 0.5)
+// 2^-24 (exact in fp32).  g = -ln w.  With logf and log1pf within 2 ulp, |g - g_exact| is
+// below 2^-21 + 2^-22, and w >= 2^-25 never reaches the fp32 subnormals.
+__device__ __forceinline__ float gumbel32_from_word(uint32_t r) {
+  const uint32_t k = r >> 8;
+  float w;
+  if (k < (1u << 23)) {
+    w = -logf(((float)k + 0.5f) * 0x1p-24f);
+  } else {
+    const uint32_t m = (1u << 24) - 1u - k;
+    w = -log1pf(-(((float)m + 0.5f) * 0x1p-24f));
+  }
+  return -logf(w);
+}
+
+// One block per row.  The V-split states carry the entropy sums, the temperature-0 argmax and
+// each split's best level-1 key; one lane merges them in split order.  Level 2 re-reads the
+// winning chunk.  Its scores x_v / T + g_v are first formed in fp32 (error below
+// 1.2e-5 + 2.4e-7 |score|); when a single entry is within the margin of the fp32 maximum it is
+// the fp64 argmax, otherwise the entries within the margin are scored again in fp64 (the
+// definition) and the fp64 argmax decides.
 __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
-    const float* __restrict__ logits, int V, int nC, int S, float temperature, uint32_t k0,
-    uint32_t k1, uint32_t step, const uint8_t* __restrict__ frozen,
-    const PartState* __restrict__ part, const float* __restrict__ lmass,
+    const float* __restrict__ logits, int V, int S, float temperature, uint32_t k0, uint32_t k1,
+    uint32_t step, const uint8_t* __restrict__ frozen, const PartState* __restrict__ part,
     int32_t* __restrict__ tokens_out, float* __restrict__ entropy_out,
     float* __restrict__ conf_out) {
   const int p = blockIdx.x;
@@ -309,27 +374,13 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     return;
   }
   __shared__ PartState sp[kMaxSplits];
-  __shared__ double wkey[2][kFinishWaves];
-  __shared__ int widx[2][kFinishWaves];
-  __shared__ int sValid, sArg;
+  __shared__ double wkey[kFinishWaves];
+  __shared__ int widx[kFinishWaves];
+  __shared__ float wmax[kFinishWaves];
+  __shared__ int sValid, sChunk;
   for (int s = tid; s < S; s += kFinishThreads) sp[s] = part[(size_t)p * S + s];
-  const bool sampled = temperature != 0.f;
-  // Level 1: chunk keys K_c = L_c + G_c, G_c from counter (c, p, step, 1) word 0.
-  double best = -INFINITY;
-  int bestc = 0x7fffffff;
-  if (sampled) {
-    for (int c = tid; c < nC; c += kFinishThreads) {
-      const float L = lmass[(size_t)p * nC + c];
-      if (L == -INFINITY) continue;
-      const Philox4 r = philox4x32_10((uint32_t)c, (uint32_t)p, step, 1u, k0, k1);
-      const double key = (double)L + gumbel_from_word(r.w[0]);
-      if (better_key(key, c, best, bestc)) {
-        best = key;
-        bestc = c;
-      }
-    }
-  }
   __syncthreads();
+  const bool sampled = temperature != 0.f;
   if (tid == 0) {
     PartState acc = sp[0];
     for (int s = 1; s < S; ++s) merge_state(acc, sp[s]);
@@ -343,40 +394,73 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
       valid = !(H != H);
     }
     sValid = valid ? 1 : 0;
-    sArg = acc.best_i;
+    sChunk = acc.best_c;
     if (entropy_out != nullptr) entropy_out[p] = valid ? H : NAN;
     if (conf_out != nullptr) conf_out[p] = valid ? conf : NAN;
     if (!valid) tokens_out[p] = -1;
     else if (!sampled) tokens_out[p] = acc.best_i;
   }
   if (!sampled) return;
-  block_argmax(best, bestc, wkey[0], widx[0]);  // its barrier also publishes sValid
+  __syncthreads();
   if (!sValid) return;
   // Level 2: inside chunk bestc, maximise x_v / T + g_v, g_v from (v >> 2, p, step, 0).
+  const int bestc = sChunk;
+  if (bestc < 0 || bestc >= (V + kChunk - 1) / kChunk) {  // no chunk had a comparable key
+    if (tid == 0) tokens_out[p] = -1;
+    return;
+  }
   const int v0 = bestc * kChunk + 4 * tid;
   const int vend = min(V, (bestc + 1) * kChunk);
-  double sbest = -INFINITY;
-  int sv = 0x7fffffff;
+  float xv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float s32[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  Philox4 r = {};
+  float lmax = -INFINITY;
   if (v0 < vend) {
     const float* row = logits + (size_t)p * V;
-    float xv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) xv[q] = v0 + q < vend ? row[v0 + q] : -INFINITY;
-    const Philox4 r = philox4x32_10((uint32_t)(v0 >> 2), (uint32_t)p, step, 0u, k0, k1);
-    const double T = (double)temperature;
+    r = philox4x32_10((uint32_t)(v0 >> 2), (uint32_t)p, step, 0u, k0, k1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int v = v0 + q;
-      if (v < vend) {
-        const double sc = (double)xv[q] / T + gumbel_from_word(r.w[q]);
-        if (better_key(sc, v, sbest, sv)) {
-          sbest = sc;
-          sv = v;
-        }
+      if (v0 + q < vend) {
+        s32[q] = xv[q] / temperature + gumbel32_from_word(r.w[q]);
+        lmax = fmaxf(lmax, s32[q]);
       }
     }
   }
-  block_argmax(sbest, sv, wkey[1], widx[1]);
+  float m = wave_max(lmax);
+  if (lane_id() == 0) wmax[tid / kWave] = m;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kFinishWaves; ++w) m = fmaxf(m, wmax[w]);
+  // Entries that may still be the fp64 argmax: within twice the fp32 error bound of the
+  // maximum (all entries when the fp32 maximum is not finite).
+  const bool all = !(fabsf(m) < 1e30f);
+  const float margin = 2e-4f + 2e-6f * fabsf(m);
+  int mask = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (v0 + q < vend && (all || s32[q] >= m - margin)) mask |= 1 << q;
+  const int holders = __syncthreads_count(mask != 0);
+  const int multi = __syncthreads_count(__builtin_popcount(mask) > 1);
+  if (holders == 1 && multi == 0) {
+    if (mask != 0) tokens_out[p] = v0 + __builtin_ctz(mask);
+    return;
+  }
+  double sbest = -INFINITY;
+  int sv = 0x7fffffff;
+  const double T = (double)temperature;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (mask & (1 << q)) {
+      const double sc = (double)xv[q] / T + gumbel_from_word(r.w[q]);
+      if (better_key(sc, v0 + q, sbest, sv)) {
+        sbest = sc;
+        sv = v0 + q;
+      }
+    }
+  }
+  block_argmax(sbest, sv, wkey, widx);
   if (tid == 0) tokens_out[p] = sv;
 }
 
@@ -585,31 +669,28 @@ hipError_t launch_sample_entropy(const float* logits, int P, int V, float temper
   const int nC = (V + kChunk - 1) / kChunk;
   const int S = sample_split_count(P, V);
   PartState* part = reinterpret_cast<PartState*>(workspace);
-  float* lmass = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                          align_up((size_t)P * S * sizeof(PartState)));
   const dim3 grid(S, P);
   const float invT = temperature > 0.f ? 1.f / temperature : 0.f;
+  const uint32_t k0 = (uint32_t)(seed & 0xffffffffu), k1 = (uint32_t)(seed >> 32);
   if (temperature == 0.f)
     hipLaunchKernelGGL(sample_stream_kernel<0>, grid, dim3(kStreamThreads), 0, stream, logits, V,
-                       nC, S, invT, frozen, part, lmass);
+                       nC, S, invT, k0, k1, step, frozen, part);
   else if (temperature == 1.f)
     hipLaunchKernelGGL(sample_stream_kernel<1>, grid, dim3(kStreamThreads), 0, stream, logits, V,
-                       nC, S, invT, frozen, part, lmass);
+                       nC, S, invT, k0, k1, step, frozen, part);
   else
     hipLaunchKernelGGL(sample_stream_kernel<2>, grid, dim3(kStreamThreads), 0, stream, logits, V,
-                       nC, S, invT, frozen, part, lmass);
+                       nC, S, invT, k0, k1, step, frozen, part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(sample_finish_kernel, dim3(P), dim3(kFinishThreads), 0, stream, logits, V, nC,
-                     S, temperature, (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32), step,
-                     frozen, part, lmass, tokens_out, entropy_out, conf_out);
+  hipLaunchKernelGGL(sample_finish_kernel, dim3(P), dim3(kFinishThreads), 0, stream, logits, V, S,
+                     temperature, k0, k1, step, frozen, part, tokens_out, entropy_out, conf_out);
   return hipGetLastError();
 }
 
 size_t sample_workspace_bytes(int P, int V) {
-  const int nC = (V + kChunk - 1) / kChunk;
   const int S = sample_split_count(P, V);
-  return align_up((size_t)P * S * sizeof(PartState)) + align_up((size_t)P * nC * sizeof(float));
+  return align_up((size_t)P * S * sizeof(PartState));
 }
 
 hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, float bound,

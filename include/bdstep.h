@@ -281,7 +281,7 @@ size_t bd_sample_workspace_size(int P, int V);
  *   frozen       uint8 [P] or NULL (none frozen).  Frozen rows are not read; they get
  *                tokens_out = -1 and entropy_out = +inf.
  *   A row containing NaN or +inf, or only -inf, gets entropy NaN and token -1.
- *   temperature  >= 0 and finite
+ *   temperature  0, or positive with 1/temperature finite in fp32 (>= about 2.9e-39)
  *   P in 1..BD_MAX_POSITIONS, V in 1..BD_MAX_VOCAB.  V % 4 == 0 takes the vector path;
  *   other V are handled, more slowly.
  */

@@ -110,7 +110,7 @@ def test_combine_validation(lib):
 def test_sampler_validation(lib):
     P = ctypes.c_void_p(0x1000)
     n = lib.bd_sample_workspace_size(256, 262144)
-    assert n >= 256 * 256 * 4
+    assert n >= 256 * 40          # one 40-byte partial state per split and row
     assert lib.bd_sample_workspace_size(0, 10) == 0
     assert lib.bd_sample_workspace_size(1025, 10) == 0
     assert lib.bd_sample_workspace_size(10, (1 << 24) + 1) == 0
@@ -118,6 +118,7 @@ def test_sampler_validation(lib):
     assert call(P, 256, 262144, -1.0, 0, 0, None, P, P, P, n, None) == 2
     assert call(P, 256, 262144, float("nan"), 0, 0, None, P, P, P, n, None) == 2
     assert call(P, 256, 262144, float("inf"), 0, 0, None, P, P, P, n, None) == 2
+    assert call(P, 256, 262144, 1e-45, 0, 0, None, P, P, P, n, None) == 2   # 1/T overflows
     assert call(P, 256, 262144, 1.0, 0, 0, None, P, P, P, n - 1, None) == 4
     assert call(None, 256, 262144, 1.0, 0, 0, None, P, P, P, n, None) == 1
     assert call(ctypes.c_void_p(0x1004), 256, 262144, 1.0, 0, 0, None, P, P, P, n, None) == 3
