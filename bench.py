@@ -48,6 +48,8 @@ def parse():
                     help="stack (default): the whole denoising step; layer: one FFN layer at the "
                          "256-token canvas with uniform routing; sampler: the sampler alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true",
+                    help="skip the one-launch-at-a-time part timings (e.g. for counter runs)")
     return ap.parse_args()
 
 
@@ -496,8 +498,10 @@ def main():
                       dtype=np.float64)
     gu_gbs = gu_alg.sum() / (gu_ms.sum() * 1e-3) / 1e9
     traffic = measured_traffic(float(gu_alg.mean()))
-    log("timing the parts one launch at a time")
-    parts = components(bd, workloads, layers, x, logits, sshape, ws, sws)
+    parts = None
+    if not args.no_components:
+        log("timing the parts one launch at a time")
+        parts = components(bd, workloads, layers, x, logits, sshape, ws, sws)
 
     result = {
         "metric": "denoising-step MoE+sampler latency (ms) and achieved HBM GB/s vs peak, 1 GPU",
@@ -520,7 +524,7 @@ def main():
             "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
             "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
             "step_algorithmic_bytes": int(step_bytes),
-            "components": parts,
+            **({"components": parts} if parts is not None else {}),
         },
         "roofline": {
             "kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22>)",
