@@ -146,3 +146,15 @@ def test_drafts_off_and_finished_block_is_left_alone(bd):
     torch.cuda.synchronize()
     assert np.array_equal(canvas.cpu().numpy(), np.arange(P))
     assert list(state.cpu().numpy()) == [2, 2, 1, 0]
+
+
+def test_full_size_block_in_lockstep(bd):
+    """The sampler workload's logits ([256, 262144], T = 1, bound 2.0) driven for six steps
+    (the budget), every step checked against the oracle: masks, canvas, frozen set, state."""
+    from block_diffusion_lm_router_amd import workloads
+    shape = workloads.SAMPLER
+    x = workloads.make_logits(shape)
+    say("loop: full-size block", x.shape)
+    steps, excused = run_block(bd, lambda s: x, shape.temperature, "entropy", shape.bound,
+                               threshold=3, max_steps=6, seed=shape.seed)
+    assert steps == 6 and excused <= 3
