@@ -138,7 +138,16 @@ def test_sampler_validation(lib):
 
 
 def test_confidence_sampler_validation(lib):
+    import json
+    opts = json.load(open(os.path.join(ROOT, "tests", "golden", "diffusion_options.json")))
+    lo, hi = opts["confidence_threshold_range"]
     P = ctypes.c_void_p(0x1000)
+    acc = lib.diffusion_accept_confidence
+    # the documented range is accepted at both ends (the call then fails only on P = 0)
+    assert acc(P, P, 0, lo, None, None, P, P, None) == 2
+    assert acc(None, P, 8, lo, None, None, P, P, None) == 1
+    assert acc(None, P, 8, hi, None, None, P, P, None) == 1
+    assert acc(None, P, 8, opts["confidence_threshold_default"], None, None, P, P, None) == 1
     n = lib.bd_sample_workspace_size(256, 262144)
     call = lib.diffusion_sample_confidence
     assert call(P, 256, 262144, -1.0, 0, 0, None, P, None, P, P, n, None) == 2

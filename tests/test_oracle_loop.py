@@ -1,5 +1,8 @@
 """Pins of the denoising-loop driver oracle (oracle/loop.py); no GPU."""
 
+import json
+import os
+
 import numpy as np
 import pytest
 from scipy import stats
@@ -8,12 +11,17 @@ from oracle import loop
 from oracle.philox import philox4x32, seed_key
 
 
+OPTIONS = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "diffusion_options.json")))
+
+
 @pytest.mark.parametrize("remaining,expect", [(0, 64), (12, 64), (64, 64), (65, 65), (200, 200),
                                               (256, 256), (257, 256), (10000, 256)])
 def test_canvas_length_with_the_documented_defaults(remaining, expect):
-    # minimum 64 and maximum 256 are the documented defaults
-    assert loop.canvas_length(256, 64, remaining) == expect
-    assert loop.canvas_length(256, 64, remaining, full_canvas=True) == 256
+    # the page's defaults: minimum canvas 64, maximum (the model's canvas) typically 256
+    lo, hi = OPTIONS["min_canvas_default"], OPTIONS["max_canvas_typical"]
+    assert (lo, hi) == (64, 256)
+    assert loop.canvas_length(hi, lo, remaining) == expect
+    assert loop.canvas_length(hi, lo, remaining, full_canvas=True) == hi
 
 
 def test_init_canvas_mapping_edges_and_range():

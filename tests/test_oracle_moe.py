@@ -217,11 +217,17 @@ def test_group_128_equals_group_64_with_each_pair_sharing_scale_and_zero():
 
 
 def test_checkpoint_format_groups_per_matrix():
-    """gate_up at g = 128 and down at g = 64 (the model card's checkpoint format): the
-    expert matrices come from each matrix's own group size, checked against scalar loops."""
+    """gate_up at g = 128 and down at g = 64 (the model card's checkpoint format, from the
+    page-figures fixture): the expert matrices come from each matrix's own group size, checked
+    against scalar loops."""
+    import json
+    import os
     from block_diffusion_lm_router_amd import workloads
+    figs = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+    assert (figs["gate_up_group"], figs["down_group"]) == (128, 64)
     shape = workloads.LayerShape(4, 256, 128, 3, 2)
-    w = workloads.make_weights(shape, 0, gate_up_group=128, down_group=64)
+    w = workloads.make_weights(shape, 0, gate_up_group=figs["gate_up_group"],
+                               down_group=figs["down_group"])
     assert w["gate_up_scale"].shape == (3, 256, 2) and w["down_scale"].shape == (3, 256, 2)
     wg, wu, wd = moe.expert_matrices(w, 1, 128, 64)
     q = moe.unpack_nibbles(w["gate_up_q"][1])
