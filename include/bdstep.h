@@ -398,8 +398,8 @@ int diffusion_canvas_init(int32_t* canvas, int32_t* prev_canvas, uint8_t* frozen
  * takes the canvas; steps += 1; the unchanged count is reset on any change, else
  * incremented; done = unchanged >= stability_threshold, or every position frozen, or
  * steps >= max_steps.
- * Source: DiffusionGemma block-diffusion page, "How it works" (the model refines the whole
- * block each step; the stable-and-confident early stop after stability_threshold unchanged
+ * Source: DiffusionGemma block-diffusion page, "How it works" (the whole canvas is updated
+ * at every step; the early stop once the canvas has not changed for stability_threshold
  * steps; the step budget).
  *   tokens  int32 [P] (may be NULL if write_drafts == 0); canvas, prev_canvas int32 [P];
  *   frozen  uint8 [P] (after the step's acceptance); loop_state int32 [4] in/out.

@@ -19,7 +19,8 @@ Readings taken where the pages are silent (each listed in the design doc):
   (p, b, 0, 2), word 0, mapped to [0, vocab) as floor(word * vocab / 2^32);
 * after each step the canvas holds every sampled position's draft token (the sampler
   itself writes only accepted positions; the driver then writes the drafts of the others),
-  so "the model refines the whole block each step"; frozen positions keep their token;
+  so the whole canvas is updated at every step, as the page describes; frozen positions
+  keep their token;
 * "unchanged" compares the whole canvas with the canvas before the step; the stable count
   is the number of consecutive unchanged steps;
 * the block ends when the stable count reaches the threshold, when every position is
