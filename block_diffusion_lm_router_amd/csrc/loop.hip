@@ -1,9 +1,9 @@
 // Denoising-loop driver kernels around the per-step sampler: the random initial canvas of a
 // block and the per-step stability update that ends a block early.
 //
-// Source: DiffusionGemma block-diffusion page, "How it works" (a block's canvas starts as
-// seeded uniformly random token ids; after each step the early stop checks whether the canvas
-// has been unchanged for stability_threshold consecutive steps), "CLI flags" (step budget).
+// Source: DiffusionGemma block-diffusion page, "How it works" (the canvas starts from seeded
+// random ids; a block ends early once its canvas has stayed the same for stability_threshold
+// steps in a row), "CLI flags" (step budget).
 //
 // Both kernels keep the driver's state on the device (int32 [4]: steps run, consecutive
 // unchanged steps, done, frozen count) so a host loop needs no synchronisation to advance

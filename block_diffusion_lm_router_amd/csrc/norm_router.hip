@@ -1,9 +1,9 @@
 // The two steps either side of the expert FFN's routing: the fused RMS norm that produces the
 // FFN input, and the router projection whose fp32 logits feed the top-k.
 //
-// Sources: axe-diffusion-ksl-xe model card, "the kernels we built" (the RMS norm as one
-// launch instead of about six elementwise ones, 180 times per forward pass); "what the model
-// is" (128 experts scored per token, top-8 kept).
+// Sources: axe-diffusion-ksl-xe model card, "the kernels we built" (one fused launch for the
+// RMS norm in place of about six element-wise ones; the norm runs 180 times in a forward
+// pass); "what the model is" (128 experts scored per token, top-8 kept).
 //
 // RMS norm.  One wave per row, four rows per 256-thread block.  A row of d <= 4096 halves is
 // at most eight 16-byte vectors per lane: the wave loads the row once into registers, sums

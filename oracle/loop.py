@@ -3,13 +3,12 @@ block, the random initial canvas, and the per-step stability update that ends a 
 
 Passages followed (pages named in the package docstring):
 
-* Block-diffusion generation (DiffusionGemma), "How it works": a block's canvas starts as
-  uniformly random token ids (seeded) and has length min(max_canvas, max(remaining,
-  min_canvas)); up to the step budget of denoising steps run; after each step an early stop
-  checks whether the canvas has been unchanged for stability_threshold consecutive steps,
-  and if so the block is committed.
+* Block-diffusion generation (DiffusionGemma), "How it works": the canvas of a block is
+  drawn at random from the vocabulary with a seed, its length is min(max_canvas,
+  max(remaining, min_canvas)), at most the step budget of steps run, and the block ends early
+  once the canvas has stayed the same for stability_threshold steps in a row.
 * same, "CLI flags": the minimum canvas (64) and the maximum canvas (the model's canvas
-  length, typically 256), the option to always use the full canvas, the step budget
+  length, 256 for the model described), the option to always use the full canvas, the step budget
   (typically 48).
 * same, "Reproducibility": the seed fixes the canvas initialisation.
 
