@@ -13,7 +13,12 @@ Two modes:
                way on the copy.
            The per-dispatch mean of every kernel the entry point launches is summed.
 
+  counters per-kernel means of any counters (raw or derived, e.g. MfmaUtil, VALUBusy) from a
+           `rocprofv3 --pmc ...` run, one line per kernel pattern.
+
 Usage:
+  python -m block_diffusion_lm_router_amd.profsum counters --csv X_counter_collection.csv \
+      --kernel NAME=REGEX [--kernel NAME=REGEX ...] --command "..." --out profiles/NAME.txt
   python -m block_diffusion_lm_router_amd.profsum stats --csv X_kernel_stats.csv \
       --command "..." --out profiles/NAME.txt
   python -m block_diffusion_lm_router_amd.profsum traffic --fetch A.csv --write B.csv \
@@ -67,6 +72,33 @@ def stats(args):
                    f"{float(r['MaxNs']) / 1e3:>9.2f} {100 * float(r['TotalDurationNs']) / total:>6.2f}"
                    f"  {_short(r['Name'])}")
     out.append(f"\nall kernels: {total / 1e3:.1f} us over {sum(int(r['Calls']) for r in rows)} calls")
+    text = "\n".join(out) + "\n"
+    with open(args.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def counters(args):
+    """Mean of every counter per kernel pattern (the first pattern that matches a kernel name)."""
+    pats = [kv.split("=", 1) for kv in args.kernel]
+    vals = {}
+    for r in _rows(args.csv):
+        for name, rx in pats:
+            if re.search(rx, r["Kernel_Name"]):
+                d = vals.setdefault(name, {}).setdefault(r["Counter_Name"], {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+                break
+    names = sorted({c for per in vals.values() for c in per})
+    out = [f"command: {args.command}", "",
+           f"{'kernel':<16} {'dispatches':>10} " + " ".join(f"{c:>14}" for c in names)]
+    for name, _ in pats:
+        per = vals.get(name, {})
+        n = max((len(d) for d in per.values()), default=0)
+        cells = []
+        for c in names:
+            d = per.get(c, {})
+            cells.append(f"{sum(d.values()) / len(d):>14.2f}" if d else f"{'-':>14}")
+        out.append(f"{name:<16} {n:>10} " + " ".join(cells))
     text = "\n".join(out) + "\n"
     with open(args.out, "w") as f:
         f.write(text)
@@ -148,6 +180,11 @@ def main():
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--top", type=int, default=20)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--kernel", action="append", required=True, help="NAME=REGEX")
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write", "command", "out", "entry"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
@@ -156,7 +193,7 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--kernel", action="append", required=True)
     args = ap.parse_args()
-    (stats if args.mode == "stats" else traffic)(args)
+    {"stats": stats, "traffic": traffic, "counters": counters}[args.mode](args)
 
 
 if __name__ == "__main__":
