@@ -76,7 +76,8 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int V,
 
 struct LaneState {
   float m;  // wave-uniform running maximum
-  float n, s, t;
+  float n;  // wave-uniform count of entries equal to m (the whole wave's)
+  float s, t;  // per-lane sums
   float best_v;  // temperature-0 argmax (wave-uniform)
   int best_i;
   bool nan;      // NaN seen in a chunk with no finite entry (wave-uniform)
@@ -118,7 +119,8 @@ __device__ __forceinline__ float process_chunk(const float (&x)[16], int c, floa
     if (wave_any(bad)) st.nan = true;
     return -INFINITY;
   }
-  float nc = 0.f, sc = 0.f, tc = 0.f, zt = 0.f;
+  float sc = 0.f, tc = 0.f, zt = 0.f;
+  int at_max = 0;  // wave-wide count of the chunk's entries equal to mc (scalar popcounts)
   const float scaleT = kLog2e * invT;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -126,10 +128,13 @@ __device__ __forceinline__ float process_chunk(const float (&x)[16], int c, floa
     const float e = __builtin_amdgcn_exp2f(d * kLog2e);
     const bool off_max = d != 0.f;  // true for NaN as well, which then poisons s
     sc += off_max ? e : 0.f;
-    nc += off_max ? 0.f : 1.f;
+    at_max += __popcll(__ballot(!off_max));
     tc = fmaf(e, fmaxf(d, -200.f), tc);
     if (MODE == 2) zt += __builtin_amdgcn_exp2f(d * scaleT);
   }
+  const float nc = (float)at_max;
+  // The maximal entries count once for the wave: lane 0 carries them in the per-lane sums.
+  const float nl = lane == 0 ? st.n : 0.f;
   // Fold the chunk into the running per-lane state (branches are wave-uniform).
   if (mc > st.m) {
     if (st.m == -INFINITY) {
@@ -139,8 +144,8 @@ __device__ __forceinline__ float process_chunk(const float (&x)[16], int c, floa
     } else {
       const float delta = st.m - mc;
       const float r = __builtin_amdgcn_exp2f(delta * kLog2e);
-      st.t = fmaf(r, fmaf(delta, st.n + st.s, st.t), tc);
-      st.s = fmaf(r, st.s + st.n, sc);
+      st.t = fmaf(r, fmaf(delta, st.s + nl, st.t), tc);
+      st.s = fmaf(r, st.s + nl, sc);
       st.n = nc;
     }
     st.m = mc;
@@ -151,7 +156,7 @@ __device__ __forceinline__ float process_chunk(const float (&x)[16], int c, floa
   } else {
     const float delta = mc - st.m;
     const float r = __builtin_amdgcn_exp2f(delta * kLog2e);
-    const float zc = nc + sc;
+    const float zc = (lane == 0 ? nc : 0.f) + sc;
     st.t = fmaf(r, fmaf(delta, zc, tc), st.t);
     st.s = fmaf(r, zc, st.s);
   }
@@ -167,7 +172,7 @@ __device__ __forceinline__ float process_chunk(const float (&x)[16], int c, floa
     }
     return 0.f;
   }
-  const float z = wave_sum(MODE == 1 ? nc + sc : zt);
+  const float z = MODE == 1 ? nc + wave_sum(sc) : wave_sum(zt);
   return (MODE == 1 ? mc : mc * invT) + __builtin_amdgcn_logf(z) * kLn2;
 }
 
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
   ws.best_key = wkey;
   ws.best_c = wc;
   ws.m = st.m;
-  ws.n = wave_sum(st.n);
+  ws.n = st.n;
   ws.s = wave_sum(st.s);
   ws.t = wave_sum(st.t);
   ws.best_v = st.best_v;
