@@ -76,6 +76,7 @@ SEED_LOGITS = 5
 SEED_WEIGHTS = 100
 SEED_HIDDEN = 6
 SEED_NORM_ROUTER = 200
+SEED_AFFINE = 300
 
 
 def _rng(seed):
@@ -97,20 +98,29 @@ def _zeros(rng, shape):
     return (_random_bytes(rng, shape) & 0x0F).astype(np.float16)
 
 
+def _biases(rng, scales):
+    """Affine biases b = -z' s with a continuous z' ~ U[0, 15] (so b / s is not an integer),
+    rounded to fp16: the same range as the asymmetric form's -z s."""
+    zc = rng.random(scales.shape, dtype=np.float32) * np.float32(15.0)
+    return (-(zc * scales.astype(np.float32))).astype(np.float16)
+
+
 def make_weights(shape: LayerShape, layer: int = 0, gate_up_group: int = None,
-                 down_group: int = None):
+                 down_group: int = None, affine: bool = False):
     """Packed uint4 expert weights of one layer (seed 100 + layer).
 
     Layout (see include/bdstep.h): gate_up_q [E][2f][d/2] (gate rows first),
     gate_up_scale / gate_up_zero fp16 [E][2f][d/g]; down_q [E][d][f/2],
     down_scale / down_zero fp16 [E][d][f/g_down].  The group sizes default to shape.group;
     gate_up_group=128 with down_group=64 is the format of the model card's checkpoint.
+    affine=True puts affine biases (seed 300 + layer) in the *_zero arrays instead of
+    zero-points.
     """
     E, d, f = shape.experts, shape.d_model, shape.d_ff
     g = gate_up_group or shape.group
     gd = down_group or shape.group
     rng = _rng(SEED_WEIGHTS + layer)
-    return {
+    w = {
         "gate_up_q": _random_bytes(rng, (E, 2 * f, d // 2)),
         "gate_up_scale": _scales(rng, (E, 2 * f, d // g)),
         "gate_up_zero": _zeros(rng, (E, 2 * f, d // g)),
@@ -118,6 +128,11 @@ def make_weights(shape: LayerShape, layer: int = 0, gate_up_group: int = None,
         "down_scale": _scales(rng, (E, d, f // gd)),
         "down_zero": _zeros(rng, (E, d, f // gd)),
     }
+    if affine:
+        brng = _rng(SEED_AFFINE + layer)
+        w["gate_up_zero"] = _biases(brng, w["gate_up_scale"])
+        w["down_zero"] = _biases(brng, w["down_scale"])
+    return w
 
 
 def make_activations(shape: LayerShape, seed: int = SEED_X):

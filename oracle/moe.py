@@ -55,6 +55,19 @@ def dequant(packed, scale, zero, group=GROUP):
     return (q - z) * s
 
 
+def dequant_affine(packed, scale, bias, group=GROUP):
+    """Affine form: w[n, k] = q[n, k] * s[n, k // g] + b[n, k // g] (exact in float64).
+
+    The MLX-style 4-bit checkpoints (a 4/64 affine format named on the TensorFold XPU page)
+    store a free fp16 bias per group instead of an integer zero-point; b = -z * s gives back
+    the asymmetric form.
+    """
+    q = unpack_nibbles(packed).astype(np.float64)
+    s = np.repeat(np.asarray(scale, dtype=np.float16).astype(np.float64), group, axis=-1)
+    b = np.repeat(np.asarray(bias, dtype=np.float16).astype(np.float64), group, axis=-1)
+    return q * s + b
+
+
 def route_topk(router_logits, k):
     """Top-k experts per token and their softmax weights.
 
@@ -80,20 +93,22 @@ def gelu_tanh(a):
     return 0.5 * a * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (a + 0.044715 * a ** 3)))
 
 
-def expert_matrices(weights, e, group=GROUP, down_group=None):
+def expert_matrices(weights, e, group=GROUP, down_group=None, affine=False):
     """Dense float64 gate, up and down matrices of expert ``e``.
 
     ``weights`` maps the names gate_up_q, gate_up_scale, gate_up_zero, down_q,
     down_scale, down_zero to arrays laid out [E][rows][...] as in the C header.
     ``group`` is the gate/up group size, ``down_group`` the down one (None: the same);
     the checkpoint format on the model card's "requirements" groups gate_up at 128 and
-    down at 64.  Returns (W_gate [f, d], W_up [f, d], W_down [d, f]).
+    down at 64.  With ``affine`` the *_zero arrays hold the affine bias b instead of a
+    zero-point (w = q s + b).  Returns (W_gate [f, d], W_up [f, d], W_down [d, f]).
     """
-    gu = dequant(weights["gate_up_q"][e], weights["gate_up_scale"][e],
-                 weights["gate_up_zero"][e], group)
+    deq = dequant_affine if affine else dequant
+    gu = deq(weights["gate_up_q"][e], weights["gate_up_scale"][e],
+             weights["gate_up_zero"][e], group)
     f = gu.shape[0] // 2
-    wd = dequant(weights["down_q"][e], weights["down_scale"][e],
-                 weights["down_zero"][e], group if down_group is None else down_group)
+    wd = deq(weights["down_q"][e], weights["down_scale"][e],
+             weights["down_zero"][e], group if down_group is None else down_group)
     return gu[:f], gu[f:], wd
 
 
@@ -105,7 +120,8 @@ def expert_ffn(x_rows, w_gate, w_up, w_down):
     return (gelu_tanh(a) * u) @ w_down.T
 
 
-def moe_expert_outputs(x, ids, weights, group=GROUP, tokens=None, down_group=None):
+def moe_expert_outputs(x, ids, weights, group=GROUP, tokens=None, down_group=None,
+                       affine=False):
     """Per-assignment expert outputs o[t, j] = FFN_{ids[t, j]}(x[t]).
 
     ``x`` fp16 [T, d]; returns float64 [T, k, d].  With ``tokens`` given, only
@@ -120,7 +136,7 @@ def moe_expert_outputs(x, ids, weights, group=GROUP, tokens=None, down_group=Non
     mask[rows] = True
     for e in np.unique(ids[rows]):
         tt, jj = np.nonzero((ids == e) & mask[:, None])
-        w_gate, w_up, w_down = expert_matrices(weights, int(e), group, down_group)
+        w_gate, w_up, w_down = expert_matrices(weights, int(e), group, down_group, affine)
         out[tt, jj] = expert_ffn(x64[tt], w_gate, w_up, w_down)
     return out
 
@@ -135,11 +151,12 @@ def combine(expert_out, topk_weights):
     return y
 
 
-def moe_ffn(x, router_logits, weights, k, group=GROUP, tokens=None, down_group=None):
+def moe_ffn(x, router_logits, weights, k, group=GROUP, tokens=None, down_group=None,
+            affine=False):
     """The whole layer: route, run the selected experts, combine.
 
     Returns (ids, topk_weights, expert_out [T, k, d], y [T, d]) in float64.
     """
     ids, tw = route_topk(router_logits, k)
-    o = moe_expert_outputs(x, ids, weights, group, tokens, down_group)
+    o = moe_expert_outputs(x, ids, weights, group, tokens, down_group, affine)
     return ids, tw, o, combine(o, tw)

@@ -240,3 +240,45 @@ def test_checkpoint_format_groups_per_matrix():
     for n, col in ((0, 0), (77, 127), (255, 64)):
         g = col // 64
         assert wd[n, col] == (qd[n, col] - float(w["down_zero"][1, n, g])) * float(w["down_scale"][1, n, g])
+
+
+# ---------------------------------------------------------------- affine (MLX-style) form
+
+
+def test_affine_dequant_closed_form_all_codes():
+    """w = q s + b for every 4-bit code q, against a table written out per code."""
+    s = np.float16(0.0137)
+    b = np.float16(-0.0911)
+    packed = np.array([[(2 * i) | ((2 * i + 1) << 4) for i in range(8)] * 8], dtype=np.uint8)
+    w = moe.dequant_affine(packed, np.full((1, 2), s), np.full((1, 2), b), 64)
+    codes = list(range(16)) * 8
+    assert w.shape == (1, 128)
+    for k, q in enumerate(codes):
+        assert w[0, k] == q * float(s) + float(b)
+
+
+def test_affine_with_bias_minus_z_s_is_the_asymmetric_form():
+    """b = -z s (exact in fp16 for these s, z) turns the affine form into (q - z) s."""
+    rng = np.random.default_rng(41)
+    N, K = 5, 256
+    packed = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    s = (np.float16(2.0) ** -rng.integers(5, 9, (N, K // 64))).astype(np.float16)  # powers of 2
+    z = rng.integers(0, 16, (N, K // 64)).astype(np.float16)
+    b = (-(z.astype(np.float64) * s.astype(np.float64))).astype(np.float16)
+    assert np.array_equal(b.astype(np.float64), -(z.astype(np.float64) * s.astype(np.float64)))
+    assert np.array_equal(moe.dequant_affine(packed, s, b, 64), moe.dequant(packed, s, z, 64))
+
+
+def test_affine_expert_matrices_use_the_bias_arrays():
+    from block_diffusion_lm_router_amd import workloads
+    shape = workloads.LayerShape(4, 256, 128, 2, 1)
+    w = workloads.make_weights(shape, 0, affine=True)
+    wz = workloads.make_weights(shape, 0)
+    assert np.array_equal(w["gate_up_q"], wz["gate_up_q"])            # same codes and scales
+    assert not np.array_equal(w["gate_up_zero"], wz["gate_up_zero"])  # biases, not zero-points
+    ratio = w["gate_up_zero"].astype(np.float64) / w["gate_up_scale"].astype(np.float64)
+    assert ratio.min() >= -15.1 and ratio.max() <= 0.0
+    assert np.mean(np.abs(ratio - np.round(ratio)) > 1e-3) > 0.9        # not integer zero-points
+    wg, wu, wd = moe.expert_matrices(w, 1, affine=True)
+    q = moe.unpack_nibbles(w["down_q"][1])
+    assert wd[7, 70] == q[7, 70] * float(w["down_scale"][1, 7, 1]) + float(w["down_zero"][1, 7, 1])
