@@ -45,6 +45,7 @@ class MoeWeightsC(ctypes.Structure):
         ("gate_up_packed", _P),
         ("down_packed", _P),
         ("down_group_size", ctypes.c_int32),
+        ("format", ctypes.c_int32),
     ]
 
 
@@ -161,9 +162,10 @@ class MoeWeights:
 
     KEYS = ("gate_up_q", "gate_up_scale", "gate_up_zero", "down_q", "down_scale", "down_zero")
 
-    def __init__(self, tensors, top_k, group_size=None, down_group_size=None):
+    def __init__(self, tensors, top_k, group_size=None, down_group_size=None, affine=False):
         """Group sizes default to what the scale arrays' shapes imply (d_model / groups of
-        gate/up, d_ff / groups of down)."""
+        gate/up, d_ff / groups of down).  affine=True: the *_zero arrays hold the biases of the
+        affine form w = q s + b (BD_FORMAT_AFFINE; the GEMMs then need prepare())."""
         self.tensors = tensors
         gq = tensors["gate_up_q"]
         E, two_f, half_d = gq.shape
@@ -173,10 +175,12 @@ class MoeWeights:
         if down_group_size is None:
             down_group_size = self.d_ff // tensors["down_scale"].shape[-1]
         self.top_k, self.group_size, self.down_group_size = top_k, group_size, down_group_size
+        self.affine = affine
         dtypes = {"gate_up_q": torch.uint8, "down_q": torch.uint8}
         ptrs = {k: _ptr(tensors[k], dtypes.get(k, torch.float16), k) for k in self.KEYS}
         self.c = MoeWeightsC(E, top_k, self.d_model, self.d_ff, group_size,
-                             *[ptrs[k] for k in self.KEYS], None, None, down_group_size)
+                             *[ptrs[k] for k in self.KEYS], None, None, down_group_size,
+                             1 if affine else 0)
         self.packed = None
 
     def prepare(self, drop_raw=False):
@@ -211,9 +215,9 @@ class MoeWeights:
 
     @classmethod
     def from_numpy(cls, arrays, top_k, device="cuda", group_size=None, prepare=False,
-                   drop_raw=False, down_group_size=None):
+                   drop_raw=False, down_group_size=None, affine=False):
         t = {k: torch.from_numpy(arrays[k]).to(device) for k in cls.KEYS}
-        w = cls(t, top_k, group_size, down_group_size)
+        w = cls(t, top_k, group_size, down_group_size, affine)
         return w.prepare(drop_raw=drop_raw) if prepare else w
 
     def ref(self):

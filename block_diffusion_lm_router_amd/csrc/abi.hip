@@ -26,6 +26,7 @@ int check_moe_shape(const bd_moe_weights* w, int T) {
     return BD_ERR_UNSUPPORTED;
   if (w->d_model % 128 != 0 || w->d_ff % 64 != 0) return BD_ERR_UNSUPPORTED;
   if (w->d_model % w->group_size != 0 || w->d_ff % gd != 0) return BD_ERR_SHAPE;
+  if (w->format != BD_FORMAT_ASYMMETRIC && w->format != BD_FORMAT_AFFINE) return BD_ERR_UNSUPPORTED;
   if (w->d_model > 4096 || w->d_ff > 4096) return BD_ERR_UNSUPPORTED;  // per-block scale table
   if ((int64_t)T * w->top_k > (int64_t)BD_MAX_TOKENS * BD_MAX_TOPK) return BD_ERR_SHAPE;
   return BD_OK;
@@ -41,9 +42,10 @@ int check_workspace(const void* ws, size_t have, size_t need) {
 // A matrix is usable by the GEMMs through its packed stream (then the raw arrays may be NULL)
 // or through its raw nibble, scale and zero-point arrays.
 int check_matrix(const uint8_t* q, const uint16_t* scale, const uint16_t* zero,
-                 const uint8_t* packed, int group) {
+                 const uint8_t* packed, int group, int format) {
   if (packed) return aligned16(packed) ? BD_OK : BD_ERR_ALIGN;
-  if (group != 64) return BD_ERR_UNSUPPORTED;  // 128-groups go through the packed stream
+  // 128-groups and the affine form go through the packed stream only
+  if (group != 64 || format != BD_FORMAT_ASYMMETRIC) return BD_ERR_UNSUPPORTED;
   if (!q || !scale || !zero) return BD_ERR_NULL;
   if (!aligned16(q) || !aligned16(scale) || !aligned16(zero)) return BD_ERR_ALIGN;
   return BD_OK;
@@ -55,19 +57,21 @@ int down_group(const bd_moe_weights* w) {
 
 int check_gate_up_weights(const bd_moe_weights* w) {
   return check_matrix(w->gate_up_q, w->gate_up_scale, w->gate_up_zero, w->gate_up_packed,
-                      w->group_size);
+                      w->group_size, w->format);
 }
 
 int check_down_weights(const bd_moe_weights* w) {
-  return check_matrix(w->down_q, w->down_scale, w->down_zero, w->down_packed, down_group(w));
+  return check_matrix(w->down_q, w->down_scale, w->down_zero, w->down_packed, down_group(w),
+                      w->format);
 }
 
 bd::W4A16Matrix gate_up_of(const bd_moe_weights* w) {
   return bd::W4A16Matrix{w->gate_up_q, w->gate_up_scale, w->gate_up_zero, w->gate_up_packed,
-                         w->group_size};
+                         w->group_size, w->format == BD_FORMAT_AFFINE ? 1 : 0};
 }
 bd::W4A16Matrix down_of(const bd_moe_weights* w) {
-  return bd::W4A16Matrix{w->down_q, w->down_scale, w->down_zero, w->down_packed, down_group(w)};
+  return bd::W4A16Matrix{w->down_q, w->down_scale, w->down_zero, w->down_packed, down_group(w),
+                         w->format == BD_FORMAT_AFFINE ? 1 : 0};
 }
 
 int check_sample_shape(int P, int V, float temperature) {

@@ -57,6 +57,7 @@ struct W4A16Matrix {
   const uint16_t* zero;
   const uint8_t* pk;    // packed stream for the 256-row tiles, or nullptr
   int group;            // group size of scale/zero (64, or 128 for repacking only)
+  int affine;           // zero holds the bias b of w = q s + b (packed stream only)
 };
 
 int pk_tiles(bool gated, int d_model, int d_ff);

@@ -112,6 +112,7 @@ struct GemmArgs {
   uint16_t* h_out;         // gate/up output [T*k][d_ff]
   float* o_out;            // down output [T*k][d_model]
   int out_ld;
+  int affine;              // packed stream holds (scale, bias) of w = q s + b, not (scale, zero)
 };
 
 // The masks and the magic exponent are passed in registers (see DequantConsts) so that each
@@ -142,6 +143,40 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 zc1, _Float16 z
   const half2_t hb = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, b), sixteenth, z2);
   const half2_t hc = __builtin_bit_cast(half2_t, c) + z1;
   const half2_t hd = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, d), sixteenth, z2);
+  half8_t r;
+  r[0] = ha[0];
+  r[1] = ha[1];
+  r[2] = hb[0];
+  r[3] = hb[1];
+  r[4] = hc[0];
+  r[5] = hc[1];
+  r[6] = hd[0];
+  r[7] = hd[1];
+  return r;
+}
+
+// Affine form (w = q s + b with a free fp16 bias): the same nibble extraction, the exact fp16
+// q (one packed add or fma), then one packed fma q s + b, rounded once to fp16.  The weights
+// come out in the same k-order as dequant8's.
+__device__ __forceinline__ half8_t dequant8_affine(uint32_t w, half2_t s2, half2_t b2,
+                                                   const DequantConsts& k) {
+  const uint32_t kLo = k.lo, kHi = k.hi, kMagic = k.magic;
+  const uint32_t a = (w & kLo) | kMagic;
+  const uint32_t b = (w & kHi) | kMagic;
+  const uint32_t w8 = w >> 8;
+  const uint32_t c = (w8 & kLo) | kMagic;
+  const uint32_t d = (w8 & kHi) | kMagic;
+  const half2_t m1024 = {(_Float16)-1024.f, (_Float16)-1024.f};
+  const half2_t m64 = {(_Float16)-64.f, (_Float16)-64.f};
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t qa = __builtin_bit_cast(half2_t, a) + m1024;
+  const half2_t qb = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, b), sixteenth, m64);
+  const half2_t qc = __builtin_bit_cast(half2_t, c) + m1024;
+  const half2_t qd = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, d), sixteenth, m64);
+  const half2_t ha = __builtin_elementwise_fma(qa, s2, b2);
+  const half2_t hb = __builtin_elementwise_fma(qb, s2, b2);
+  const half2_t hc = __builtin_elementwise_fma(qc, s2, b2);
+  const half2_t hd = __builtin_elementwise_fma(qd, s2, b2);
   half8_t r;
   r[0] = ha[0];
   r[1] = ha[1];
@@ -432,11 +467,68 @@ constexpr int kPkDepth = 3;                                     // stages in reg
 constexpr int kPkXSlot = kItemTokens * kXRowBytes;              // 8 KB
 static_assert(kSG == 2 && kItemTokens == 32 && kXRowBytes == 256, "packed stage geometry");
 
+// One 64-group of a stage for a wave's two 16-row sets (A, B) and NMT 16-token tiles: the
+// weights dequantised into MFMA operands, the activation fragments from the LDS tile, and the
+// products added to the running fp32 sums.  Asymmetric form: exact fp16 (q - z), the group's
+// MFMA sum scaled by its fp32 scale.  Affine form: fp16 q s + b, accumulated directly.
+// sz holds, per set, (scale g0, scale g1, zero or bias g0, zero or bias g1).
+template <int NMT, bool AFF>
+__device__ __forceinline__ void group_mfma(const u32x4_t& wa, const u32x4_t& wb, half4_t szA,
+                                           half4_t szB, int j, const char* xt, int n, int kb,
+                                           float4_t (&totA)[NMT], float4_t (&totB)[NMT],
+                                           const DequantConsts& dq) {
+  half8_t bA0, bA1, bB0, bB1;
+  float fsA = 0.f, fsB = 0.f;
+  if constexpr (AFF) {
+    const half2_t sA = {szA[j], szA[j]}, oA = {szA[2 + j], szA[2 + j]};
+    const half2_t sB = {szB[j], szB[j]}, oB = {szB[2 + j], szB[2 + j]};
+    bA0 = dequant8_affine(wa[2 * j], sA, oA, dq);
+    bA1 = dequant8_affine(wa[2 * j + 1], sA, oA, dq);
+    bB0 = dequant8_affine(wb[2 * j], sB, oB, dq);
+    bB1 = dequant8_affine(wb[2 * j + 1], sB, oB, dq);
+  } else {
+    const _Float16 zA = szA[2 + j], zB = szB[2 + j];
+    const _Float16 za1 = -((_Float16)1024.f + zA), za2 = -((_Float16)64.f + zA);
+    const _Float16 zb1 = -((_Float16)1024.f + zB), zb2 = -((_Float16)64.f + zB);
+    fsA = (float)szA[j];
+    fsB = (float)szB[j];
+    bA0 = dequant8(wa[2 * j], za1, za2, dq);
+    bA1 = dequant8(wa[2 * j + 1], za1, za2, dq);
+    bB0 = dequant8(wb[2 * j], zb1, zb2, dq);
+    bB1 = dequant8(wb[2 * j + 1], zb1, zb2, dq);
+  }
+  const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int m = mt * 16 + n;
+    const char* xrow = xt + m * kXRowBytes;
+    const int c8 = j * 8 + kb * 2;
+    const half8_t a0 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 0) ^ xswz(m)) << 4)));
+    const half8_t a1 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 1) ^ xswz(m)) << 4)));
+    if constexpr (AFF) {
+      totA[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bA0, totA[mt], 0, 0, 0);
+      totA[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bA1, totA[mt], 0, 0, 0);
+      totB[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bB0, totB[mt], 0, 0, 0);
+      totB[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bB1, totB[mt], 0, 0, 0);
+    } else {
+      float4_t accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bA0, zero4, 0, 0, 0);
+      accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bA1, accA, 0, 0, 0);
+      float4_t accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bB0, zero4, 0, 0, 0);
+      accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bB1, accB, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        totA[mt][q] = fmaf(fsA, accA[q], totA[mt][q]);
+        totB[mt][q] = fmaf(fsB, accB[q], totB[mt][q]);
+      }
+    }
+  }
+}
+
 struct PkStage {
   u32x4_t wa, wb, sz, x;
 };
 
-template <bool GATED, int NMT, int NSC>
+template <bool GATED, int NMT, int NSC, bool AFF>
 __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e, int pos0,
                                             int mcount, int tile) {
   const int tid = threadIdx.x;
@@ -506,31 +598,7 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
     for (int j = 0; j < 2; ++j) {
       const int g = 2 * c + j;
       if (g >= G) break;
-      const _Float16 zA = szA[2 + j], zB = szB[2 + j];
-      const _Float16 za1 = -((_Float16)1024.f + zA), za2 = -((_Float16)64.f + zA);
-      const _Float16 zb1 = -((_Float16)1024.f + zB), zb2 = -((_Float16)64.f + zB);
-      const float fsA = (float)szA[j], fsB = (float)szB[j];
-      const half8_t bA0 = dequant8(r.wa[2 * j], za1, za2, dq);
-      const half8_t bA1 = dequant8(r.wa[2 * j + 1], za1, za2, dq);
-      const half8_t bB0 = dequant8(r.wb[2 * j], zb1, zb2, dq);
-      const half8_t bB1 = dequant8(r.wb[2 * j + 1], zb1, zb2, dq);
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const int m = mt * 16 + n;
-        const char* xrow = xt + m * kXRowBytes;
-        const int c8 = j * 8 + kb * 2;
-        const half8_t a0 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 0) ^ xswz(m)) << 4)));
-        const half8_t a1 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 1) ^ xswz(m)) << 4)));
-        float4_t accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bA0, zero4, 0, 0, 0);
-        accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bA1, accA, 0, 0, 0);
-        float4_t accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bB0, zero4, 0, 0, 0);
-        accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bB1, accB, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          totA[mt][q] = fmaf(fsA, accA[q], totA[mt][q]);
-          totB[mt][q] = fmaf(fsB, accB[q], totB[mt][q]);
-        }
-      }
+      group_mfma<NMT, AFF>(r.wa, r.wb, szA, szB, j, xt, n, kb, totA, totB, dq);
     }
   };
 
@@ -593,7 +661,7 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
 }
 
 // NSC > 0: compiled for exactly NSC stages (the caller checks); 0: any number of stages.
-template <bool GATED, int NSC>
+template <bool GATED, int NSC, bool AFF>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kPkXSlot];
   // XCD b % 8 owns a contiguous range of work items (the items of one expert are consecutive,
@@ -611,9 +679,9 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
   const int pos0 = a.items[2 + 3 * item];
   const int mcount = a.items[3 + 3 * item];
   if (mcount > 16)
-    packed_item<GATED, 2, NSC>(a, lds, e, pos0, mcount, tile);
+    packed_item<GATED, 2, NSC, AFF>(a, lds, e, pos0, mcount, tile);
   else
-    packed_item<GATED, 1, NSC>(a, lds, e, pos0, mcount, tile);
+    packed_item<GATED, 1, NSC, AFF>(a, lds, e, pos0, mcount, tile);
 }
 
 // ------------------------------------------------------------------ down, resident rows
@@ -636,7 +704,7 @@ struct PkW {
   u32x4_t wa, wb, sz;
 };
 
-template <int NMT>
+template <int NMT, bool AFF>
 __device__ __forceinline__ void down_resident_item(const GemmArgs& a, char* lds, int e, int pos0,
                                                    int mcount, int tile0, int ntiles) {
   const int tid = threadIdx.x;
@@ -720,31 +788,7 @@ __device__ __forceinline__ void down_resident_item(const GemmArgs& a, char* lds,
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (2 * c + j >= G) break;
-      const _Float16 zA = szA[2 + j], zB = szB[2 + j];
-      const _Float16 za1 = -((_Float16)1024.f + zA), za2 = -((_Float16)64.f + zA);
-      const _Float16 zb1 = -((_Float16)1024.f + zB), zb2 = -((_Float16)64.f + zB);
-      const float fsA = (float)szA[j], fsB = (float)szB[j];
-      const half8_t bA0 = dequant8(r.wa[2 * j], za1, za2, dq);
-      const half8_t bA1 = dequant8(r.wa[2 * j + 1], za1, za2, dq);
-      const half8_t bB0 = dequant8(r.wb[2 * j], zb1, zb2, dq);
-      const half8_t bB1 = dequant8(r.wb[2 * j + 1], zb1, zb2, dq);
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const int m = mt * 16 + n;
-        const char* xrow = xt + m * kXRowBytes;
-        const int c8 = j * 8 + kb * 2;
-        const half8_t a0 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 0) ^ xswz(m)) << 4)));
-        const half8_t a1 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(xrow + (((c8 + 1) ^ xswz(m)) << 4)));
-        float4_t accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bA0, zero4, 0, 0, 0);
-        accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bA1, accA, 0, 0, 0);
-        float4_t accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bB0, zero4, 0, 0, 0);
-        accB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bB1, accB, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          totA[mt][q] = fmaf(fsA, accA[q], totA[mt][q]);
-          totB[mt][q] = fmaf(fsB, accB[q], totB[mt][q]);
-        }
-      }
+      group_mfma<NMT, AFF>(r.wa, r.wb, szA, szB, j, xt, n, kb, totA, totB, dq);
     }
   };
   auto store = [&](int tile) {
@@ -782,6 +826,7 @@ __device__ __forceinline__ void down_resident_item(const GemmArgs& a, char* lds,
   }
 }
 
+template <bool AFF>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_down_resident_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds_dyn[];
   // Same XCD-aware order as the staged kernel, over (item, group of tiles).
@@ -799,29 +844,38 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_down_resident_kernel(GemmAr
   const int tile0 = grp * kDownTilesPerBlock;
   const int ntiles = min(kDownTilesPerBlock, a.tiles - tile0);
   if (mcount > 16)
-    down_resident_item<2>(a, lds_dyn, e, pos0, mcount, tile0, ntiles);
+    down_resident_item<2, AFF>(a, lds_dyn, e, pos0, mcount, tile0, ntiles);
   else
-    down_resident_item<1>(a, lds_dyn, e, pos0, mcount, tile0, ntiles);
+    down_resident_item<1, AFF>(a, lds_dyn, e, pos0, mcount, tile0, ntiles);
 }
 
 // Stage counts with a fully unrolled kernel: the contraction dims 2816 (gate/up) and 704
 // (down) of the 26B-A4B expert shape.
-template <bool GATED>
-void launch_packed(const GemmArgs& a, int max_items, hipStream_t stream) {
+template <bool GATED, bool AFF>
+void launch_packed_as(const GemmArgs& a, int max_items, hipStream_t stream) {
   const int NS = (a.K / 64 + 1) / 2;
   if (!GATED && NS <= kResidentMaxStages) {
     const int groups = (a.tiles + kDownTilesPerBlock - 1) / kDownTilesPerBlock;
-    hipLaunchKernelGGL(w4a16_down_resident_kernel, dim3(grid_blocks(max_items, groups)),
+    hipLaunchKernelGGL(w4a16_down_resident_kernel<AFF>, dim3(grid_blocks(max_items, groups)),
                        dim3(kThreads), NS * kPkXSlot, stream, a);
     return;
   }
   const dim3 grid(grid_blocks(max_items, a.tiles)), block(kThreads);
   if (NS == 22)
-    hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 22>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 22, AFF>), grid, block, 0, stream, a);
   else if (NS == 6)
-    hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 6>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 6, AFF>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 0>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((w4a16_packed_kernel<GATED, 0, AFF>), grid, block, 0, stream, a);
+}
+
+// The weight form of the packed stream picks the kernels' dequantisation.
+template <bool GATED>
+void launch_packed(const GemmArgs& a, int max_items, hipStream_t stream) {
+  if (a.affine)
+    launch_packed_as<GATED, true>(a, max_items, stream);
+  else
+    launch_packed_as<GATED, false>(a, max_items, stream);
 }
 
 // Repacking into the packed stream (layout above).  One thread per 16-byte chunk of the output;
@@ -924,6 +978,7 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.perm = ws.perm;
   a.items = ws.items;
   a.pk = gu.pk;
+  a.affine = gu.affine;
   a.h_out = ws.h;
   a.o_out = nullptr;
   a.out_ld = d_ff;
@@ -958,6 +1013,7 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
   a.perm = ws.perm;
   a.items = ws.items;
   a.pk = dn.pk;
+  a.affine = dn.affine;
   a.h_out = nullptr;
   a.o_out = expert_out;
   a.out_ld = d_model;

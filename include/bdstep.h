@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 7
+#define BD_ABI_VERSION 8
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -89,6 +89,11 @@ typedef enum {
  * group of 128 returns BD_ERR_UNSUPPORTED.  The model card's checkpoint format
  * ("requirements") is g = 128, gd = 64.
  *
+ * format BD_FORMAT_AFFINE: the *_zero arrays hold a free fp16 bias b per group and the weight
+ * is w = q * scale + b (the MLX-style affine 4-bit form, named on the TensorFold XPU page).
+ * The GEMMs then form fp16(q * scale + b) for the MFMA (one rounding per weight) and need the
+ * packed stream; over raw arrays they return BD_ERR_UNSUPPORTED.
+ *
  * gate_up_packed / down_packed (optional, NULL when absent): the matrix repacked once by
  * moe_w4a16_prepare into the stream the 256-row GEMM tiles consume.  A GEMM whose packed
  * stream is present reads only that stream (its q, scale and zero pointers may then be NULL);
@@ -96,6 +101,9 @@ typedef enum {
  * (q - z) per 64-group and scale each group's sum in fp32; they differ only in the order of
  * the fp32 sums.
  */
+#define BD_FORMAT_ASYMMETRIC 0  /* w = (q - zero) * scale, zero an integer 0..15 in fp16 */
+#define BD_FORMAT_AFFINE 1      /* w = q * scale + bias, bias a free fp16 in the zero slot */
+
 typedef struct bd_moe_weights {
   int32_t num_experts; /* E, 1..256          */
   int32_t top_k;       /* k, 1..min(E, 16)   */
@@ -111,6 +119,7 @@ typedef struct bd_moe_weights {
   const uint8_t* gate_up_packed;  /* optional, bd_moe_packed_size(w, 0) bytes, 16-byte aligned */
   const uint8_t* down_packed;     /* optional, bd_moe_packed_size(w, 1) bytes, 16-byte aligned */
   int32_t down_group_size;        /* gd of down: 0 (= g), 64 or 128 (128 via the packed stream) */
+  int32_t format;                 /* BD_FORMAT_ASYMMETRIC or BD_FORMAT_AFFINE (see above) */
 } bd_moe_weights;
 
 /* Library ABI version (BD_ABI_VERSION of the build). */

@@ -55,10 +55,10 @@ def test_version_and_status_strings(lib):
     assert lib.bd_status_string(99) == b"unknown status"
 
 
-def _weights(E=128, k=8, d=2816, f=704, g=64, ptr=0x1000, gd=0):
+def _weights(E=128, k=8, d=2816, f=704, g=64, ptr=0x1000, gd=0, fmt=0):
     from block_diffusion_lm_router_amd._binding import MoeWeightsC
     p = ctypes.c_void_p(ptr)
-    return MoeWeightsC(E, k, d, f, g, p, p, p, p, p, p, None, None, gd)
+    return MoeWeightsC(E, k, d, f, g, p, p, p, p, p, p, None, None, gd, fmt)
 
 
 def test_moe_workspace_size(lib):
@@ -76,7 +76,7 @@ def test_moe_workspace_size(lib):
     (dict(), 0, 2), (dict(), 65537, 2), (dict(E=0), 4, 2), (dict(E=257), 4, 2),
     (dict(k=0), 4, 2), (dict(k=17), 4, 2), (dict(E=4, k=5), 4, 2),
     (dict(g=32), 4, 5), (dict(g=128, gd=256), 4, 5), (dict(d=2880), 4, 5), (dict(f=700), 4, 5),
-    (dict(g=128, d=2880 - 64), 4, 2), (dict(gd=128), 4, 2),
+    (dict(g=128, d=2880 - 64), 4, 2), (dict(gd=128), 4, 2), (dict(fmt=2), 4, 5),
 ])
 def test_moe_shape_validation(lib, kw, T, code):
     w = _weights(**kw)
@@ -233,6 +233,11 @@ def test_prepare_sizes_and_validation(lib):
     assert lib.moe_w4a16_gate_up(ctypes.byref(ck), 256, p, ws, 1 << 30, None) == 5
     assert lib.moe_w4a16_down(ctypes.byref(_weights(g=64, gd=128, f=768)), 256, p, ws, 1 << 30,
                               None) == 5
+    # the affine form over raw arrays is refused by the GEMMs (it needs the packed stream)
+    aff = _weights(fmt=1)
+    assert lib.bd_moe_packed_size(ctypes.byref(aff), 0) == 128 * 6 * 22 * 18432
+    assert lib.moe_w4a16_gate_up(ctypes.byref(aff), 256, p, ws, 1 << 30, None) == 5
+    assert lib.moe_w4a16_down(ctypes.byref(aff), 256, p, ws, 1 << 30, None) == 5
     # a misaligned packed stream is rejected by the GEMM entry points before any launch
     w.gate_up_packed = 0x1008
     ws = ctypes.c_void_p(0x10000)

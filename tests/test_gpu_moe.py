@@ -27,7 +27,7 @@ def bd():
 class Layer:
     """One layer's inputs on the host and on the device."""
 
-    def __init__(self, bd, shape, x=None, logits=None, weights=None, layer=0):
+    def __init__(self, bd, shape, x=None, logits=None, weights=None, layer=0, affine=False):
         import torch
         self.shape = shape
         self.x = workloads.make_activations(shape) if x is None else x
@@ -36,7 +36,8 @@ class Layer:
         # group sizes as the scale arrays' shapes imply (gate/up, down)
         self.groups = (shape.d_model // self.w_np["gate_up_scale"].shape[-1],
                        shape.d_ff // self.w_np["down_scale"].shape[-1])
-        self.w = bd.MoeWeights.from_numpy(self.w_np, shape.top_k)
+        self.affine = affine
+        self.w = bd.MoeWeights.from_numpy(self.w_np, shape.top_k, affine=affine)
         self.x_d = torch.from_numpy(self.x).cuda()
         self.logits_d = torch.from_numpy(self.logits).cuda()
 
@@ -67,7 +68,9 @@ class Layer:
 
 def outputs_and_h_rounding_bound(layer, ids, rows):
     """Oracle expert outputs o[t, j] and the worst-case effect on them of storing the
-    GeGLU activations h in fp16 (the MFMA operand precision): |W_down| @ |h| * 2^-11."""
+    GeGLU activations h in fp16 (the MFMA operand precision): |W_down| @ |h| * 2^-11.  The
+    affine form also rounds every weight to fp16 once (2^-11 relative): the down weights add
+    the same bound again and the gate/up weights, through h, about as much once more."""
     T, k = ids.shape
     d = layer.shape.d_model
     o = np.full((T, k, d), np.nan)
@@ -77,10 +80,10 @@ def outputs_and_h_rounding_bound(layer, ids, rows):
     x64 = layer.x.astype(np.float64)
     for e in np.unique(ids[rows]):
         tt, jj = np.nonzero((ids == e) & mask[:, None])
-        wg, wu, wd = omoe.expert_matrices(layer.w_np, int(e), *layer.groups)
+        wg, wu, wd = omoe.expert_matrices(layer.w_np, int(e), *layer.groups, affine=layer.affine)
         o[tt, jj] = omoe.expert_ffn(x64[tt], wg, wu, wd)
         h = omoe.gelu_tanh(x64[tt] @ wg.T) * (x64[tt] @ wu.T)
-        bound[tt, jj] = (np.abs(h) @ np.abs(wd.T)) * 2.0 ** -11
+        bound[tt, jj] = (np.abs(h) @ np.abs(wd.T)) * 2.0 ** -11 * (3.0 if layer.affine else 1.0)
     return o, bound
 
 
@@ -357,3 +360,48 @@ def test_checkpoint_format_layer(bd, which):
     layer.w.unprepare()
     with pytest.raises(bd.BdError):
         layer.run(bd, prepared=False)
+
+
+# ---------------------------------------------------------------- affine weight form
+
+
+@pytest.mark.parametrize("which", ["tiny", "layer"])
+def test_affine_layer(bd, which):
+    """The affine form (w = q s + b, free fp16 bias) through the packed streams: ids bit-exact,
+    outputs within the FFN bar (all tokens on the tiny shape, sampled tokens at full shape);
+    the raw-array GEMM refuses it."""
+    shape = workloads.TINY_LAYER if which == "tiny" else workloads.LAYER
+    w_np = workloads.make_weights(shape, 2, affine=True)
+    say("affine layer", which)
+    layer = Layer(bd, shape, weights=w_np, affine=True)
+    tokens = None if which == "tiny" else np.random.default_rng(2).choice(shape.tokens, 6, replace=False)
+    check_layer(layer, layer.run(bd, prepared=True), tokens=tokens)
+    layer.w.unprepare()
+    with pytest.raises(bd.BdError):
+        layer.run(bd, prepared=False)
+
+
+def test_affine_with_exact_bias_matches_the_asymmetric_form(bd):
+    """b = -z s with power-of-two scales makes every fp16 weight q s + b exact, so the affine
+    path must agree with the asymmetric one up to fp32 summation order."""
+    shape = workloads.LayerShape(96, 512, 256, 8, 2)
+    w_np = workloads.make_weights(shape, 4)
+    rng = np.random.default_rng(5)
+    for kind in ("gate_up", "down"):
+        sc = w_np[kind + "_scale"]
+        w_np[kind + "_scale"] = (np.float16(2.0) ** -rng.integers(5, 8, sc.shape)).astype(np.float16)
+    aff = dict(w_np)
+    for kind in ("gate_up", "down"):
+        aff[kind + "_zero"] = (-(w_np[kind + "_zero"].astype(np.float64)
+                                 * w_np[kind + "_scale"].astype(np.float64))).astype(np.float16)
+        assert np.array_equal(aff[kind + "_zero"].astype(np.float64),
+                              -(w_np[kind + "_zero"].astype(np.float64) * w_np[kind + "_scale"].astype(np.float64)))
+    say("affine exact bias")
+    a = Layer(bd, shape, weights=w_np)
+    b = Layer(bd, shape, weights=aff, x=a.x, logits=a.logits, affine=True)
+    ga = a.run(bd, prepared=True)
+    gb = b.run(bd, prepared=True)
+    assert np.array_equal(ga[0], gb[0])
+    o_a, o_b = ga[2].astype(np.float64), gb[2].astype(np.float64)
+    scale = np.sqrt(np.mean(o_a ** 2))
+    assert np.max(np.abs(o_a - o_b)) <= 1e-5 * scale + 2.0 ** -11 * np.max(np.abs(o_a))
