@@ -296,7 +296,7 @@ def main_layer(args):
                       f"layer: one MoE FFN layer (canvas {T}, d_model {d}, expert ffn {f}, {E} experts "
                       f"top-{k}, W4A16 asym g64, uniform N(0,1) router logits), route + gate/up + "
                       f"down + combine", {"experts_touched": touched, "step_algorithmic_bytes": int(alg)})
-    rec["roofline"] = {"kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22>)", "bound": "hbm",
+    rec["roofline"] = {"kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22, false>)", "bound": "hbm",
                        "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                        "avg_launch_us": round(gu_us, 2), "alg_bytes_per_launch": int(gu_alg)}
@@ -542,7 +542,7 @@ def main():
             **({"components": parts} if parts is not None else {}),
         },
         "roofline": {
-            "kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22>)",
+            "kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22, false>)",
             "bound": "hbm",
             "achieved": round(gu_gbs, 2),
             "peak": HBM_PEAK_GBS,
