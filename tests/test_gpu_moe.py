@@ -365,13 +365,15 @@ def test_checkpoint_format_layer(bd, which):
 # ---------------------------------------------------------------- affine weight form
 
 
-@pytest.mark.parametrize("which", ["tiny", "layer"])
+@pytest.mark.parametrize("which", ["tiny", "tiny_g128", "layer"])
 def test_affine_layer(bd, which):
     """The affine form (w = q s + b, free fp16 bias) through the packed streams: ids bit-exact,
-    outputs within the FFN bar (all tokens on the tiny shape, sampled tokens at full shape);
-    the raw-array GEMM refuses it."""
-    shape = workloads.TINY_LAYER if which == "tiny" else workloads.LAYER
-    w_np = workloads.make_weights(shape, 2, affine=True)
+    outputs within the FFN bar (all tokens on the tiny shapes, sampled tokens at full shape);
+    the raw-array GEMM refuses it.  tiny_g128 groups both matrices at 128 (the repacking
+    spreads a 128-group's bias like its zero-point)."""
+    shape = workloads.LAYER if which == "layer" else workloads.TINY_LAYER
+    g = 128 if which == "tiny_g128" else None
+    w_np = workloads.make_weights(shape, 2, gate_up_group=g, down_group=g, affine=True)
     say("affine layer", which)
     layer = Layer(bd, shape, weights=w_np, affine=True)
     tokens = None if which == "tiny" else np.random.default_rng(2).choice(shape.tokens, 6, replace=False)
