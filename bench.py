@@ -211,6 +211,17 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=20):
     return out
 
 
+def read_ceiling(rate_gbs):
+    """The achievable HBM read rate, measured now with the library's streaming-read probe (two
+    1 GiB buffers in turn, together larger than the last-level cache), and rate_gbs as a
+    fraction of it."""
+    from block_diffusion_lm_router_amd import hbm_probe
+    log("measuring the HBM read ceiling")
+    gbs = hbm_probe.read_rate(1 << 30, 10, verify=False)["read_gbs"]
+    return {"GB/s": gbs, "frac": round(rate_gbs / gbs, 4),
+            "probe": "bd_hbm_read, 2 x 1 GiB buffers in turn, 10 launches"}
+
+
 def timed_loop(fn, steps, warmup):
     """ms per call of fn over `steps` calls after `warmup`, bracketed by synchronisation."""
     import torch
@@ -299,7 +310,8 @@ def main_layer(args):
     rec["roofline"] = {"kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22, false>)", "bound": "hbm",
                        "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                       "avg_launch_us": round(gu_us, 2), "alg_bytes_per_launch": int(gu_alg)}
+                       "avg_launch_us": round(gu_us, 2), "alg_bytes_per_launch": int(gu_alg),
+                       "read_ceiling": read_ceiling(gu_gbs)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         from threadpoolctl import threadpool_limits
@@ -362,7 +374,8 @@ def main_sampler(args):
     rec["roofline"] = {"kernel": "diffusion_sample_step (sample_stream_kernel + sample_finish_kernel "
                                  "+ accept_kernel)", "bound": "hbm", "achieved": round(gbs, 2),
                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                       "traffic": None, "avg_launch_us": round(us, 2), "alg_bytes_per_launch": int(alg)}
+                       "traffic": None, "avg_launch_us": round(us, 2), "alg_bytes_per_launch": int(alg),
+                       "read_ceiling": read_ceiling(gbs)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         from oracle import sampler as osamp
@@ -551,8 +564,11 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(float(gu_ms.mean()) * 1e3, 2),
             "alg_bytes_per_launch": int(gu_alg.mean()),
+            "read_ceiling": read_ceiling(gu_gbs),
         },
     }
+    result["config"]["frac_of_read_ceiling"] = round(
+        value / result["roofline"]["read_ceiling"]["GB/s"], 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(shape, x_np, baseline_layers, logits_np, sshape)
