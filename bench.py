@@ -124,6 +124,8 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=20):
 
     * ffn_layer_uniform: one whole FFN layer (route, gate/up, down, combine) at the 256-token
       canvas with uniform N(0, 1) router logits (every expert touched);
+    * ffn_layer_short_zipf: the same at a 64-token canvas with Zipf(1.2) routing (about 100 of
+      the 128 experts touched, most with a handful of tokens: the latency-bound case);
     * sampler_entropy_bound / sampler_confidence: one sampler step over all rows unfrozen;
     * rmsnorm / router: the layer neighbours at the same shape;
     * canvas_init / loop_update: the denoising-loop driver's two launches at the canvas size.
@@ -172,6 +174,28 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=20):
     timed("ffn_layer_uniform", [layer_fn(layers[0][0]), layer_fn(layers[1 % len(layers)][0])],
           touched * (gu_b + dn_b) + 2 * T * d * 2 + T * E * 4 + 2 * T * k * 4)
     out["ffn_layer_uniform"]["experts_touched"] = touched
+
+    short = workloads.SHORT_LAYER
+    Ts = short.tokens
+    xs = x[:Ts]
+    ids_s = torch.empty((Ts, k), dtype=torch.int32, device="cuda")
+    tw_s = torch.empty((Ts, k), dtype=torch.float32, device="cuda")
+    o_s = torch.empty((Ts, k, d), dtype=torch.float32, device="cuda")
+    y_s = torch.empty((Ts, d), dtype=torch.float16, device="cuda")
+    short_fns, touched_s = [], []
+    for li in range(2):
+        w = layers[li % len(layers)][0]
+        r = torch.from_numpy(workloads.make_router_logits(short, li)).cuda()
+        bd.moe_route_topk(w, r, ids_s, tw_s, ws)
+        touched_s.append(int(torch.unique(ids_s).numel()))
+        launches = (bd.bind(bd.moe_route_topk, w, r, ids_s, tw_s, ws),
+                    bd.bind(bd.moe_w4a16_gate_up, w, xs, ws),
+                    bd.bind(bd.moe_w4a16_down, w, Ts, o_s, ws),
+                    bd.bind(bd.moe_combine_fixed_order, o_s, tw_s, y_s))
+        short_fns.append(lambda launches=launches: [fn() for fn in launches])
+    timed("ffn_layer_short_zipf", short_fns,
+          float(np.mean(touched_s)) * (gu_b + dn_b) + 2 * Ts * d * 2 + Ts * E * 4 + 2 * Ts * k * 4)
+    out["ffn_layer_short_zipf"]["experts_touched"] = touched_s
 
     logits2 = logits.clone()
     frozen = torch.zeros(P, dtype=torch.uint8, device="cuda")
