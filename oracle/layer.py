@@ -8,7 +8,7 @@ Passages followed (pages named in the package docstring):
 * same, "what the model is": 128 experts, top-8 routing per token; the router scores
   every expert for every token.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * RMS norm: y = h / sqrt(mean_d(h^2) + eps) * w, per row, with a learned per-feature
   weight w and eps = 1e-6 (no mean subtraction, no bias, w used as stored);

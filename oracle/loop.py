@@ -12,7 +12,7 @@ Passages followed (pages named in the package docstring):
   (typically 48).
 * same, "Reproducibility": the seed fixes the canvas initialisation.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * initial id of position p of block b: Philox4x32-10 keyed by the 64-bit seed, counter
   (p, b, 0, 2), word 0, mapped to [0, vocab) as floor(word * vocab / 2^32);

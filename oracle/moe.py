@@ -11,7 +11,7 @@ Passages followed (pages named in the package docstring):
 * same, "requirements": two nibbles per byte, groups run along the contraction
   dimension (down_proj's contraction dimension is 704).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * byte i of a packed row holds element 2i in its low nibble and 2i+1 in its
   high nibble; rows are output features, packed along the contraction dim K;

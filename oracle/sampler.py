@@ -15,7 +15,7 @@ Passages followed (pages named in the package docstring):
   [0, 1]) is accepted; when none is, the single most confident unrevealed position
   is accepted so that every step makes progress.
 
-Readings taken where the pages are silent or loose (each listed in the design doc):
+Readings taken where the pages are silent or loose:
 
 * The entropy is that of softmax(x) at temperature 1 whatever the sampling
   temperature (else temperature 0 would give zero entropy everywhere).
