@@ -41,8 +41,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=None, help="MoE layers per step (default 30)")
     ap.add_argument("--workload", choices=("stack", "layer", "sampler"), default="stack",
                     help="stack (default): the whole denoising step; layer: one FFN layer at the "
@@ -117,7 +117,7 @@ def cpu_baseline(shape, x, layer_inputs, logits, sampler_shape):
     }
 
 
-def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=20):
+def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=50):
     """Live per-launch timings of the path's parts beside the step: each call bracketed by its
     own pair of events on the launch stream, inputs alternating between two copies (or two
     layers) so the 256 MB last-level cache cannot serve a repeat; median over n calls.
@@ -235,6 +235,35 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=20):
     return out
 
 
+GU_LAUNCHES = 60
+
+
+def gate_up_back_to_back(bd, weights, routers, x, ids, tw):
+    """Average duration (us) of one gate/up launch, from a pass right after the timed region in
+    which GU_LAUNCHES launches cycle back to back through the given layers, bracketed by one
+    event pair.  Each layer is routed once into a workspace of its own first.  A timing
+    event inside a stream of launches leaves the GPU idle for several microseconds before and
+    after the next launch (the trace shows none between unmarked launches), so events around
+    single launches inside the step would measure that idle time as well; spread over the
+    whole pass it is a fraction of a microsecond per launch."""
+    import torch
+    T = x.shape[0]
+    wss = [bd.moe_workspace(T, w) for w in weights]
+    for w, r, ws in zip(weights, routers, wss):
+        bd.moe_route_topk(w, r, ids, tw, ws)
+    runs = [bd.bind(bd.moe_w4a16_gate_up, w, x, ws) for w, ws in zip(weights, wss)]
+    for fn in runs:
+        fn()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(GU_LAUNCHES):
+        runs[i % len(runs)]()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / GU_LAUNCHES
+
+
 def read_ceiling(rate_gbs):
     """The achievable HBM read rate, measured now with the library's streaming-read probe (two
     1 GiB buffers in turn, together larger than the last-level cache), and rate_gbs as a
@@ -310,21 +339,9 @@ def main_layer(args):
     ms = timed_loop(step, args.steps, args.warmup)
     alg = touched * (gu_b + dn_b) + 2 * T * d * 2 + T * E * 4 + 2 * T * k * 4
     value = alg / (ms * 1e-3) / 1e9
-    # the gate/up launch alone, each bracketed by its own events (a separate pass)
-    stream = torch.cuda.current_stream()
-    evs = []
-    for i in range(args.steps):
-        route, gate_up, down, combine = launches[i % 2]
-        route()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        gate_up()
-        b.record(stream)
-        down()
-        combine()
-        evs.append((a, b))
-    torch.cuda.synchronize()
-    gu_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    # the gate/up launch alone: the two layers' launches back to back, one event pair around
+    # the pass (the router logits are the same for both layers in this workload)
+    gu_us = gate_up_back_to_back(bd, layers, [router, router], x, ids, tw)
     gu_alg = touched * gu_b + T * d * 2 + T * k * f * 2
     gu_gbs = gu_alg / (gu_us * 1e-6) / 1e9
     rec = base_record(args, value, ms,
@@ -380,16 +397,9 @@ def main_sampler(args):
     ms = timed_loop(step, args.steps, args.warmup)
     alg = P * V * 4 + P * (4 + 4 + 1) + 4
     value = alg / (ms * 1e-3) / 1e9
-    stream = torch.cuda.current_stream()
-    evs = []
-    for i in range(args.steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        step(i)
-        b.record(stream)
-        evs.append((a, b))
-    torch.cuda.synchronize()
-    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    # The roofline's unit is the whole call (its three launches): its average duration is the
+    # timed region's, where the calls run back to back between one event pair.
+    us = ms * 1e3
     gbs = alg / (us * 1e-6) / 1e9
     rec = base_record(args, value, ms,
                       f"sampler: fp32 logits [{P}, {V}] (N(0,1) + one entry boosted U[0,12]), "
@@ -422,6 +432,10 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 2:
+        print("bench.py needs --steps >= 2 (the gate/up timing pairs consecutive steps).",
+              file=sys.stderr)
         sys.exit(2)
     if args.workload == "layer":
         return main_layer(args)
@@ -474,33 +488,42 @@ def main():
     acc = torch.empty(P, dtype=torch.uint8, device="cuda")
     # Every launch of the stack is marshalled once up front (bd.bind), so that a step costs
     # the host a few microseconds per launch and the GPU's queue never runs dry: the timed
-    # region then measures the kernels, not the host.  A timing event in the stream costs the
-    # GPU a few microseconds of idle time, so each timed step brackets the gate/up launch of
-    # one layer only (layer i mod L at step i): over the timed steps the events sample the
-    # gate/up launches of every layer, at an overhead of one event pair per step.
+    # region then measures the kernels, not the host.  Each timed step times the gate/up
+    # kernel of one layer (layer i mod L at step i) from its own dispatch timestamps: over the
+    # timed steps these sample the gate/up launches of every layer.
     stack = []
     for w, router in layers:
         stack.append((bd.bind(bd.moe_route_topk, w, router, ids, tw, ws),
                       bd.bind(bd.moe_w4a16_gate_up, w, x, ws),
                       bd.bind(bd.moe_w4a16_down, w, T, o, ws),
                       bd.bind(bd.moe_combine_fixed_order, o, tw, y)))
-    gu_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(args.steps)]
-    gu_layer = [i % len(layers) for i in range(args.steps)]
     total = args.warmup + args.steps
     n_acc = torch.zeros(total + args.steps, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(i, events=None, ev_layer=-1):
+    # The gate/up kernel's in-step duration, by difference: timed step j brackets with one event
+    # pair the routing and gate/up launches of layer (j // 2) mod L when j is odd and the
+    # routing launch alone of the same layer when j is even.  A timing event leaves the GPU idle
+    # for several microseconds around the launches next to it (the trace shows no gap between
+    # unmarked launches), the same in both brackets, so the mean of the odd intervals minus
+    # the mean of the even ones is the gate/up launch as it runs inside the step.
+    marks = [((j // 2) % len(layers), j % 2 == 1,
+              (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+             for j in range(args.steps)]
+
+    def step(i, mark=None):
         if i % workloads.STACK_STEPS == 0:
             frozen.zero_()
         for li, (route, gate_up, down, combine) in enumerate(stack):
+            here = mark is not None and li == mark[0]
+            if here:
+                mark[2][0].record(stream)
             route()
-            if li == ev_layer:
-                events[0].record(stream)
+            if here and not mark[1]:
+                mark[2][1].record(stream)
             gate_up()
-            if li == ev_layer:
-                events[1].record(stream)
+            if here and mark[1]:
+                mark[2][1].record(stream)
             down()
             combine()
         bd.diffusion_sample_step(logits, sshape.temperature, sshape.bound, sshape.seed,
@@ -514,7 +537,7 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.warmup, total):
-        step(i, gu_events[i - args.warmup], gu_layer[i - args.warmup])
+        step(i, marks[i - args.warmup])
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -545,11 +568,13 @@ def main():
     step_bytes = ffn_bytes + float(sampler_bytes.mean())
     value = step_bytes / (ms * 1e-3) / 1e9
 
-    gu_ms = np.array([a.elapsed_time(b) for a, b in gu_events])
-    gu_alg = np.array([touched[li] * gu_bytes + T * d * 2 + T * k * f * 2 for li in gu_layer],
-                      dtype=np.float64)
-    gu_gbs = gu_alg.sum() / (gu_ms.sum() * 1e-3) / 1e9
-    traffic = measured_traffic(float(gu_alg.mean()))
+    with_gu = [a.elapsed_time(b) for _, g, (a, b) in marks if g]
+    route_only = [a.elapsed_time(b) for _, g, (a, b) in marks if not g]
+    gu_us = (float(np.mean(with_gu)) - float(np.mean(route_only))) * 1e3
+    gu_alg = float(np.mean([touched[li] * gu_bytes + T * d * 2 + T * k * f * 2
+                            for li, g, _ in marks if g]))
+    gu_gbs = gu_alg / (gu_us * 1e-6) / 1e9
+    traffic = measured_traffic(gu_alg)
     parts = None
     if not args.no_components:
         log("timing the parts one launch at a time")
@@ -586,8 +611,8 @@ def main():
             "unit": "GB/s",
             "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "avg_launch_us": round(float(gu_ms.mean()) * 1e3, 2),
-            "alg_bytes_per_launch": int(gu_alg.mean()),
+            "avg_launch_us": round(gu_us, 2),
+            "alg_bytes_per_launch": int(gu_alg),
             "read_ceiling": read_ceiling(gu_gbs),
         },
     }
