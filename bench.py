@@ -9,8 +9,10 @@ steps.  All inputs are seeded synthetic tensors resident in HBM before timing st
 
 value = algorithmic bytes of the step (touched expert weights with their scales and
 zero-points, activations in and out, router logits, the unfrozen logits rows) / time,
-in GB/s; ms_per_step is the latency of one step; config.step_ms_p10_p50_p90 is the spread of
-the step latency over a second pass of the same length with an event between steps.
+in GB/s; ms_per_step is the latency of one step, from one event pair around the timed steps
+(no other event inside); config.step_ms_p10_p50_p90 is the spread of the step latency over a
+second pass of the same length with an event between steps; the gate/up roofline comes from a
+third pass (see main).
 
 Two more workloads time the parts on their own configurations (--workload):
   layer    one MoE FFN layer (route, gate/up, down, combine) at the 256-token canvas with uniform
@@ -75,14 +77,66 @@ BASELINE_LAYERS = 4     # oracle sample: this many whole layers ...
 BASELINE_STEPS = 2      # ... and this many whole sampler steps (about 10 s of CPU work)
 
 
+def host_cores():
+    """Cores this process may run on (its affinity mask), at most 16: the host share that
+    comes with one GPU on the benchmark machines."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _sample_block(args):
+    """Worker: the oracle's entropy and token of the given rows (their original indices keep
+    the Philox counters of the full tensor)."""
+    rows_x, row_ids, temperature, seed, step = args
+    from oracle import sampler as osamp
+    H = np.empty(len(row_ids))
+    tok = np.empty(len(row_ids), dtype=np.int64)
+    for i, p in enumerate(row_ids):
+        H[i] = osamp.entropy(rows_x[i])
+        tok[i] = (osamp.draw_token(rows_x[i], temperature, seed, step, int(p))[0]
+                  if np.isfinite(H[i]) else -1)
+    return H, tok
+
+
+class SamplerPool:
+    """The oracle's sampler over row blocks on a pool of worker processes (the oracle is plain
+    Python per row, so threads would serialise on the interpreter lock).  The workers are
+    fresh interpreters, started before any timing; a worker that fails raises here (the
+    executor reports a broken pool) instead of being restarted."""
+
+    def __init__(self, workers):
+        import multiprocessing as mp
+        from concurrent.futures import ProcessPoolExecutor
+        self.workers = workers
+        self.pool = ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"))
+        warm = [(np.zeros((1, 8), np.float32), [0], 1.0, 0, 0)] * workers
+        list(self.pool.map(_sample_block, warm, timeout=300))
+
+    def sample_rows(self, logits, temperature, seed, step):
+        P = logits.shape[0]
+        blocks = [b for b in np.array_split(np.arange(P), self.workers) if b.size]
+        parts = list(self.pool.map(_sample_block, [(logits[b], b, temperature, seed, step)
+                                                   for b in blocks], timeout=600))
+        H = np.concatenate([h for h, _ in parts])
+        tok = np.concatenate([t for _, t in parts])
+        return H, tok
+
+    def close(self):
+        self.pool.shutdown(wait=True)
+
+
 def cpu_baseline(shape, x, layer_inputs, logits, sampler_shape):
     """The oracle, untuned, on a bounded sample of the same workload: whole MoE layers of the
     stack (every token, every routed expert; ``layer_inputs`` = [(router, weights), ...]) and
-    whole sampler steps (every row)."""
+    whole sampler steps (every row), on every core of the host share."""
     from threadpoolctl import threadpool_limits
-    from oracle import moe as omoe, sampler as osamp
+    from oracle import moe as omoe
     from block_diffusion_lm_router_amd import workloads
-    threads = min(os.cpu_count() or 1, 16)
+    threads = host_cores()
+    pool = SamplerPool(threads)
     gu, dn = workloads.expert_bytes(shape)
     T = shape.tokens
     P = logits.shape[0]
@@ -99,8 +153,9 @@ def cpu_baseline(shape, x, layer_inputs, logits, sampler_shape):
                           + T * shape.experts * 4 + 2 * T * shape.top_k * 4)
         t1 = time.perf_counter()
         for step in range(BASELINE_STEPS):
-            osamp.sample_rows(logits, sampler_shape.temperature, sampler_shape.seed, step)
+            pool.sample_rows(logits, sampler_shape.temperature, sampler_shape.seed, step)
         t2 = time.perf_counter()
+    pool.close()
     samp_bytes = BASELINE_STEPS * (P * sampler_shape.vocab * 4 + P * 4 * 4)
     secs = t2 - t0
     return {
@@ -112,15 +167,17 @@ def cpu_baseline(shape, x, layer_inputs, logits, sampler_shape):
                    f"tokens, {touched} experts touched, {ffn_bytes / 1e6:.1f} MB) in "
                    f"{t1 - t0:.2f} s, then {BASELINE_STEPS} sampler steps (entropy + two-level "
                    f"gumbel draw) over all {P} rows ({samp_bytes / 1e6:.1f} MB) in "
-                   f"{t2 - t1:.2f} s; rate = algorithmic bytes / wall time, same byte "
+                   f"{t2 - t1:.2f} s on {threads} cores (BLAS threads for the layers, worker "
+                   f"processes over row blocks for the sampler); rate = algorithmic bytes / wall time, same byte "
                    f"accounting as the GPU figure"),
     }
 
 
 def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=50):
-    """Live per-launch timings of the path's parts beside the step: each call bracketed by its
-    own pair of events on the launch stream, inputs alternating between two copies (or two
-    layers) so the 256 MB last-level cache cannot serve a repeat; median over n calls.
+    """Live timings of the path's parts beside the step: n calls back to back between one
+    event pair on the launch stream (an event between calls would leave the GPU idle for
+    several microseconds around it), inputs alternating between two copies (or two layers) so
+    the 256 MB last-level cache cannot serve a repeat; the mean time per call.
 
     * ffn_layer_uniform: one whole FFN layer (route, gate/up, down, combine) at the 256-token
       canvas with uniform N(0, 1) router logits (every expert touched);
@@ -139,22 +196,19 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=50):
     P, V = logits.shape
     out = {}
 
-    def timed(name, fns, alg_bytes, pre=None):
-        evs = []
-        for i in range(n + 3):
-            if pre is not None:
-                pre()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+    def timed(name, fns, alg_bytes):
+        for i in range(4):
             fns[i % len(fns)]()
-            b.record(stream)
-            if i >= 3:
-                evs.append((a, b))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fns[i % len(fns)]()
+        b.record(stream)
         torch.cuda.synchronize()
-        us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+        us = a.elapsed_time(b) * 1e3 / n
         gbs = alg_bytes / (us * 1e-6) / 1e9
-        out[name] = {"us_p50": round(us, 2), "alg_bytes": int(alg_bytes), "GB/s": round(gbs, 1),
-                     "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        out[name] = {"us": round(us, 2), "calls": n, "alg_bytes": int(alg_bytes),
+                     "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
     router = torch.from_numpy(workloads.make_router_logits(shape)).cuda()
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
@@ -200,19 +254,21 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=50):
     logits2 = logits.clone()
     frozen = torch.zeros(P, dtype=torch.uint8, device="cuda")
     canvas = torch.zeros(P, dtype=torch.int32, device="cuda")
+    # The sampler steps run with every row unfrozen and no frozen set or canvas recorded (as
+    # in the sampler workload), so that every call does the same work.
     tok = torch.empty(P, dtype=torch.int32, device="cuda")
     H = torch.empty(P, dtype=torch.float32, device="cuda")
     acc = torch.empty(P, dtype=torch.uint8, device="cuda")
     cnt = torch.empty(1, dtype=torch.int32, device="cuda")
-    samp_bytes = P * V * 4 + P * (4 + 4 + 1 + 1 + 4)
+    samp_bytes = P * V * 4 + P * (4 + 4 + 1) + 4
     timed("sampler_entropy_bound",
           [bd.bind(bd.diffusion_sample_step, lg, sshape.temperature, sshape.bound, sshape.seed, 0,
-                   frozen, canvas, tok, H, acc, cnt, sws) for lg in (logits, logits2)],
-          samp_bytes, pre=frozen.zero_)
+                   None, None, tok, H, acc, cnt, sws) for lg in (logits, logits2)],
+          samp_bytes)
     timed("sampler_confidence",
           [bd.bind(bd.diffusion_sample_step_confidence, lg, sshape.temperature, 0.9, sshape.seed,
-                   0, frozen, canvas, tok, H, acc, cnt, sws) for lg in (logits, logits2)],
-          samp_bytes, pre=frozen.zero_)
+                   0, None, None, tok, H, acc, cnt, sws) for lg in (logits, logits2)],
+          samp_bytes)
     del logits2
 
     h_np, wn_np, wr_np = workloads.make_norm_router(shape)
@@ -229,9 +285,9 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=50):
     timed("canvas_init", [bd.bind(bd.diffusion_canvas_init, canvas, prev, frozen, state, V, 0, 0)],
           P * (4 + 4 + 1) + 16)
     # a block that never ends inside the timed calls (threshold and budget out of reach)
+    frozen.zero_()
     timed("loop_update", [bd.bind(bd.diffusion_loop_update, tok, canvas, prev, frozen, state,
-                                  1 << 30, 1 << 30)], P * (4 + 4 + 4 + 4 + 1) + 32,
-          pre=frozen.zero_)
+                                  1 << 30, 1 << 30)], P * (4 + 4 + 4 + 4 + 1) + 32)
     return out
 
 
@@ -357,7 +413,7 @@ def main_layer(args):
         log("timing the CPU oracle on a bounded sample")
         from threadpoolctl import threadpool_limits
         from oracle import moe as omoe
-        threads = min(os.cpu_count() or 1, 16)
+        threads = host_cores()
         secs = 0.0
         with threadpool_limits(limits=threads):
             for l in range(BASELINE_LAYERS):
@@ -414,16 +470,19 @@ def main_sampler(args):
         log("timing the CPU oracle on a bounded sample")
         from oracle import sampler as osamp
         n_steps = 10
+        threads = host_cores()
+        pool = SamplerPool(threads)
         t0 = time.perf_counter()
         for st in range(n_steps):
-            H_ref, _ = osamp.sample_rows(lg_np, sshape.temperature, sshape.seed, st)
+            H_ref, _ = pool.sample_rows(lg_np, sshape.temperature, sshape.seed, st)
             osamp.accept(H_ref.astype(np.float32), sshape.bound)
         secs = time.perf_counter() - t0
+        pool.close()
         rec["cpu_baseline"] = {"value": round(n_steps * alg / secs / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle",
+                               "cores": threads, "kind": "oracle",
                                "sample": f"numpy fp64 oracle: {n_steps} whole sampler steps over all "
-                                         f"{P} rows in {secs:.2f} s (numpy element-wise, one "
-                                         f"thread); same byte accounting"}
+                                         f"{P} rows in {secs:.2f} s (rows split over {threads} "
+                                         f"worker processes); same byte accounting"}
     print(json.dumps(rec), flush=True)
 
 
@@ -498,15 +557,17 @@ def main():
                       bd.bind(bd.moe_w4a16_down, w, T, o, ws),
                       bd.bind(bd.moe_combine_fixed_order, o, tw, y)))
     total = args.warmup + args.steps
-    n_acc = torch.zeros(total + args.steps, dtype=torch.int32, device="cuda")
+    n_acc = torch.zeros(total + 2 * args.steps, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # The gate/up kernel's in-step duration, by difference: timed step j brackets with one event
-    # pair the routing and gate/up launches of layer (j // 2) mod L when j is odd and the
-    # routing launch alone of the same layer when j is even.  A timing event leaves the GPU idle
-    # for several microseconds around the launches next to it (the trace shows no gap between
-    # unmarked launches), the same in both brackets, so the mean of the odd intervals minus
-    # the mean of the even ones is the gate/up launch as it runs inside the step.
+    # The gate/up kernel's in-step duration, by difference, from a third pass after the timed
+    # region (the timed region itself holds no event but its two ends): step j of that pass
+    # brackets with one event pair the routing and gate/up launches of layer (j // 2) mod L
+    # when j is odd and the routing launch alone of the same layer when j is even.  A timing
+    # event leaves the GPU idle for several microseconds around the launches next to it (the
+    # trace shows no gap between unmarked launches), the same in both brackets, so the mean of
+    # the odd intervals minus the mean of the even ones is the gate/up launch as it runs
+    # inside the step.
     marks = [((j // 2) % len(layers), j % 2 == 1,
               (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
              for j in range(args.steps)]
@@ -537,7 +598,7 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.warmup, total):
-        step(i, marks[i - args.warmup])
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -551,6 +612,11 @@ def main():
         step_ev[i - total + 1].record(stream)
     torch.cuda.synchronize()
     per_step = np.array([a.elapsed_time(b) for a, b in zip(step_ev[:-1], step_ev[1:])])
+
+    # Third pass: the gate/up difference brackets (see marks above).
+    for i in range(total + args.steps, total + 2 * args.steps):
+        step(i, marks[i - total - args.steps])
+    torch.cuda.synchronize()
 
     # Unfrozen rows seen by each timed step's sampler, from the device's acceptance counts.
     counts = n_acc.cpu().numpy()

@@ -15,6 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbdstep.so")
 
 BD_SAMPLE_CHUNK = 1024
+BD_MOE_ITEM_TOKENS = 32
 
 _STATUS = {0: "ok", 1: "BD_ERR_NULL", 2: "BD_ERR_SHAPE", 3: "BD_ERR_ALIGN",
            4: "BD_ERR_WORKSPACE", 5: "BD_ERR_UNSUPPORTED", 6: "BD_ERR_HIP"}
@@ -55,6 +56,7 @@ SIGNATURES = {
     "bd_abi_version": (_I, []),
     "bd_status_string": (ctypes.c_char_p, [_I]),
     "bd_moe_workspace_size": (_SZ, [_I, _W]),
+    "bd_moe_w4a16_ffn_workspace_size": (_SZ, [_I, _W]),
     "bd_moe_packed_size": (_SZ, [_W, _I]),
     "moe_w4a16_prepare": (_I, [_W, _P, _P, _P]),
     "moe_route_topk": (_I, [_W, _I, _P, _P, _P, _P, _SZ, _P]),
@@ -157,6 +159,20 @@ def _ptr(t, dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, shape, name, what):
+    """Raise ValueError unless tensor t has exactly `shape` (checked before any pointer is
+    taken, so a mis-shaped tensor never reaches the kernels)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _at_least(t, n, name, what):
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{what}: {name} needs at least {n} elements, got {t.numel()}")
+
+
 class MoeWeights:
     """Device tensors of one layer's packed expert weights plus the C struct over them."""
 
@@ -176,6 +192,15 @@ class MoeWeights:
             down_group_size = self.d_ff // tensors["down_scale"].shape[-1]
         self.top_k, self.group_size, self.down_group_size = top_k, group_size, down_group_size
         self.affine = affine
+        E, f, d = self.num_experts, self.d_ff, self.d_model
+        want = {"gate_up_q": (E, 2 * f, d // 2),
+                "gate_up_scale": (E, 2 * f, d // group_size),
+                "gate_up_zero": (E, 2 * f, d // group_size),
+                "down_q": (E, d, f // 2),
+                "down_scale": (E, d, f // down_group_size),
+                "down_zero": (E, d, f // down_group_size)}
+        for key, shape in want.items():
+            _shape(tensors[key], shape, key, "MoeWeights")
         dtypes = {"gate_up_q": torch.uint8, "down_q": torch.uint8}
         ptrs = {k: _ptr(tensors[k], dtypes.get(k, torch.float16), k) for k in self.KEYS}
         self.c = MoeWeightsC(E, top_k, self.d_model, self.d_ff, group_size,
@@ -241,6 +266,10 @@ def moe_workspace(T, w: MoeWeights, device="cuda"):
 
 def moe_route_topk(w, router_logits, topk_ids, topk_weights, workspace):
     T = router_logits.shape[0]
+    what = "moe_route_topk"
+    _shape(router_logits, (T, w.num_experts), "router_logits", what)
+    _shape(topk_ids, (T, w.top_k), "topk_ids", what)
+    _shape(topk_weights, (T, w.top_k), "topk_weights", what)
     return _invoke("moe_route_topk", w.ref(), T,
                    _ptr(router_logits, torch.float32, "router_logits"),
                    _ptr(topk_ids, torch.int32, "topk_ids"),
@@ -249,16 +278,24 @@ def moe_route_topk(w, router_logits, topk_ids, topk_weights, workspace):
 
 
 def moe_w4a16_gate_up(w, x, workspace):
+    _shape(x, (x.shape[0], w.d_model), "x", "moe_w4a16_gate_up")
     return _invoke("moe_w4a16_gate_up", w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
 
 
 def moe_w4a16_down(w, T, expert_out, workspace):
+    _shape(expert_out, (T, w.top_k, w.d_model), "expert_out", "moe_w4a16_down")
     return _invoke("moe_w4a16_down", w.ref(), T, _ptr(expert_out, torch.float32, "expert_out"),
                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
 
 
 def moe_w4a16_ffn(w, x, router_logits, topk_ids, topk_weights, expert_out, workspace):
+    T, what = x.shape[0], "moe_w4a16_ffn"
+    _shape(x, (T, w.d_model), "x", what)
+    _shape(router_logits, (T, w.num_experts), "router_logits", what)
+    _shape(topk_ids, (T, w.top_k), "topk_ids", what)
+    _shape(topk_weights, (T, w.top_k), "topk_weights", what)
+    _shape(expert_out, (T, w.top_k, w.d_model), "expert_out", what)
     return _invoke("moe_w4a16_ffn", w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
                    _ptr(router_logits, torch.float32, "router_logits"),
                    _ptr(topk_ids, torch.int32, "topk_ids"),
@@ -268,7 +305,11 @@ def moe_w4a16_ffn(w, x, router_logits, topk_ids, topk_weights, expert_out, works
 
 
 def moe_combine_fixed_order(expert_out, topk_weights, y):
+    if expert_out.dim() != 3:
+        raise ValueError("moe_combine_fixed_order: expert_out must be [T, k, d]")
     T, k, d = expert_out.shape
+    _shape(topk_weights, (T, k), "topk_weights", "moe_combine_fixed_order")
+    _shape(y, (T, d), "y", "moe_combine_fixed_order")
     return _invoke("moe_combine_fixed_order", _ptr(expert_out, torch.float32, "expert_out"),
                    _ptr(topk_weights, torch.float32, "topk_weights"), T, k, d,
                    _ptr(y, torch.float16, "y"), _stream())
@@ -303,9 +344,23 @@ def sample_workspace(P, V, device="cuda"):
     return torch.zeros(sample_workspace_size(P, V), dtype=torch.uint8, device=device)
 
 
+def _rows(what, P, **named):
+    """Every named per-position tensor must be [P]."""
+    for name, t in named.items():
+        _shape(t, (P,), name, what)
+
+
+def _logits_shape(logits, what):
+    if logits.dim() != 2:
+        raise ValueError(f"{what}: logits must be [P, V]")
+    return logits.shape
+
+
 def diffusion_sample_entropy(logits, temperature, seed, step, frozen, tokens_out, entropy_out,
                              workspace):
-    P, V = logits.shape
+    P, V = _logits_shape(logits, "diffusion_sample_entropy")
+    _rows("diffusion_sample_entropy", P, frozen=frozen, tokens_out=tokens_out,
+          entropy_out=entropy_out)
     return _invoke("diffusion_sample_entropy", _ptr(logits, torch.float32, "logits"), P, V,
                    float(temperature), int(seed), int(step), _ptr(frozen, torch.uint8, "frozen"),
                    _ptr(tokens_out, torch.int32, "tokens_out"),
@@ -316,6 +371,9 @@ def diffusion_sample_entropy(logits, temperature, seed, step, frozen, tokens_out
 def diffusion_accept_entropy_bound(entropy, tokens, bound, frozen, canvas, accept_out,
                                    num_accepted):
     P = entropy.shape[0]
+    _rows("diffusion_accept_entropy_bound", P, entropy=entropy, tokens=tokens, frozen=frozen,
+          canvas=canvas, accept_out=accept_out)
+    _at_least(num_accepted, 1, "num_accepted", "diffusion_accept_entropy_bound")
     return _invoke("diffusion_accept_entropy_bound", _ptr(entropy, torch.float32, "entropy"),
                    _ptr(tokens, torch.int32, "tokens"), P, float(bound),
                    _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
@@ -325,7 +383,10 @@ def diffusion_accept_entropy_bound(entropy, tokens, bound, frozen, canvas, accep
 
 def diffusion_sample_step(logits, temperature, entropy_bound, seed, step, frozen, canvas,
                           tokens_out, entropy_out, accept_out, num_accepted, workspace):
-    P, V = logits.shape
+    P, V = _logits_shape(logits, "diffusion_sample_step")
+    _rows("diffusion_sample_step", P, frozen=frozen, canvas=canvas, tokens_out=tokens_out,
+          entropy_out=entropy_out, accept_out=accept_out)
+    _at_least(num_accepted, 1, "num_accepted", "diffusion_sample_step")
     return _invoke("diffusion_sample_step", _ptr(logits, torch.float32, "logits"), P, V,
                    float(temperature), float(entropy_bound), int(seed), int(step),
                    _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
@@ -338,7 +399,9 @@ def diffusion_sample_step(logits, temperature, entropy_bound, seed, step, frozen
 
 def diffusion_sample_confidence(logits, temperature, seed, step, frozen, tokens_out, entropy_out,
                                 confidence_out, workspace):
-    P, V = logits.shape
+    P, V = _logits_shape(logits, "diffusion_sample_confidence")
+    _rows("diffusion_sample_confidence", P, frozen=frozen, tokens_out=tokens_out,
+          entropy_out=entropy_out, confidence_out=confidence_out)
     return _invoke("diffusion_sample_confidence", _ptr(logits, torch.float32, "logits"), P, V,
                    float(temperature), int(seed), int(step), _ptr(frozen, torch.uint8, "frozen"),
                    _ptr(tokens_out, torch.int32, "tokens_out"),
@@ -350,6 +413,9 @@ def diffusion_sample_confidence(logits, temperature, seed, step, frozen, tokens_
 def diffusion_accept_confidence(confidence, tokens, threshold, frozen, canvas, accept_out,
                                 num_accepted):
     P = confidence.shape[0]
+    _rows("diffusion_accept_confidence", P, confidence=confidence, tokens=tokens, frozen=frozen,
+          canvas=canvas, accept_out=accept_out)
+    _at_least(num_accepted, 1, "num_accepted", "diffusion_accept_confidence")
     return _invoke("diffusion_accept_confidence", _ptr(confidence, torch.float32, "confidence"),
                    _ptr(tokens, torch.int32, "tokens"), P, float(threshold),
                    _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
@@ -360,7 +426,10 @@ def diffusion_accept_confidence(confidence, tokens, threshold, frozen, canvas, a
 def diffusion_sample_step_confidence(logits, temperature, threshold, seed, step, frozen, canvas,
                                      tokens_out, confidence_out, accept_out, num_accepted,
                                      workspace):
-    P, V = logits.shape
+    P, V = _logits_shape(logits, "diffusion_sample_step_confidence")
+    _rows("diffusion_sample_step_confidence", P, frozen=frozen, canvas=canvas,
+          tokens_out=tokens_out, confidence_out=confidence_out, accept_out=accept_out)
+    _at_least(num_accepted, 1, "num_accepted", "diffusion_sample_step_confidence")
     return _invoke("diffusion_sample_step_confidence", _ptr(logits, torch.float32, "logits"), P,
                    V, float(temperature), float(threshold), int(seed), int(step),
                    _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
@@ -381,8 +450,8 @@ def canvas_length(max_canvas, min_canvas, remaining, full_canvas=False):
 
 def diffusion_canvas_init(canvas, prev_canvas, frozen, loop_state, vocab, seed, block):
     P = canvas.shape[0]
-    if loop_state.numel() < 4:
-        raise ValueError("loop_state needs 4 int32 elements")
+    _rows("diffusion_canvas_init", P, canvas=canvas, prev_canvas=prev_canvas, frozen=frozen)
+    _at_least(loop_state, 4, "loop_state", "diffusion_canvas_init")
     return _invoke("diffusion_canvas_init", _ptr(canvas, torch.int32, "canvas"),
                    _ptr(prev_canvas, torch.int32, "prev_canvas"), _ptr(frozen, torch.uint8, "frozen"),
                    _ptr(loop_state, torch.int32, "loop_state"), P, int(vocab), int(seed), int(block),
@@ -392,8 +461,9 @@ def diffusion_canvas_init(canvas, prev_canvas, frozen, loop_state, vocab, seed, 
 def diffusion_loop_update(tokens, canvas, prev_canvas, frozen, loop_state, stability_threshold,
                           max_steps, write_drafts=True):
     P = canvas.shape[0]
-    if loop_state.numel() < 4:
-        raise ValueError("loop_state needs 4 int32 elements")
+    _rows("diffusion_loop_update", P, tokens=tokens, canvas=canvas, prev_canvas=prev_canvas,
+          frozen=frozen)
+    _at_least(loop_state, 4, "loop_state", "diffusion_loop_update")
     return _invoke("diffusion_loop_update", _ptr(tokens, torch.int32, "tokens"),
                    _ptr(canvas, torch.int32, "canvas"), _ptr(prev_canvas, torch.int32, "prev_canvas"),
                    _ptr(frozen, torch.uint8, "frozen"), _ptr(loop_state, torch.int32, "loop_state"),

@@ -13,7 +13,6 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 int to_status(hipError_t err) { return err == hipSuccess ? BD_OK : BD_ERR_HIP; }
 
-hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int check_moe_shape(const bd_moe_weights* w, int T) {
   if (w == nullptr) return BD_ERR_NULL;
@@ -107,7 +106,7 @@ size_t bd_moe_packed_size(const bd_moe_weights* w, int matrix) {
 }
 
 int moe_w4a16_prepare(const bd_moe_weights* w, uint8_t* gate_up_packed, uint8_t* down_packed,
-                      void* stream) {
+                      hipStream_t stream) {
   int st = check_moe_shape(w, 1);
   if (st != BD_OK) return st;
   if (!gate_up_packed || !down_packed || !w->gate_up_q || !w->gate_up_scale ||
@@ -120,10 +119,10 @@ int moe_w4a16_prepare(const bd_moe_weights* w, uint8_t* gate_up_packed, uint8_t*
   gu.pk = nullptr;
   dn.pk = nullptr;
   st = to_status(bd::launch_pack(gu, true, w->num_experts, w->d_model, w->d_ff, gate_up_packed,
-                                 as_stream(stream)));
+                                 stream));
   if (st != BD_OK) return st;
   return to_status(bd::launch_pack(dn, false, w->num_experts, w->d_model, w->d_ff, down_packed,
-                                   as_stream(stream)));
+                                   stream));
 }
 
 size_t bd_moe_workspace_size(int T, const bd_moe_weights* w) {
@@ -131,8 +130,12 @@ size_t bd_moe_workspace_size(int T, const bd_moe_weights* w) {
   return bd::moe_workspace_bytes(T, w->num_experts, w->top_k, w->d_model, w->d_ff);
 }
 
+size_t bd_moe_w4a16_ffn_workspace_size(int T, const bd_moe_weights* w) {
+  return bd_moe_workspace_size(T, w);
+}
+
 int moe_route_topk(const bd_moe_weights* w, int T, const float* router_logits, int32_t* topk_ids,
-                   float* topk_weights, void* workspace, size_t workspace_bytes, void* stream) {
+                   float* topk_weights, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_moe_shape(w, T);
   if (st != BD_OK) return st;
   if (!router_logits || !topk_ids || !topk_weights) return BD_ERR_NULL;
@@ -143,11 +146,11 @@ int moe_route_topk(const bd_moe_weights* w, int T, const float* router_logits, i
   const bd::MoeWorkspace ws =
       bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_model, w->d_ff);
   return to_status(bd::launch_route(router_logits, T, w->num_experts, w->top_k, topk_ids,
-                                    topk_weights, ws, as_stream(stream)));
+                                    topk_weights, ws, stream));
 }
 
 int moe_w4a16_gate_up(const bd_moe_weights* w, int T, const uint16_t* x, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, hipStream_t stream) {
   int st = check_moe_shape(w, T);
   if (st != BD_OK) return st;
   if ((st = check_gate_up_weights(w)) != BD_OK) return st;
@@ -158,11 +161,11 @@ int moe_w4a16_gate_up(const bd_moe_weights* w, int T, const uint16_t* x, void* w
   const bd::MoeWorkspace ws =
       bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_model, w->d_ff);
   return to_status(bd::launch_gate_up(gate_up_of(w), w->num_experts, w->d_model, w->d_ff,
-                                      w->top_k, T, x, ws, as_stream(stream)));
+                                      w->top_k, T, x, ws, stream));
 }
 
 int moe_w4a16_down(const bd_moe_weights* w, int T, float* expert_out, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   size_t workspace_bytes, hipStream_t stream) {
   int st = check_moe_shape(w, T);
   if (st != BD_OK) return st;
   if ((st = check_down_weights(w)) != BD_OK) return st;
@@ -173,12 +176,12 @@ int moe_w4a16_down(const bd_moe_weights* w, int T, float* expert_out, void* work
   const bd::MoeWorkspace ws =
       bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_model, w->d_ff);
   return to_status(bd::launch_down(down_of(w), w->num_experts, w->d_model, w->d_ff, w->top_k, T,
-                                   expert_out, ws, as_stream(stream)));
+                                   expert_out, ws, stream));
 }
 
 int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x, const float* router_logits,
                   int32_t* topk_ids, float* topk_weights, float* expert_out, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  size_t workspace_bytes, hipStream_t stream) {
   int st = check_moe_shape(w, T);
   if (st != BD_OK) return st;
   if ((st = check_gate_up_weights(w)) != BD_OK) return st;
@@ -191,7 +194,7 @@ int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x, const float
   if (st != BD_OK) return st;
   const bd::MoeWorkspace ws =
       bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_model, w->d_ff);
-  hipStream_t s = as_stream(stream);
+  hipStream_t s = stream;
   hipError_t err = bd::launch_route(router_logits, T, w->num_experts, w->top_k, topk_ids,
                                     topk_weights, ws, s);
   if (err == hipSuccess)
@@ -204,32 +207,32 @@ int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x, const float
 }
 
 int moe_combine_fixed_order(const float* expert_out, const float* topk_weights, int T, int k,
-                            int d, uint16_t* y, void* stream) {
+                            int d, uint16_t* y, hipStream_t stream) {
   if (!expert_out || !topk_weights || !y) return BD_ERR_NULL;
   if (T < 1 || T > BD_MAX_TOKENS || k < 1 || k > BD_MAX_TOPK || d < 4 || d % 4 != 0)
     return BD_ERR_SHAPE;
   if (!aligned16(expert_out) || !aligned4(topk_weights) || !aligned16(y)) return BD_ERR_ALIGN;
-  return to_status(bd::launch_combine(expert_out, topk_weights, T, k, d, y, as_stream(stream)));
+  return to_status(bd::launch_combine(expert_out, topk_weights, T, k, d, y, stream));
 }
 
 int moe_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps, uint16_t* y,
-                void* stream) {
+                hipStream_t stream) {
   if (T < 1 || T > BD_MAX_TOKENS || d < 8 || d > BD_MAX_FEATURES || d % 8 != 0 ||
       !isfinite(eps) || eps < 0.f)
     return BD_ERR_SHAPE;
   if (!h || !weight || !y) return BD_ERR_NULL;
   if (!aligned16(h) || !aligned16(weight) || !aligned16(y)) return BD_ERR_ALIGN;
-  return to_status(bd::launch_rmsnorm(h, weight, T, d, eps, y, as_stream(stream)));
+  return to_status(bd::launch_rmsnorm(h, weight, T, d, eps, y, stream));
 }
 
 int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
-                      float* logits, void* stream) {
+                      float* logits, hipStream_t stream) {
   if (T < 1 || T > BD_MAX_TOKENS || E < 1 || E > BD_MAX_EXPERTS || d < 128 ||
       d > BD_MAX_FEATURES || d % 128 != 0)
     return BD_ERR_SHAPE;
   if (!x || !w_router || !logits) return BD_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_router) || !aligned4(logits)) return BD_ERR_ALIGN;
-  return to_status(bd::launch_router(x, w_router, T, d, E, logits, as_stream(stream)));
+  return to_status(bd::launch_router(x, w_router, T, d, E, logits, stream));
 }
 
 size_t bd_sample_workspace_size(int P, int V) {
@@ -240,7 +243,7 @@ size_t bd_sample_workspace_size(int P, int V) {
 int diffusion_sample_entropy(const float* logits, int P, int V, float temperature, uint64_t seed,
                              uint32_t step, const uint8_t* frozen, int32_t* tokens_out,
                              float* entropy_out, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             hipStream_t stream) {
   int st = check_sample_shape(P, V, temperature);
   if (st != BD_OK) return st;
   if (!logits || !tokens_out || !entropy_out) return BD_ERR_NULL;
@@ -249,26 +252,26 @@ int diffusion_sample_entropy(const float* logits, int P, int V, float temperatur
   if (st != BD_OK) return st;
   return to_status(bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
                                              tokens_out, entropy_out, nullptr, workspace,
-                                             as_stream(stream)));
+                                             stream));
 }
 
 int diffusion_accept_entropy_bound(const float* entropy, const int32_t* tokens, int P, float bound,
                                    uint8_t* frozen, int32_t* canvas, uint8_t* accept_out,
-                                   int32_t* num_accepted, void* stream) {
+                                   int32_t* num_accepted, hipStream_t stream) {
   if (P < 1 || P > BD_MAX_POSITIONS || !isfinite(bound)) return BD_ERR_SHAPE;
   if (!entropy || !tokens || !accept_out || !num_accepted) return BD_ERR_NULL;
   if (!aligned4(entropy) || !aligned4(tokens) || !aligned4(num_accepted) ||
       (canvas && !aligned4(canvas)))
     return BD_ERR_ALIGN;
   return to_status(bd::launch_accept(entropy, tokens, P, bound, frozen, canvas, accept_out,
-                                     num_accepted, as_stream(stream)));
+                                     num_accepted, stream));
 }
 
 int diffusion_sample_step(const float* logits, int P, int V, float temperature,
                           float entropy_bound, uint64_t seed, uint32_t step, uint8_t* frozen,
                           int32_t* canvas, int32_t* tokens_out, float* entropy_out,
                           uint8_t* accept_out, int32_t* num_accepted, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, hipStream_t stream) {
   int st = check_sample_shape(P, V, temperature);
   if (st != BD_OK) return st;
   if (!isfinite(entropy_bound)) return BD_ERR_SHAPE;
@@ -278,7 +281,7 @@ int diffusion_sample_step(const float* logits, int P, int V, float temperature,
     return BD_ERR_ALIGN;
   st = check_workspace(workspace, workspace_bytes, bd::sample_workspace_bytes(P, V));
   if (st != BD_OK) return st;
-  hipStream_t s = as_stream(stream);
+  hipStream_t s = stream;
   hipError_t err = bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
                                              tokens_out, entropy_out, nullptr, workspace, s);
   if (err == hipSuccess)
@@ -292,7 +295,7 @@ static bool threshold_ok(float threshold) { return threshold >= 0.f && threshold
 int diffusion_sample_confidence(const float* logits, int P, int V, float temperature,
                                 uint64_t seed, uint32_t step, const uint8_t* frozen,
                                 int32_t* tokens_out, float* entropy_out, float* confidence_out,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_sample_shape(P, V, temperature);
   if (st != BD_OK) return st;
   if (!logits || !tokens_out || !confidence_out) return BD_ERR_NULL;
@@ -303,19 +306,19 @@ int diffusion_sample_confidence(const float* logits, int P, int V, float tempera
   if (st != BD_OK) return st;
   return to_status(bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
                                              tokens_out, entropy_out, confidence_out, workspace,
-                                             as_stream(stream)));
+                                             stream));
 }
 
 int diffusion_accept_confidence(const float* confidence, const int32_t* tokens, int P,
                                 float threshold, uint8_t* frozen, int32_t* canvas,
-                                uint8_t* accept_out, int32_t* num_accepted, void* stream) {
+                                uint8_t* accept_out, int32_t* num_accepted, hipStream_t stream) {
   if (P < 1 || P > BD_MAX_POSITIONS || !threshold_ok(threshold)) return BD_ERR_SHAPE;
   if (!confidence || !tokens || !accept_out || !num_accepted) return BD_ERR_NULL;
   if (!aligned4(confidence) || !aligned4(tokens) || !aligned4(num_accepted) ||
       (canvas && !aligned4(canvas)))
     return BD_ERR_ALIGN;
   return to_status(bd::launch_accept_confidence(confidence, tokens, P, threshold, frozen, canvas,
-                                                accept_out, num_accepted, as_stream(stream)));
+                                                accept_out, num_accepted, stream));
 }
 
 int diffusion_sample_step_confidence(const float* logits, int P, int V, float temperature,
@@ -323,7 +326,7 @@ int diffusion_sample_step_confidence(const float* logits, int P, int V, float te
                                      uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
                                      float* confidence_out, uint8_t* accept_out,
                                      int32_t* num_accepted, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+                                     size_t workspace_bytes, hipStream_t stream) {
   int st = check_sample_shape(P, V, temperature);
   if (st != BD_OK) return st;
   if (!threshold_ok(threshold)) return BD_ERR_SHAPE;
@@ -334,7 +337,7 @@ int diffusion_sample_step_confidence(const float* logits, int P, int V, float te
     return BD_ERR_ALIGN;
   st = check_workspace(workspace, workspace_bytes, bd::sample_workspace_bytes(P, V));
   if (st != BD_OK) return st;
-  hipStream_t s = as_stream(stream);
+  hipStream_t s = stream;
   hipError_t err = bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
                                              tokens_out, nullptr, confidence_out, workspace, s);
   if (err == hipSuccess)
@@ -352,18 +355,18 @@ int bd_canvas_length(int max_canvas, int min_canvas, int remaining, int full_can
 
 int diffusion_canvas_init(int32_t* canvas, int32_t* prev_canvas, uint8_t* frozen,
                           int32_t* loop_state, int P, int vocab, uint64_t seed, uint32_t block,
-                          void* stream) {
+                          hipStream_t stream) {
   if (P < 1 || P > BD_MAX_POSITIONS || vocab < 1 || vocab > BD_MAX_VOCAB) return BD_ERR_SHAPE;
   if (!canvas || !prev_canvas || !frozen || !loop_state) return BD_ERR_NULL;
   if (!aligned4(canvas) || !aligned4(prev_canvas) || !aligned4(loop_state)) return BD_ERR_ALIGN;
   return to_status(bd::launch_canvas_init(canvas, prev_canvas, frozen, loop_state, P, vocab, seed,
-                                          block, as_stream(stream)));
+                                          block, stream));
 }
 
 int diffusion_loop_update(const int32_t* tokens, int32_t* canvas, int32_t* prev_canvas,
                           const uint8_t* frozen, int32_t* loop_state, int P,
                           int stability_threshold, int max_steps, int write_drafts,
-                          void* stream) {
+                          hipStream_t stream) {
   if (P < 1 || P > BD_MAX_POSITIONS || stability_threshold < 1 || max_steps < 1)
     return BD_ERR_SHAPE;
   if (!canvas || !prev_canvas || !frozen || !loop_state || (write_drafts && !tokens))
@@ -373,21 +376,21 @@ int diffusion_loop_update(const int32_t* tokens, int32_t* canvas, int32_t* prev_
     return BD_ERR_ALIGN;
   return to_status(bd::launch_loop_update(tokens, canvas, prev_canvas, frozen, loop_state, P,
                                           stability_threshold, max_steps, write_drafts ? 1 : 0,
-                                          as_stream(stream)));
+                                          stream));
 }
 
-int bd_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
+int bd_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
   if (!src || !dst) return BD_ERR_NULL;
   if (bytes % 16 != 0) return BD_ERR_SHAPE;
   if (!aligned16(src) || !aligned16(dst)) return BD_ERR_ALIGN;
-  return to_status(bd::launch_copy(src, dst, bytes, as_stream(stream)));
+  return to_status(bd::launch_copy(src, dst, bytes, stream));
 }
 
-int bd_hbm_read(const void* src, size_t bytes, uint32_t* checksum, void* stream) {
+int bd_hbm_read(const void* src, size_t bytes, uint32_t* checksum, hipStream_t stream) {
   if (!checksum || (!src && bytes)) return BD_ERR_NULL;
   if (bytes % 16 != 0) return BD_ERR_SHAPE;
   if (!aligned16(src) || !aligned16(checksum)) return BD_ERR_ALIGN;
-  return to_status(bd::launch_read(src, bytes, checksum, as_stream(stream)));
+  return to_status(bd::launch_read(src, bytes, checksum, stream));
 }
 
 }  // extern "C"

@@ -113,7 +113,31 @@ struct GemmArgs {
   float* o_out;            // down output [T*k][d_model]
   int out_ld;
   int affine;              // packed stream holds (scale, bias) of w = q s + b, not (scale, zero)
+  int E;                   // experts
+  int A;                   // assignments T * top_k of this call
+  int max_items;           // capacity of the work list
 };
+
+// Work item `item` of the list: (expert, first bucket position, tokens), every value clamped
+// into the ranges of this call, so that no workspace content can index past the caller's
+// buffers (a workspace routed for another shape gives wrong outputs, never a wild access).
+struct Item {
+  int e, pos0, mcount;
+};
+__device__ __forceinline__ int item_count(const GemmArgs& a) {
+  return min(max(a.items[0], 0), a.max_items);
+}
+__device__ __forceinline__ Item load_item(const GemmArgs& a, int item) {
+  Item it;
+  it.e = min(max(a.items[1 + 3 * item], 0), a.E - 1);
+  it.pos0 = min(max(a.items[2 + 3 * item], 0), a.A - 1);
+  it.mcount = min(max(a.items[3 + 3 * item], 1), min(kItemTokens, a.A - it.pos0));
+  return it;
+}
+// Assignment t*k + j at a bucket position, clamped into [0, A).
+__device__ __forceinline__ int perm_at(const GemmArgs& a, int pos) {
+  return min(max(a.perm[pos], 0), a.A - 1);
+}
 
 // The masks and the magic exponent are passed in registers (see DequantConsts) so that each
 // (w & mask) | magic is one v_and_or_b32.
@@ -252,7 +276,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, i
   const uint16_t* xsrc;
   {
     const int mm = min(xm, mcount - 1);                         // padding rows re-read a valid row
-    const int row = GATED ? a.perm[pos0 + mm] / a.top_k : pos0 + mm;
+    const int row = GATED ? perm_at(a, pos0 + mm) / a.top_k : pos0 + mm;
     xsrc = a.act + (size_t)row * a.K;   // both activations are stored k-permuted
   }
   const int xchunk = (lane % kXChunks) ^ xswz(xm);
@@ -410,7 +434,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, i
         const _Float16 h16 = (_Float16)hv;
         a.h_out[(size_t)(pos0 + m) * a.d_ff + pcol] = __builtin_bit_cast(uint16_t, h16);
       } else {
-        const int slot = a.perm[pos0 + m];
+        const int slot = perm_at(a, pos0 + m);
         const int row = tile * kRowsPerBlock + rg * 32 + n;
         a.o_out[(size_t)slot * a.out_ld + row] = totA[mt][r];
         a.o_out[(size_t)slot * a.out_ld + row + 16] = totB[mt][r];
@@ -426,10 +450,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(GemmArgs a) {
   const int local = b / kXcds;
   const int item = (local / a.tiles) * kXcds + (b % kXcds);
   const int tile = local % a.tiles;
-  if (item >= a.items[0]) return;
-  const int e = a.items[1 + 3 * item];
-  const int pos0 = a.items[2 + 3 * item];
-  const int mcount = a.items[3 + 3 * item];
+  if (item >= item_count(a)) return;
+  const Item it = load_item(a, item);
+  const int e = it.e, pos0 = it.pos0, mcount = it.mcount;
   if (kItemTokens > 16 && mcount > 16)
     gemm_item<GATED, (kItemTokens > 16 ? 2 : 1)>(a, lds, e, pos0, mcount, tile);
   else
@@ -524,6 +547,17 @@ __device__ __forceinline__ void group_mfma(const u32x4_t& wa, const u32x4_t& wb,
   }
 }
 
+#ifndef BD_NT_WEIGHTS
+#define BD_NT_WEIGHTS 0
+#endif
+// One 16-byte load of the packed weight stream.
+__device__ __forceinline__ u32x4_t wload(const char* p) {
+  if constexpr (BD_NT_WEIGHTS)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  else
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+
 struct PkStage {
   u32x4_t wa, wb, sz, x;
 };
@@ -557,14 +591,22 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
   const int xm = (tid >> 4) & (NMT * 16 - 1);
   const int xc = tid & 15;
   const bool x_writer = tid < NMT * 256;
+  // Gate/up rows index x [T][K] (T * K * 2 < 2^32 bytes), so the offset of the row stays a
+  // 32-bit lane offset from the block-uniform base; down rows index h [T * k][K], which can
+  // pass 2^32 bytes, so the row's address is formed in 64 bits.
+  const char* act = reinterpret_cast<const char*>(a.act);
   uint32_t x_off;
   {
     const int mm = min(xm, mcount - 1);
-    const int row = GATED ? a.perm[pos0 + mm] / a.top_k : pos0 + mm;
-    x_off = ((uint32_t)row * (uint32_t)a.K + xc * 8) * 2;
+    const int row = GATED ? perm_at(a, pos0 + mm) / a.top_k : pos0 + mm;
+    if constexpr (GATED) {
+      x_off = ((uint32_t)row * (uint32_t)a.K + xc * 8) * 2;
+    } else {
+      act += (size_t)row * a.K * 2;
+      x_off = xc * 16;
+    }
   }
   const bool x_tail = xc * 8 >= (a.K & 127);             // chunk past K in a half stage
-  const char* act = reinterpret_cast<const char*>(a.act);
   const int xdst = xm * kXRowBytes + ((xc ^ xswz(xm)) << 4);
 
   auto load = [&](int c) {
@@ -574,9 +616,9 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
     const uint32_t xo = x_off + ((cl * kStageK * 2 + 256 > a.K * 2 && x_tail) ? 0u : (uint32_t)cl * kStageK * 2);
     PkStage r;
     r.x = *reinterpret_cast<const u32x4_t*>(act + xo);
-    r.wa = *reinterpret_cast<const u32x4_t*>(st + wa_off);
-    r.wb = *reinterpret_cast<const u32x4_t*>(st + wa_off + 1024);
-    r.sz = *reinterpret_cast<const u32x4_t*>(st + sz_off);
+    r.wa = wload(st + wa_off);
+    r.wb = wload(st + wa_off + 1024);
+    r.sz = wload(st + sz_off);
     return r;
   };
   auto put_x = [&](const PkStage& r, int slot) {
@@ -651,7 +693,7 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
         const _Float16 h16 = (_Float16)hv;
         a.h_out[(size_t)(pos0 + m) * a.d_ff + pcol] = __builtin_bit_cast(uint16_t, h16);
       } else {
-        const int slot = a.perm[pos0 + m];
+        const int slot = perm_at(a, pos0 + m);
         const int row = tile * kPkRows + wave * 32 + n;
         a.o_out[(size_t)slot * a.out_ld + row] = totA[mt][r];
         a.o_out[(size_t)slot * a.out_ld + row + 16] = totB[mt][r];
@@ -669,15 +711,14 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
   // tile of neighbouring items start together, and all but the first read the tile's stream
   // from that XCD's L2.
   const int b = blockIdx.x;
-  const int n_items = a.items[0];
+  const int n_items = item_count(a);
   const int per = (n_items + kXcds - 1) / kXcds;
   const int local = b / kXcds;
   const int tile = local / per;
   const int item = (b % kXcds) * per + local % per;
   if (tile >= a.tiles || item >= n_items) return;
-  const int e = a.items[1 + 3 * item];
-  const int pos0 = a.items[2 + 3 * item];
-  const int mcount = a.items[3 + 3 * item];
+  const Item it = load_item(a, item);
+  const int e = it.e, pos0 = it.pos0, mcount = it.mcount;
   if (mcount > 16)
     packed_item<GATED, 2, NSC, AFF>(a, lds, e, pos0, mcount, tile);
   else
@@ -723,9 +764,9 @@ __device__ __forceinline__ void down_resident_item(const GemmArgs& a, char* lds,
   auto load = [&](int f) {
     const char* st = pk + (size_t)min(f, F - 1) * kPkStage;
     PkW r;
-    r.wa = *reinterpret_cast<const u32x4_t*>(st + wa_off);
-    r.wb = *reinterpret_cast<const u32x4_t*>(st + wa_off + 1024);
-    r.sz = *reinterpret_cast<const u32x4_t*>(st + sz_off);
+    r.wa = wload(st + wa_off);
+    r.wb = wload(st + wa_off + 1024);
+    r.sz = wload(st + sz_off);
     return r;
   };
 
@@ -737,7 +778,7 @@ __device__ __forceinline__ void down_resident_item(const GemmArgs& a, char* lds,
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mt * 16 + kb * 4 + r;
-      slot[mt][r] = a.perm[pos0 + min(m, mcount - 1)];
+      slot[mt][r] = perm_at(a, pos0 + min(m, mcount - 1));
       if (m >= mcount) slot[mt][r] = -1;
     }
 
@@ -832,15 +873,14 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_down_resident_kernel(GemmAr
   // Same XCD-aware order as the staged kernel, over (item, group of tiles).
   const int b = blockIdx.x;
   const int groups = (a.tiles + kDownTilesPerBlock - 1) / kDownTilesPerBlock;
-  const int n_items = a.items[0];
+  const int n_items = item_count(a);
   const int per = (n_items + kXcds - 1) / kXcds;
   const int local = b / kXcds;
   const int grp = local / per;
   const int item = (b % kXcds) * per + local % per;
   if (grp >= groups || item >= n_items) return;
-  const int e = a.items[1 + 3 * item];
-  const int pos0 = a.items[2 + 3 * item];
-  const int mcount = a.items[3 + 3 * item];
+  const Item it = load_item(a, item);
+  const int e = it.e, pos0 = it.pos0, mcount = it.mcount;
   const int tile0 = grp * kDownTilesPerBlock;
   const int ntiles = min(kDownTilesPerBlock, a.tiles - tile0);
   if (mcount > 16)
@@ -982,7 +1022,9 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.h_out = ws.h;
   a.o_out = nullptr;
   a.out_ld = d_ff;
-  (void)E;
+  a.E = E;
+  a.A = T * top_k;
+  a.max_items = ws.max_items;
   // The expert buckets and the work list are in ws from the routing launch.  The packed
   // kernel reorders x in registers; the tile kernel needs a reordered copy first.
   if (gu.pk) {
@@ -1017,8 +1059,9 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
   a.h_out = nullptr;
   a.o_out = expert_out;
   a.out_ld = d_model;
-  (void)E;
-  (void)T;
+  a.E = E;
+  a.A = T * top_k;
+  a.max_items = ws.max_items;
   if (dn.pk) {
     a.tiles = pk_tiles(false, d_model, d_ff);
     launch_packed<false>(a, ws.max_items, stream);

@@ -20,8 +20,8 @@
  *  - Every pointer argument except `workspace` sizes and host structs is a DEVICE
  *    pointer into memory the caller owns.  The library allocates nothing, frees
  *    nothing and keeps no pointer after the call's work completes on the stream.
- *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
- *    All work is enqueued on it asynchronously; no call synchronises the host.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  All work is
+ *    enqueued on it asynchronously; no call synchronises the host.
  *  - fp16 values travel as uint16_t bit patterns.  Arrays are dense and row-major.
  *    The arrays read or written with vector accesses -- logits, x, expert_out, y, the
  *    packed weights with their scales and zero-points, and workspaces -- must be
@@ -36,6 +36,7 @@
 #ifndef BDSTEP_H
 #define BDSTEP_H
 
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 8
+#define BD_ABI_VERSION 9
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -53,6 +54,8 @@ extern "C" {
 #define BD_MAX_POSITIONS 1024
 #define BD_MAX_VOCAB (1 << 24)
 #define BD_MAX_FEATURES 4096
+/* Routed tokens per work item of the grouped GEMMs (see the routing state below). */
+#define BD_MOE_ITEM_TOKENS 32
 
 typedef enum {
   BD_OK = 0,
@@ -156,7 +159,7 @@ size_t bd_moe_packed_size(const bd_moe_weights* w, int matrix);
  * entry points to use them.
  */
 int moe_w4a16_prepare(const bd_moe_weights* w, uint8_t* gate_up_packed, uint8_t* down_packed,
-                      void* stream);
+                      hipStream_t stream);
 
 /*
  * Device workspace bytes needed by the MoE entry points for T tokens.  The same
@@ -164,8 +167,25 @@ int moe_w4a16_prepare(const bd_moe_weights* w, uint8_t* gate_up_packed, uint8_t*
  * moe_w4a16_down (a copy of the top-k ids, the expert buckets, the work list, the
  * permuted activations for raw weights and the fp16 GeGLU activations h [T*k][d_ff]).
  * Its contents need no initialisation.  Returns 0 if the shape is invalid.
+ *
+ * Routing state (written by moe_route_topk, read by the GEMMs; with A = T*k, up(n) = n
+ * rounded up to a multiple of 256 and M = A / BD_MOE_ITEM_TOKENS + min(E, A)):
+ *   byte 0:                    int32 offsets[E + 1]; offsets[e] = assignments routed to
+ *                              experts below e (offsets[E] = A)
+ *   byte up(4(E + 1)):         int32 items[1 + 3M]; items[0] = number of work items, then per
+ *                              item (expert, first bucket position, tokens): every touched
+ *                              expert in ascending order, its bucket cut into consecutive
+ *                              items of BD_MOE_ITEM_TOKENS positions (the last may be shorter)
+ *   byte up(4(E + 1)) + up(4(1 + 3M)):  int32 perm[A]; bucket position -> t*k + j, each
+ *                              expert's bucket in ascending t (a stable counting sort)
+ * The GEMMs clamp every index they read from the workspace into the ranges of the current
+ * call, so a workspace routed for another shape gives wrong outputs but no access outside the
+ * caller's buffers.
  */
 size_t bd_moe_workspace_size(int T, const bd_moe_weights* w);
+
+/* The same value under the name the hot-path contract gives it (moe_w4a16_ffn's workspace). */
+size_t bd_moe_w4a16_ffn_workspace_size(int T, const bd_moe_weights* w);
 
 /*
  * Routing: per token, the top_k experts by descending router logit (the lower expert
@@ -183,7 +203,7 @@ size_t bd_moe_workspace_size(int T, const bd_moe_weights* w);
  */
 int moe_route_topk(const bd_moe_weights* w, int T, const float* router_logits,
                    int32_t* topk_ids, float* topk_weights,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Gate/up grouped W4A16 GEMM with the GeGLU epilogue, over every touched expert in
@@ -202,7 +222,7 @@ int moe_route_topk(const bd_moe_weights* w, int T, const float* router_logits,
  *   x   fp16 [T][d_model]
  */
 int moe_w4a16_gate_up(const bd_moe_weights* w, int T, const uint16_t* x,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Down grouped W4A16 GEMM: o[t][j] = W_down[e] h_(t,j) for every assignment, written
@@ -212,12 +232,12 @@ int moe_w4a16_gate_up(const bd_moe_weights* w, int T, const uint16_t* x,
  *   expert_out  fp32 [T][k][d_model]   out
  */
 int moe_w4a16_down(const bd_moe_weights* w, int T, float* expert_out,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* moe_route_topk, moe_w4a16_gate_up and moe_w4a16_down in one call. */
 int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x,
                   const float* router_logits, int32_t* topk_ids, float* topk_weights,
-                  float* expert_out, void* workspace, size_t workspace_bytes, void* stream);
+                  float* expert_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Fixed-order weighted combine: y[t] = fp16( sum_{j=0}^{k-1} w[t][j] * o[t][j] ), the
@@ -232,7 +252,7 @@ int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x,
  *   y             fp16 [T][d]   out;  d % 4 == 0
  */
 int moe_combine_fixed_order(const float* expert_out, const float* topk_weights,
-                            int T, int k, int d, uint16_t* y, void* stream);
+                            int T, int k, int d, uint16_t* y, hipStream_t stream);
 
 /* ------------------------------------------------------------------ layer neighbours */
 
@@ -248,7 +268,7 @@ int moe_combine_fixed_order(const float* expert_out, const float* topk_weights,
  *   T in 1..BD_MAX_TOKENS; d in 8..BD_MAX_FEATURES with d % 8 == 0; eps finite, >= 0.
  */
 int moe_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps, uint16_t* y,
-                void* stream);
+                hipStream_t stream);
 
 /*
  * Router projection: logits[t][e] = sum_i x[t][i] * w_router[e][i], fp16 operands (exact
@@ -262,7 +282,7 @@ int moe_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float e
  *   T in 1..BD_MAX_TOKENS; E in 1..BD_MAX_EXPERTS; d in 128..BD_MAX_FEATURES, d % 128 == 0.
  */
 int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
-                      float* logits, void* stream);
+                      float* logits, hipStream_t stream);
 
 /* ------------------------------------------------------------------ sampler */
 
@@ -297,7 +317,7 @@ size_t bd_sample_workspace_size(int P, int V);
 int diffusion_sample_entropy(const float* logits, int P, int V, float temperature,
                              uint64_t seed, uint32_t step, const uint8_t* frozen,
                              int32_t* tokens_out, float* entropy_out,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Entropy-bound acceptance on one workgroup.  Candidates are the positions that are
@@ -319,14 +339,14 @@ int diffusion_sample_entropy(const float* logits, int P, int V, float temperatur
  */
 int diffusion_accept_entropy_bound(const float* entropy, const int32_t* tokens, int P,
                                    float bound, uint8_t* frozen, int32_t* canvas,
-                                   uint8_t* accept_out, int32_t* num_accepted, void* stream);
+                                   uint8_t* accept_out, int32_t* num_accepted, hipStream_t stream);
 
 /* diffusion_sample_entropy then diffusion_accept_entropy_bound on the same stream. */
 int diffusion_sample_step(const float* logits, int P, int V, float temperature,
                           float entropy_bound, uint64_t seed, uint32_t step,
                           uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
                           float* entropy_out, uint8_t* accept_out, int32_t* num_accepted,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Confidence-threshold variant of the sampler.  The same single streaming pass as
@@ -342,7 +362,7 @@ int diffusion_sample_step(const float* logits, int P, int V, float temperature,
 int diffusion_sample_confidence(const float* logits, int P, int V, float temperature,
                                 uint64_t seed, uint32_t step, const uint8_t* frozen,
                                 int32_t* tokens_out, float* entropy_out, float* confidence_out,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Confidence-threshold acceptance on one workgroup.  Candidates are the positions that
@@ -364,7 +384,7 @@ int diffusion_sample_confidence(const float* logits, int P, int V, float tempera
  */
 int diffusion_accept_confidence(const float* confidence, const int32_t* tokens, int P,
                                 float threshold, uint8_t* frozen, int32_t* canvas,
-                                uint8_t* accept_out, int32_t* num_accepted, void* stream);
+                                uint8_t* accept_out, int32_t* num_accepted, hipStream_t stream);
 
 /* diffusion_sample_confidence (no entropy output) then diffusion_accept_confidence on the
  * same stream. */
@@ -373,7 +393,7 @@ int diffusion_sample_step_confidence(const float* logits, int P, int V, float te
                                      uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
                                      float* confidence_out, uint8_t* accept_out,
                                      int32_t* num_accepted, void* workspace,
-                                     size_t workspace_bytes, void* stream);
+                                     size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------ denoising-loop driver */
 
@@ -397,7 +417,7 @@ int bd_canvas_length(int max_canvas, int min_canvas, int remaining, int full_can
  */
 int diffusion_canvas_init(int32_t* canvas, int32_t* prev_canvas, uint8_t* frozen,
                           int32_t* loop_state, int P, int vocab, uint64_t seed, uint32_t block,
-                          void* stream);
+                          hipStream_t stream);
 
 /*
  * The driver's update after one step's sampler call (one workgroup).  Unless loop_state
@@ -417,7 +437,7 @@ int diffusion_canvas_init(int32_t* canvas, int32_t* prev_canvas, uint8_t* frozen
 int diffusion_loop_update(const int32_t* tokens, int32_t* canvas, int32_t* prev_canvas,
                           const uint8_t* frozen, int32_t* loop_state, int P,
                           int stability_threshold, int max_steps, int write_drafts,
-                          void* stream);
+                          hipStream_t stream);
 
 /* ------------------------------------------------------------------ measurement */
 
@@ -426,7 +446,7 @@ int diffusion_loop_update(const int32_t* tokens, int32_t* canvas, int32_t* prev_
  * aligned) with a streaming kernel: the calibration for HBM traffic counters and the
  * achievable-bandwidth figure beside the 8 TB/s specification.
  */
-int bd_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
+int bd_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 /*
  * Streaming read of `bytes` bytes at src (bytes % 16 == 0; src and checksum 16-byte aligned,
@@ -437,7 +457,7 @@ int bd_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
  * the per-block partials); the caller owns both buffers.  src may be NULL when bytes == 0.
  */
 #define BD_HBM_READ_WORDS 2049
-int bd_hbm_read(const void* src, size_t bytes, uint32_t* checksum, void* stream);
+int bd_hbm_read(const void* src, size_t bytes, uint32_t* checksum, hipStream_t stream);
 
 #ifdef __cplusplus
 }

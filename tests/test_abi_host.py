@@ -47,6 +47,22 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
     assert set(_binding.SIGNATURES) == set(names)
 
 
+def test_workspace_size_under_both_names(lib):
+    w = _weights()
+    for T in (1, 64, 256, 4096):
+        n = lib.bd_moe_workspace_size(T, ctypes.byref(w))
+        assert n > 0 and lib.bd_moe_w4a16_ffn_workspace_size(T, ctypes.byref(w)) == n
+    assert lib.bd_moe_w4a16_ffn_workspace_size(0, ctypes.byref(w)) == 0
+
+
+def test_header_constants_match_the_binding():
+    from block_diffusion_lm_router_amd import _binding
+    text = open(HEADER).read()
+    for name in ("BD_MOE_ITEM_TOKENS", "BD_SAMPLE_CHUNK"):
+        value = int(re.search(rf"#define {name} (\d+)", text).group(1))
+        assert getattr(_binding, name) == value, name
+
+
 def test_version_and_status_strings(lib):
     version = int(re.search(r"#define BD_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
     assert lib.bd_abi_version() == version

@@ -442,3 +442,32 @@ def test_accept_counts_around_the_selection_steps(bd, bound, expect):
     assert ref_n == expect and cnt == expect and np.array_equal(acc, ref_mask)
     assert np.array_equal(acc, (np.arange(P) < expect).astype(np.uint8))
     assert np.array_equal(fr, ref_mask) and np.array_equal(cv, np.where(ref_mask == 1, tokens, 0))
+
+
+def test_full_size_step_repeats_bit_identical(bd):
+    """The sampler step at full size (the timed configuration), three runs on fresh frozen and
+    canvas state: tokens, entropy bits, acceptance mask, count, canvas and frozen set
+    identical every run."""
+    import torch
+    shape = workloads.SAMPLER
+    x = workloads.make_logits(shape)
+    P, V = x.shape
+    say("full-size sampler repeats")
+    logits = torch.from_numpy(x).cuda()
+    ws = bd.sample_workspace(P, V)
+    runs = []
+    for _ in range(3):
+        frozen = torch.zeros(P, dtype=torch.uint8, device="cuda")
+        frozen[::5] = 1
+        canvas = torch.full((P,), -7, dtype=torch.int32, device="cuda")
+        tok = torch.empty(P, dtype=torch.int32, device="cuda")
+        H = torch.empty(P, dtype=torch.float32, device="cuda")
+        acc = torch.empty(P, dtype=torch.uint8, device="cuda")
+        cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+        bd.diffusion_sample_step(logits, shape.temperature, shape.bound, shape.seed, 3, frozen,
+                                 canvas, tok, H, acc, cnt, ws)
+        torch.cuda.synchronize()
+        runs.append([t.cpu().numpy() for t in (tok, H, acc, cnt, canvas, frozen)])
+    for other in runs[1:]:
+        for a, b in zip(runs[0], other):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
