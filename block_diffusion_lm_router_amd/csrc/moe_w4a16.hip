@@ -495,10 +495,23 @@ static_assert(kSG == 2 && kItemTokens == 32 && kXRowBytes == 256, "packed stage 
 // products added to the running fp32 sums.  Asymmetric form: exact fp16 (q - z), the group's
 // MFMA sum scaled by its fp32 scale.  Affine form: fp16 q s + b, accumulated directly.
 // sz holds, per set, (scale g0, scale g1, zero or bias g0, zero or bias g1).
+// The zero-point constants of both groups of a stage for one row set, formed with two packed
+// ops: -(1024 + z) for the low nibbles and -(64 + z) for the high ones (see dequant8).
+struct ZeroPairs {
+  half2_t z1, z2;
+};
+__device__ __forceinline__ ZeroPairs zero_pairs(half4_t sz) {
+  const half2_t z = {sz[2], sz[3]};
+  const half2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+  const half2_t k64 = {(_Float16)64.f, (_Float16)64.f};
+  return ZeroPairs{-(k1024 + z), -(k64 + z)};
+}
+
 template <int NMT, bool AFF>
 __device__ __forceinline__ void group_mfma(const u32x4_t& wa, const u32x4_t& wb, half4_t szA,
-                                           half4_t szB, int j, const char* xt, int n, int kb,
-                                           float4_t (&totA)[NMT], float4_t (&totB)[NMT],
+                                           half4_t szB, const ZeroPairs& zpA,
+                                           const ZeroPairs& zpB, int j, const char* xt, int n,
+                                           int kb, float4_t (&totA)[NMT], float4_t (&totB)[NMT],
                                            const DequantConsts& dq) {
   half8_t bA0, bA1, bB0, bB1;
   float fsA = 0.f, fsB = 0.f;
@@ -510,9 +523,8 @@ __device__ __forceinline__ void group_mfma(const u32x4_t& wa, const u32x4_t& wb,
     bB0 = dequant8_affine(wb[2 * j], sB, oB, dq);
     bB1 = dequant8_affine(wb[2 * j + 1], sB, oB, dq);
   } else {
-    const _Float16 zA = szA[2 + j], zB = szB[2 + j];
-    const _Float16 za1 = -((_Float16)1024.f + zA), za2 = -((_Float16)64.f + zA);
-    const _Float16 zb1 = -((_Float16)1024.f + zB), zb2 = -((_Float16)64.f + zB);
+    const _Float16 za1 = zpA.z1[j], za2 = zpA.z2[j];
+    const _Float16 zb1 = zpB.z1[j], zb2 = zpB.z2[j];
     fsA = (float)szA[j];
     fsB = (float)szB[j];
     bA0 = dequant8(wa[2 * j], za1, za2, dq);
@@ -547,22 +559,26 @@ __device__ __forceinline__ void group_mfma(const u32x4_t& wa, const u32x4_t& wb,
   }
 }
 
-#ifndef BD_NT_WEIGHTS
-#define BD_NT_WEIGHTS 0
-#endif
-// One 16-byte load of the packed weight stream.
-__device__ __forceinline__ u32x4_t wload(const char* p) {
-  if constexpr (BD_NT_WEIGHTS)
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  else
-    return *reinterpret_cast<const u32x4_t*>(p);
+// Buffer loads: a block-uniform descriptor (base, byte range) in scalar registers, a lane
+// offset in one VGPR and the stage offset in a scalar register, so that a stage's loads cost
+// no vector address arithmetic; a read past the range returns zeros.  Word 3 of a gfx9
+// descriptor: raw 32-bit data, no swizzle.  AUX 2 marks the load nontemporal (the line is not
+// kept for reuse), used for weight streams that no other block reads.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
 }
 
 struct PkStage {
   u32x4_t wa, wb, sz, x;
 };
 
-template <bool GATED, int NMT, int NSC, bool AFF>
+template <bool GATED, int NMT, int NSC, bool AFF, bool NT>
 __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e, int pos0,
                                             int mcount, int tile) {
   const int tid = threadIdx.x;
@@ -577,10 +593,10 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
   const int rows_here = GATED ? min(128, a.d_ff - tile * 128) : min(kPkRows, a.R - tile * kPkRows);
   const bool valid = GATED ? wave * 16 < rows_here : wave * 32 < rows_here;
   const int lw = valid ? wave : wave - 4;              // whose stream this wave loads
-  // Loads address a block-uniform base plus a 32-bit lane offset, so that they take the
-  // scalar-base form and no 64-bit address registers are held per stream.
-  const char* pk = reinterpret_cast<const char*>(a.pk) +
-                   ((size_t)e * a.tiles + tile) * (size_t)NS * kPkStage;
+  // The (expert, tile) stream: one descriptor, the lane's offsets within a stage.
+  const uint32_t stream_bytes = (uint32_t)NS * kPkStage;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(a.pk + ((size_t)e * a.tiles + tile) * stream_bytes, stream_bytes);
   const uint32_t wa_off = ((lw * 2 + 0) * 64 + lane) * 16;
   const uint32_t sz_off = kPkWBytes + (lw * 16 + n) * 16;
 
@@ -591,34 +607,29 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
   const int xm = (tid >> 4) & (NMT * 16 - 1);
   const int xc = tid & 15;
   const bool x_writer = tid < NMT * 256;
-  // Gate/up rows index x [T][K] (T * K * 2 < 2^32 bytes), so the offset of the row stays a
-  // 32-bit lane offset from the block-uniform base; down rows index h [T * k][K], which can
-  // pass 2^32 bytes, so the row's address is formed in 64 bits.
-  const char* act = reinterpret_cast<const char*>(a.act);
+  // Activation rows: gate/up gathers token rows of x [T][K] (T * K * 2 < 2^32 bytes); down
+  // reads the item's consecutive rows of h [T * k][K] from the item's first row on.  The
+  // chunks past K in the half stage of an odd group count read whatever follows (or zeros past
+  // the range) and are never used.
+  const __amdgpu_buffer_rsrc_t xrs =
+      GATED ? make_rsrc(a.act, (uint32_t)(a.A / a.top_k) * (uint32_t)a.K * 2u)
+            : make_rsrc(a.act + (size_t)pos0 * a.K, (uint32_t)mcount * (uint32_t)a.K * 2u);
   uint32_t x_off;
   {
     const int mm = min(xm, mcount - 1);
-    const int row = GATED ? perm_at(a, pos0 + mm) / a.top_k : pos0 + mm;
-    if constexpr (GATED) {
-      x_off = ((uint32_t)row * (uint32_t)a.K + xc * 8) * 2;
-    } else {
-      act += (size_t)row * a.K * 2;
-      x_off = xc * 16;
-    }
+    const int row = GATED ? perm_at(a, pos0 + mm) / a.top_k : mm;
+    x_off = ((uint32_t)row * (uint32_t)a.K + xc * 8) * 2;
   }
-  const bool x_tail = xc * 8 >= (a.K & 127);             // chunk past K in a half stage
   const int xdst = xm * kXRowBytes + ((xc ^ xswz(xm)) << 4);
+  constexpr int kAux = NT ? 2 : 0;
 
   auto load = [&](int c) {
-    const int cl = min(c, NS - 1);
-    const char* st = pk + (size_t)cl * kPkStage;
-    // the half stage past an odd G re-reads the row's first chunk (never used)
-    const uint32_t xo = x_off + ((cl * kStageK * 2 + 256 > a.K * 2 && x_tail) ? 0u : (uint32_t)cl * kStageK * 2);
+    const uint32_t st = (uint32_t)min(c, NS - 1) * kPkStage;
     PkStage r;
-    r.x = *reinterpret_cast<const u32x4_t*>(act + xo);
-    r.wa = wload(st + wa_off);
-    r.wb = wload(st + wa_off + 1024);
-    r.sz = wload(st + sz_off);
+    r.x = bload<0>(xrs, x_off, (uint32_t)min(c, NS - 1) * kStageK * 2);
+    r.wa = bload<kAux>(wrs, wa_off, st);
+    r.wb = bload<kAux>(wrs, wa_off + 1024, st);
+    r.sz = bload<kAux>(wrs, sz_off, st);
     return r;
   };
   auto put_x = [&](const PkStage& r, int slot) {
@@ -636,11 +647,12 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
     // [scale g0, scale g1, zero g0, zero g1] of the lane's row in set A, then set B
     const half4_t szA = __builtin_bit_cast(half4_t, u32x2_t{r.sz[0], r.sz[1]});
     const half4_t szB = __builtin_bit_cast(half4_t, u32x2_t{r.sz[2], r.sz[3]});
+    const ZeroPairs zpA = zero_pairs(szA), zpB = zero_pairs(szB);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int g = 2 * c + j;
       if (g >= G) break;
-      group_mfma<NMT, AFF>(r.wa, r.wb, szA, szB, j, xt, n, kb, totA, totB, dq);
+      group_mfma<NMT, AFF>(r.wa, r.wb, szA, szB, zpA, zpB, j, xt, n, kb, totA, totB, dq);
     }
   };
 
@@ -719,10 +731,22 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
   if (tile >= a.tiles || item >= n_items) return;
   const Item it = load_item(a, item);
   const int e = it.e, pos0 = it.pos0, mcount = it.mcount;
-  if (mcount > 16)
-    packed_item<GATED, 2, NSC, AFF>(a, lds, e, pos0, mcount, tile);
-  else
-    packed_item<GATED, 1, NSC, AFF>(a, lds, e, pos0, mcount, tile);
+  // An expert whose tokens fit one work item has its stream read by this block alone: those
+  // loads are nontemporal.  An expert split over several items keeps them cached, so that its
+  // other items' blocks on the same XCD read the stream from L2.
+  const bool alone = (item == 0 || a.items[1 + 3 * (item - 1)] != a.items[1 + 3 * item]) &&
+                     (item + 1 >= n_items || a.items[1 + 3 * (item + 1)] != a.items[1 + 3 * item]);
+  if (mcount > 16) {
+    if (alone)
+      packed_item<GATED, 2, NSC, AFF, true>(a, lds, e, pos0, mcount, tile);
+    else
+      packed_item<GATED, 2, NSC, AFF, false>(a, lds, e, pos0, mcount, tile);
+  } else {
+    if (alone)
+      packed_item<GATED, 1, NSC, AFF, true>(a, lds, e, pos0, mcount, tile);
+    else
+      packed_item<GATED, 1, NSC, AFF, false>(a, lds, e, pos0, mcount, tile);
+  }
 }
 
 // ------------------------------------------------------------------ down, resident rows
@@ -757,16 +781,17 @@ __device__ __forceinline__ void down_resident_item(const GemmArgs& a, char* lds,
   const int NS = (G + 1) >> 1;
   const int F = ntiles * NS;                           // stages the block streams
   const DequantConsts dq = dequant_consts();
-  const char* pk = reinterpret_cast<const char*>(a.pk) +
-                   ((size_t)e * a.tiles + tile0) * (size_t)NS * kPkStage;
+  const uint32_t run_bytes = (uint32_t)F * kPkStage;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(a.pk + ((size_t)e * a.tiles + tile0) * (size_t)NS * kPkStage, run_bytes);
   const uint32_t wa_off = ((wave * 2 + 0) * 64 + lane) * 16;
   const uint32_t sz_off = kPkWBytes + (wave * 16 + n) * 16;
   auto load = [&](int f) {
-    const char* st = pk + (size_t)min(f, F - 1) * kPkStage;
+    const uint32_t st = (uint32_t)min(f, F - 1) * kPkStage;
     PkW r;
-    r.wa = wload(st + wa_off);
-    r.wb = wload(st + wa_off + 1024);
-    r.sz = wload(st + sz_off);
+    r.wa = bload<0>(wrs, wa_off, st);
+    r.wb = bload<0>(wrs, wa_off + 1024, st);
+    r.sz = bload<0>(wrs, sz_off, st);
     return r;
   };
 
@@ -826,10 +851,11 @@ __device__ __forceinline__ void down_resident_item(const GemmArgs& a, char* lds,
     const char* xt = lds + c * kPkXSlot;
     const half4_t szA = __builtin_bit_cast(half4_t, u32x2_t{r.sz[0], r.sz[1]});
     const half4_t szB = __builtin_bit_cast(half4_t, u32x2_t{r.sz[2], r.sz[3]});
+    const ZeroPairs zpA = zero_pairs(szA), zpB = zero_pairs(szB);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (2 * c + j >= G) break;
-      group_mfma<NMT, AFF>(r.wa, r.wb, szA, szB, j, xt, n, kb, totA, totB, dq);
+      group_mfma<NMT, AFF>(r.wa, r.wb, szA, szB, zpA, zpB, j, xt, n, kb, totA, totB, dq);
     }
   };
   auto store = [&](int tile) {
