@@ -71,6 +71,8 @@ SIGNATURES = {
     "diffusion_accept_entropy_bound": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
     "diffusion_sample_step": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P, _P, _P,
                                    _SZ, _P]),
+    "diffusion_sample_step_noalloc": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P,
+                                           _P, _P]),
     "diffusion_sample_confidence": (_I, [_P, _I, _I, _F, _U64, _U32, _P, _P, _P, _P, _P, _SZ,
                                          _P]),
     "diffusion_accept_confidence": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
@@ -395,6 +397,21 @@ def diffusion_sample_step(logits, temperature, entropy_bound, seed, step, frozen
                    _ptr(accept_out, torch.uint8, "accept_out"),
                    _ptr(num_accepted, torch.int32, "num_accepted"),
                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+
+
+def diffusion_sample_step_noalloc(logits, temperature, entropy_bound, seed, step, frozen, canvas,
+                                  tokens_out, entropy_out, accept_out, num_accepted):
+    P, V = _logits_shape(logits, "diffusion_sample_step_noalloc")
+    _rows("diffusion_sample_step_noalloc", P, frozen=frozen, canvas=canvas, tokens_out=tokens_out,
+          entropy_out=entropy_out, accept_out=accept_out)
+    _at_least(num_accepted, 1, "num_accepted", "diffusion_sample_step_noalloc")
+    return _invoke("diffusion_sample_step_noalloc", _ptr(logits, torch.float32, "logits"), P, V,
+                   float(temperature), float(entropy_bound), int(seed), int(step),
+                   _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
+                   _ptr(tokens_out, torch.int32, "tokens_out"),
+                   _ptr(entropy_out, torch.float32, "entropy_out"),
+                   _ptr(accept_out, torch.uint8, "accept_out"),
+                   _ptr(num_accepted, torch.int32, "num_accepted"), _stream())
 
 
 def diffusion_sample_confidence(logits, temperature, seed, step, frozen, tokens_out, entropy_out,

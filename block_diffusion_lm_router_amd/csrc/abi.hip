@@ -290,6 +290,30 @@ int diffusion_sample_step(const float* logits, int P, int V, float temperature,
   return to_status(err);
 }
 
+int diffusion_sample_step_noalloc(const float* logits, int P, int V, float temperature,
+                                  float entropy_bound, uint64_t seed, uint32_t step,
+                                  uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                                  float* entropy_out, uint8_t* accept_out, int32_t* num_accepted,
+                                  hipStream_t stream) {
+  int st = check_sample_shape(P, V, temperature);
+  if (st != BD_OK) return st;
+  if (!isfinite(entropy_bound)) return BD_ERR_SHAPE;
+  if (!logits || !tokens_out || !entropy_out || !accept_out || !num_accepted) return BD_ERR_NULL;
+  if (!aligned16(logits) || !aligned4(tokens_out) || !aligned4(entropy_out) ||
+      !aligned4(num_accepted) || (canvas && !aligned4(canvas)))
+    return BD_ERR_ALIGN;
+  void* workspace = nullptr;
+  const hipError_t got = bd::static_sample_scratch(bd::sample_workspace_bytes(P, V), &workspace);
+  if (got == hipErrorInvalidValue) return BD_ERR_WORKSPACE;
+  if (got != hipSuccess) return BD_ERR_HIP;
+  hipError_t err = bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
+                                             tokens_out, entropy_out, nullptr, workspace, stream);
+  if (err == hipSuccess)
+    err = bd::launch_accept(entropy_out, tokens_out, P, entropy_bound, frozen, canvas, accept_out,
+                            num_accepted, stream);
+  return to_status(err);
+}
+
 static bool threshold_ok(float threshold) { return threshold >= 0.f && threshold <= 1.f; }
 
 int diffusion_sample_confidence(const float* logits, int P, int V, float temperature,

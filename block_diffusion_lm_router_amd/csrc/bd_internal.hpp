@@ -85,6 +85,9 @@ hipError_t launch_sample_entropy(const float* logits, int P, int V, float temper
                                  uint64_t seed, uint32_t step, const uint8_t* frozen,
                                  int32_t* tokens_out, float* entropy_out, float* conf_out,
                                  void* workspace, hipStream_t stream);
+// The per-device address of the static split-state array (for the allocation-free entry
+// point); hipErrorInvalidValue if `need` bytes do not fit it.
+hipError_t static_sample_scratch(size_t need, void** out);
 hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, float bound,
                          uint8_t* frozen, int32_t* canvas, uint8_t* accept_out,
                          int32_t* num_accepted, hipStream_t stream);

@@ -23,6 +23,8 @@
 // split order by the finish kernel, which re-reads the one winning chunk (1024 entries) for
 // the level-2 draw.
 
+#include <mutex>
+
 #include "bd_device.hpp"
 #include "bd_internal.hpp"
 
@@ -711,6 +713,46 @@ hipError_t launch_accept_confidence(const float* conf, const int32_t* tokens, in
   hipLaunchKernelGGL(accept_conf_kernel, dim3(1), dim3(kAcceptThreads), 0, stream, conf, tokens,
                      P, threshold, frozen, canvas, accept_out, num_accepted);
   return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------- allocation-free workspace
+//
+// For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+// loops, harnesses that forbid hipMalloc): the split states of the streaming pass live in one
+// static device array per GPU instead of a caller's workspace.  Its device address is looked
+// up once per device with that device current and kept per device; host code uses only that
+// address, never the array's name (which on the host is a stand-in, not a device pointer).
+// Every call on a GPU shares its array, and the array keeps the last call's contents: the
+// streaming pass writes every state the finish reads, so nothing needs clearing, and calls
+// that overlap on one GPU race.
+
+namespace {
+constexpr size_t kStaticScratchBytes = 128 * 1024;
+constexpr int kMaxScratchDevices = 64;
+// The largest workspace: P * S states with S = min(ceil(1024 / P), ...) gives at most
+// 1024 + P - 1 <= 2047 states, 256-byte aligned.
+static_assert(2047 * sizeof(PartState) + 256 <= kStaticScratchBytes, "static sampler scratch");
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_sample_scratch(size_t need, void** out) {
+  if (need > kStaticScratchBytes) return hipErrorInvalidValue;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace bd

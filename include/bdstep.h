@@ -349,6 +349,23 @@ int diffusion_sample_step(const float* logits, int P, int V, float temperature,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * diffusion_sample_step without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (less the workspace), same results bit for bit.  The streaming pass's split
+ * states live in a static device array of the library (128 KiB per GPU, held until the
+ * process ends; every valid P, V fits, else BD_ERR_WORKSPACE); the call allocates nothing.
+ * All calls on one GPU share that array: calls that overlap on a GPU (other streams, other
+ * threads) race and must not be issued; calls ordered on one stream are safe.  The first call
+ * on a device looks the array's address up (hipGetSymbolAddress, no allocation); make it
+ * outside graph capture if the capture forbids that.
+ */
+int diffusion_sample_step_noalloc(const float* logits, int P, int V, float temperature,
+                                  float entropy_bound, uint64_t seed, uint32_t step,
+                                  uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                                  float* entropy_out, uint8_t* accept_out, int32_t* num_accepted,
+                                  hipStream_t stream);
+
+/*
  * Confidence-threshold variant of the sampler.  The same single streaming pass as
  * diffusion_sample_entropy (same tokens, same entropies), which also writes the top-1
  * probability of every position that is not frozen:

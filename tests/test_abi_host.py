@@ -258,3 +258,18 @@ def test_prepare_sizes_and_validation(lib):
     w.gate_up_packed = 0x1008
     ws = ctypes.c_void_p(0x10000)
     assert lib.moe_w4a16_gate_up(ref, 256, p, ws, 1 << 30, None) == 3
+
+
+def test_noalloc_sampler_step_validation(lib):
+    """The allocation-free sampler step validates like diffusion_sample_step and returns before
+    any device work (no GPU needed for these)."""
+    P = ctypes.c_void_p(0x1000)
+    call = lib.diffusion_sample_step_noalloc
+    assert call(P, 0, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, P, None) == 2
+    assert call(P, 1025, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, P, None) == 2
+    assert call(P, 8, 4096, float("nan"), 2.0, 0, 0, None, None, P, P, P, P, None) == 2
+    assert call(P, 8, 4096, 1.0, float("inf"), 0, 0, None, None, P, P, P, P, None) == 2
+    assert call(None, 8, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, P, None) == 1
+    assert call(P, 8, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, None, None) == 1
+    assert call(ctypes.c_void_p(0x1004), 8, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, P,
+                None) == 3
