@@ -9,18 +9,20 @@ namespace bd {
 
 inline size_t align_up(size_t n, size_t a = 256) { return (n + a - 1) / a * a; }
 
-// Partial state of one V-split of one row (40 bytes): the entropy sums, the temperature-0
-// argmax and the split's best level-1 draw.
+// Partial state of one V-split of one row (56 bytes): the entropy sums, the temperature-0
+// argmax and the split's best two level-1 draws.
 struct PartState {
-  float m;          // reference maximum (-inf: empty)
-  float n;          // entries equal to m
-  float s;          // sum of exp(x - m) over the other entries
-  float t;          // sum of exp(x - m) (x - m)
-  float best_v;     // temperature-0 argmax value
-  int best_i;       // and its lowest index
-  int nan;          // a NaN was seen where no finite entry could carry it
-  int best_c;       // chunk of the largest level-1 key (lowest chunk on ties)
-  double best_key;  // that key, L_c + G_c (-inf: none)
+  float m;            // reference maximum (-inf: empty)
+  float n;            // entries equal to m
+  float s;            // sum of exp(x - m) over the other entries
+  float t;            // sum of exp(x - m) (x - m)
+  float best_v;       // temperature-0 argmax value
+  int best_i;         // and its lowest index
+  int nan;            // a NaN was seen where no finite entry could carry it
+  int best_c;         // chunk of the largest level-1 key (lowest chunk on ties)
+  int second_c;       // chunk of the second largest
+  double best_key;    // the largest key, L_c + G_c (-inf: none)
+  double second_key;  // the second largest (-inf: none)
 };
 
 // ---------------------------------------------------------------- MoE

@@ -19,9 +19,10 @@
 // argmax needs only the chunk maxima.  For T > 0 the pass also forms each chunk's log-mass
 // L_c = ln sum exp(x / T) and draws the level-1 key L_c + G_c (Philox, fp64): lane b of a wave
 // keeps the b-th chunk's L_c, and every 64 chunks (and at the end) the lanes draw their keys
-// at once and the wave keeps the best.  Partial states of the V-splits of a row are merged in
-// split order by the finish kernel, which re-reads the one winning chunk (1024 entries) for
-// the level-2 draw.
+// at once and the wave keeps its best two.  Partial states of the V-splits of a row are merged
+// in split order by the finish kernel.  Its level-1 decision is the fp64 one: the chunks whose
+// fp32 keys lie too close to the best to be told apart are rescored in fp64.  It then re-reads
+// the one winning chunk (1024 entries) for the level-2 draw.
 
 #include <mutex>
 
@@ -178,13 +179,38 @@ __device__ __forceinline__ float process_chunk(const float (&x)[16], int c, floa
   return (MODE == 1 ? mc : mc * invT) + __builtin_amdgcn_logf(z) * kLn2;
 }
 
-// Merge entropy state b into a (a's maximum is the reference when larger).
+// Best two level-1 (key, chunk) pairs by better_key.  Chunk ids are distinct, so the pair is
+// the same whatever order the candidates arrive in.
+struct Top2 {
+  double k1, k2;
+  int c1, c2;
+};
+__device__ __forceinline__ Top2 top2_empty() {
+  return Top2{-INFINITY, -INFINITY, 0x7fffffff, 0x7fffffff};
+}
+__device__ __forceinline__ void top2_insert(Top2& t, double k, int c) {
+  if (better_key(k, c, t.k1, t.c1)) {
+    t.k2 = t.k1;
+    t.c2 = t.c1;
+    t.k1 = k;
+    t.c1 = c;
+  } else if (better_key(k, c, t.k2, t.c2)) {
+    t.k2 = k;
+    t.c2 = c;
+  }
+}
+
+// Merge state b into a (a's maximum is the reference when larger); the level-1 pairs of both
+// are merged into a's best two.
 __device__ __forceinline__ void merge_state(PartState& a, const PartState& b) {
   a.nan |= b.nan;
-  if (better_key(b.best_key, b.best_c, a.best_key, a.best_c)) {
-    a.best_key = b.best_key;
-    a.best_c = b.best_c;
-  }
+  Top2 t{a.best_key, a.second_key, a.best_c, a.second_c};
+  top2_insert(t, b.best_key, b.best_c);
+  top2_insert(t, b.second_key, b.second_c);
+  a.best_key = t.k1;
+  a.best_c = t.c1;
+  a.second_key = t.k2;
+  a.second_c = t.c2;
   if (b.best_v > a.best_v || (b.best_v == a.best_v && b.best_i < a.best_i)) {
     a.best_v = b.best_v;
     a.best_i = b.best_i;
@@ -217,28 +243,23 @@ __device__ __forceinline__ void merge_state(PartState& a, const PartState& b) {
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
-    const float* __restrict__ logits, int V, int nC, int S, float invT, uint32_t k0,
-    uint32_t k1, uint32_t step, const uint8_t* __restrict__ frozen,
-    PartState* __restrict__ part) {
-  const int p = blockIdx.y;
-  const int s = blockIdx.x;
-  if (frozen != nullptr && frozen[p]) return;
+// One wave's streaming pass over chunks c_begin + wave, c_begin + wave + WAVES, ... < c_end of
+// row p: its entropy sums, its temperature-0 argmax and its best two level-1 keys.
+template <int MODE, int WAVES>
+__device__ __forceinline__ PartState stream_chunks(const float* __restrict__ row, int V, int p,
+                                                   int c_begin, int c_end, float invT,
+                                                   uint32_t k0, uint32_t k1, uint32_t step) {
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int c_begin = (int)((int64_t)s * nC / S);
-  const int c_end = (int)((int64_t)(s + 1) * nC / S);
-  const float* __restrict__ row = logits + (size_t)p * V;
   const bool vec = (V & 3) == 0;
 
   // Level-1 batch: lane b holds the log-mass of the b-th chunk since the last draw.  A draw
-  // gives each held chunk its key L_c + G_c, G_c from counter (c, p, step, 1) word 0.
+  // gives each held chunk its key L_c + G_c, G_c from counter (c, p, step, 1) word 0, and
+  // folds the batch's best two keys into the wave's.
   float bL = -INFINITY;
   int bC = 0;
   int nb = 0;
-  double wkey = -INFINITY;
-  int wc = 0x7fffffff;
+  Top2 top = top2_empty();
   auto draw = [&]() {
     double key = -INFINITY;
     int kc = 0x7fffffff;
@@ -247,11 +268,14 @@ __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
       key = (double)bL + gumbel_from_word(r.w[0]);
       kc = bC;
     }
-    wave_argmax(key, kc);
-    if (better_key(key, kc, wkey, wc)) {
-      wkey = key;
-      wc = kc;
-    }
+    double ka = key;
+    int ca = kc;
+    wave_argmax(ka, ca);
+    double kb = kc == ca ? -INFINITY : key;
+    int cb = kc == ca ? 0x7fffffff : kc;
+    wave_argmax(kb, cb);
+    top2_insert(top, ka, ca);
+    top2_insert(top, kb, cb);
     nb = 0;
   };
   auto fold = [&](float L, int c) {
@@ -276,25 +300,26 @@ __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
   const int c0 = c_begin + wave;
 #pragma unroll
   for (int r = 0; r < kRing; ++r)
-    if (c0 + r * kStreamWaves < c_end) load_chunk(row, V, c0 + r * kStreamWaves, vec, x[r]);
-  for (int base = c0; base < c_end; base += kRing * kStreamWaves) {
+    if (c0 + r * WAVES < c_end) load_chunk(row, V, c0 + r * WAVES, vec, x[r]);
+  for (int base = c0; base < c_end; base += kRing * WAVES) {
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
-      const int c = base + r * kStreamWaves;
+      const int c = base + r * WAVES;
       if (c < c_end) {
         fold(process_chunk<MODE>(x[r], c, invT, st), c);
-        const int cn = c + kRing * kStreamWaves;
+        const int cn = c + kRing * WAVES;
         if (cn < c_end) load_chunk(row, V, cn, vec, x[r]);
       }
     }
   }
-
   if (MODE != 0 && nb > 0) draw();
 
   // Lanes share the reference maximum: the wave state is a plain sum.
   PartState ws;
-  ws.best_key = wkey;
-  ws.best_c = wc;
+  ws.best_key = top.k1;
+  ws.best_c = top.c1;
+  ws.second_key = top.k2;
+  ws.second_c = top.c2;
   ws.m = st.m;
   ws.n = st.n;
   ws.s = wave_sum(st.s);
@@ -302,9 +327,25 @@ __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
   ws.best_v = st.best_v;
   ws.best_i = st.best_i;
   ws.nan = st.nan ? 1 : 0;
+  return ws;
+}
 
+// Block (s, p) streams split s of row p with kStreamWaves waves and writes their
+// merged state (waves in order) to part[p][s].
+template <int MODE>
+__global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
+    const float* __restrict__ logits, int V, int nC, int S, float invT, uint32_t k0,
+    uint32_t k1, uint32_t step, const uint8_t* __restrict__ frozen,
+    PartState* __restrict__ part) {
+  const int p = blockIdx.y;
+  const int s = blockIdx.x;
+  if (frozen != nullptr && frozen[p]) return;
+  const int c_begin = (int)((int64_t)s * nC / S);
+  const int c_end = (int)((int64_t)(s + 1) * nC / S);
+  const PartState ws = stream_chunks<MODE, kStreamWaves>(logits + (size_t)p * V, V, p, c_begin,
+                                                         c_end, invT, k0, k1, step);
   __shared__ PartState wstate[kStreamWaves];
-  if (lane_id() == 0) wstate[wave] = ws;
+  if (lane_id() == 0) wstate[threadIdx.x / kWave] = ws;
   __syncthreads();
   if (threadIdx.x == 0) {
     PartState acc = wstate[0];
@@ -313,13 +354,13 @@ __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
   }
 }
 
-// ---------------------------------------------------------------- finish (one block per row)
+// ---------------------------------------------------------------- finishing a row
 
-constexpr int kFinishThreads = 256;
-constexpr int kFinishWaves = kFinishThreads / kWave;
 constexpr int kMaxSplits = BD_SAMPLE_BLOCKS;  // sample_split_count never exceeds this
+constexpr int kMaxCand = 64;                   // level-1 candidates rescored one by one
 
 // Block-wide argmax of (key, index) by better_key; uniform result, one barrier.
+template <int NW>
 __device__ __forceinline__ void block_argmax(double& key, int& idx, double* wkey, int* widx) {
   wave_argmax(key, idx);
   const int wave = threadIdx.x / kWave;
@@ -331,7 +372,7 @@ __device__ __forceinline__ void block_argmax(double& key, int& idx, double* wkey
   key = wkey[0];
   idx = widx[0];
 #pragma unroll
-  for (int w = 1; w < kFinishWaves; ++w)
+  for (int w = 1; w < NW; ++w)
     if (better_key(wkey[w], widx[w], key, idx)) {
       key = wkey[w];
       idx = widx[w];
@@ -355,12 +396,202 @@ __device__ __forceinline__ float gumbel32_from_word(uint32_t r) {
   return -logf(w);
 }
 
-// One block per row.  The V-split states carry the entropy sums, the temperature-0 argmax and
-// each split's best level-1 key; one lane merges them in split order.  Level 2 re-reads the
-// winning chunk.  Its scores x_v / T + g_v are first formed in fp32 (error below
-// 1.2e-5 + 2.4e-7 |score|); when a single entry is within the margin of the fp32 maximum it is
-// the fp64 argmax, otherwise the entries within the margin are scored again in fp64 (the
-// definition) and the fp64 argmax decides.
+// How far a level-1 key formed from fp32 chunk sums can sit from the fp64 key of the same
+// chunk, doubled (both the winner's key and a rival's may be off).  The fp32 log-mass
+// L = m / T + ln(sum_c exp2((x - m) log2(e) / T)) carries: per term a relative error below
+// 1.2e-7 (exp2) plus 1.5e-7 per unit of the exponent's magnitude (the rounding of x - m,
+// 1/T and the product), which the sum weights by exp(x - m) so that it stays below ~1.3e-6
+// in relative terms; the fp32 summation over at most 16 per lane and six wave levels below
+// 1.3e-6; the log2 within 1 ulp (under 1e-6 absolute for sums of at most 1024 terms), and
+// the rounding of m / T and of the final sums, below 2e-7 |L|.  That is below 5e-6 +
+// 2e-7 |L|; the margin takes twice 1e-5 + 1e-6 |L| with |L| <= |key| + 20 (the Gumbel draw
+// of a 24-bit uniform lies in [-2.9, 17]).
+__device__ __forceinline__ double level1_margin(double key) {
+  return 2.0 * (1e-5 + 1e-6 * (fabs(key) + 20.0));
+}
+
+// The level-1 key of chunk c of row p in fp64, the definition: L_c = m + ln sum exp(x_v / T -
+// m) over the chunk's finite entries (m their largest x_v / T), plus G_c.  Run by one wave
+// (every lane gets the same value; the sums are taken in a fixed order).
+__device__ double chunk_key64(const float* __restrict__ row, int V, int c, double T, int p,
+                              uint32_t step, uint32_t k0, uint32_t k1) {
+  const int lane = lane_id();
+  double y[16];
+  double m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int v = c * kChunk + ((i >> 2) * kWave + lane) * 4 + (i & 3);
+    const float xv = v < V ? row[v] : -INFINITY;
+    y[i] = (double)xv / T;
+    if (y[i] > m) m = y[i];
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+  if (m == -INFINITY) return -INFINITY;
+  double z = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z += y[i] == -INFINITY ? 0.0 : exp(y[i] - m);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) z += __shfl_xor(z, off);
+  const Philox4 r = philox4x32_10((uint32_t)c, (uint32_t)p, step, 1u, k0, k1);
+  return m + log(z) + gumbel_from_word(r.w[0]);
+}
+
+// Finish row p with the block's kFinishThreads threads from the nst partial states in st (LDS, in stream order):
+// entropy, top-1 probability and token.  The states are merged in order by one lane.  At
+// T > 0 the level-1 winner is the chunk with the best fp32 key unless another chunk's key lies
+// within level1_margin of it: then the candidates (each state's best key within the margin)
+// are rescored in fp64 by chunk_key64 and the fp64 best wins; if some state's second key is
+// also within the margin, that state may hold further candidates, and every chunk of the row
+// is rescored.  Level 2 re-reads the winning chunk: its scores x_v / T + g_v are first formed
+// in fp32 (error below 1.2e-5 + 2.4e-7 |score|); when a single entry is within the margin of
+// the fp32 maximum it is the fp64 argmax, otherwise the entries within the margin are scored
+// again in fp64 (the definition) and the fp64 argmax decides.
+constexpr int kFinishThreads = 256;
+
+__device__ __forceinline__ void finish_row(const float* __restrict__ logits, int V, int p,
+                                           const PartState* st, int nst, float temperature,
+                                           uint32_t k0, uint32_t k1, uint32_t step,
+                                           int32_t* __restrict__ tokens_out,
+                                           float* __restrict__ entropy_out,
+                                           float* __restrict__ conf_out) {
+  constexpr int NT = kFinishThreads;
+  constexpr int NW = NT / kWave;
+  constexpr int EPT = kChunk / NT;  // level-2 entries per thread: one Philox call's four words
+  static_assert(EPT == 4, "a chunk covers four entries per thread");
+  __shared__ double wkey[NW];
+  __shared__ int widx[NW];
+  __shared__ float wmax[NW];
+  __shared__ int sValid, sChunk, sRescore, sFallback, sCand;
+  __shared__ double sLim;
+  __shared__ int cand[kMaxCand];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const bool sampled = temperature != 0.f;
+  const float* row = logits + (size_t)p * V;
+  if (tid == 0) {
+    PartState acc = st[0];
+    for (int s = 1; s < nst; ++s) merge_state(acc, st[s]);
+    float H = NAN, conf = NAN;
+    bool valid = !acc.nan && acc.m != -INFINITY;
+    if (valid) {
+      // Z = sum exp(x - m); the top-1 probability is exp(0) / Z.
+      const float Z = acc.n + acc.s;
+      H = log1pf((acc.n - 1.f) + acc.s) - acc.t / Z;
+      conf = 1.f / Z;
+      valid = !(H != H);
+    }
+    sValid = valid && (!sampled || acc.best_key > -INFINITY) ? 1 : 0;
+    sChunk = acc.best_c;
+    sLim = acc.best_key - level1_margin(acc.best_key);
+    // The merged pair is the best two keys over every state, so when the second lies outside
+    // the margin the best chunk is the only candidate and nothing needs rescoring.
+    sRescore = acc.second_key >= sLim ? 1 : 0;
+    sFallback = 0;
+    sCand = 0;
+    if (entropy_out != nullptr) entropy_out[p] = valid ? H : NAN;
+    if (conf_out != nullptr) conf_out[p] = valid ? conf : NAN;
+    if (!valid) tokens_out[p] = -1;
+    else if (!sampled) tokens_out[p] = acc.best_i;
+  }
+  if (!sampled) return;
+  __syncthreads();
+  if (!sValid) {
+    if (tid == 0) tokens_out[p] = -1;   // valid row without a comparable chunk key
+    return;
+  }
+  const int nC = (V + kChunk - 1) / kChunk;
+  int bestc = sChunk;
+  if (sRescore) {
+    // Level 1: the chunks whose fp32 key may still be the fp64 best.
+    const double lim = sLim;
+    for (int s = tid; s < nst; s += NT) {
+      if (st[s].second_key >= lim) sFallback = 1;
+      if (st[s].best_key >= lim) {
+        const int i = atomicAdd(&sCand, 1);
+        if (i < kMaxCand) cand[i] = st[s].best_c;
+      }
+    }
+    __syncthreads();
+    // The second key within the margin is another state's best (a second candidate) or a
+    // state's second (a state that may hold more): rescore the candidates, or every chunk.
+    const bool all = sFallback || sCand > kMaxCand;
+    const int n = all ? nC : sCand;
+    double best = -INFINITY;
+    int bc = 0x7fffffff;
+    for (int i = wave; i < n; i += NW) {
+      const int c = all ? i : cand[i];
+      const double key = chunk_key64(row, V, c, (double)temperature, p, step, k0, k1);
+      if (better_key(key, c, best, bc)) {
+        best = key;
+        bc = c;
+      }
+    }
+    block_argmax<NW>(best, bc, wkey, widx);
+    bestc = bc;
+  }
+  if (bestc < 0 || bestc >= nC) {  // no chunk had a comparable key
+    if (tid == 0) tokens_out[p] = -1;
+    return;
+  }
+  // Level 2: inside chunk bestc, maximise x_v / T + g_v, g_v from (v >> 2, p, step, 0).
+  const int v0 = bestc * kChunk + EPT * tid;
+  const int vend = min(V, (bestc + 1) * kChunk);
+  float xv[EPT], s32[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) xv[q] = s32[q] = -INFINITY;
+  Philox4 r = {};
+  float lmax = -INFINITY;
+  if (v0 < vend) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) xv[q] = v0 + q < vend ? row[v0 + q] : -INFINITY;
+    r = philox4x32_10((uint32_t)(v0 >> 2), (uint32_t)p, step, 0u, k0, k1);
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      if (v0 + q < vend) {
+        s32[q] = xv[q] / temperature + gumbel32_from_word(r.w[(v0 + q) & 3]);
+        lmax = fmaxf(lmax, s32[q]);
+      }
+    }
+  }
+  float m = wave_max(lmax);
+  if (lane_id() == 0) wmax[wave] = m;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) m = fmaxf(m, wmax[w]);
+  // Entries that may still be the fp64 argmax: within twice the fp32 error bound of the
+  // maximum (all entries when the fp32 maximum is not finite).
+  const bool everything = !(fabsf(m) < 1e30f);
+  const float margin = 2e-4f + 2e-6f * fabsf(m);
+  int mask = 0;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q)
+    if (v0 + q < vend && (everything || s32[q] >= m - margin)) mask |= 1 << q;
+  const int holders = __syncthreads_count(mask != 0);
+  const int multi = __syncthreads_count(__builtin_popcount(mask) > 1);
+  if (holders == 1 && multi == 0) {
+    if (mask != 0) tokens_out[p] = v0 + __builtin_ctz(mask);
+    return;
+  }
+  double sbest = -INFINITY;
+  int sv = 0x7fffffff;
+  const double T = (double)temperature;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    if (mask & (1 << q)) {
+      const double sc = (double)xv[q] / T + gumbel_from_word(r.w[(v0 + q) & 3]);
+      if (better_key(sc, v0 + q, sbest, sv)) {
+        sbest = sc;
+        sv = v0 + q;
+      }
+    }
+  }
+  block_argmax<NW>(sbest, sv, wkey, widx);
+  if (tid == 0) tokens_out[p] = sv;
+}
+
+// Second launch: one block per row merges the row's split states in split order
+// and finishes the row.
 __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     const float* __restrict__ logits, int V, int S, float temperature, uint32_t k0, uint32_t k1,
     uint32_t step, const uint8_t* __restrict__ frozen, const PartState* __restrict__ part,
@@ -377,94 +608,10 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     return;
   }
   __shared__ PartState sp[kMaxSplits];
-  __shared__ double wkey[kFinishWaves];
-  __shared__ int widx[kFinishWaves];
-  __shared__ float wmax[kFinishWaves];
-  __shared__ int sValid, sChunk;
   for (int s = tid; s < S; s += kFinishThreads) sp[s] = part[(size_t)p * S + s];
   __syncthreads();
-  const bool sampled = temperature != 0.f;
-  if (tid == 0) {
-    PartState acc = sp[0];
-    for (int s = 1; s < S; ++s) merge_state(acc, sp[s]);
-    float H = NAN, conf = NAN;
-    bool valid = !acc.nan && acc.m != -INFINITY;
-    if (valid) {
-      // Z = sum exp(x - m); the top-1 probability is exp(0) / Z.
-      const float Z = acc.n + acc.s;
-      H = log1pf((acc.n - 1.f) + acc.s) - acc.t / Z;
-      conf = 1.f / Z;
-      valid = !(H != H);
-    }
-    sValid = valid ? 1 : 0;
-    sChunk = acc.best_c;
-    if (entropy_out != nullptr) entropy_out[p] = valid ? H : NAN;
-    if (conf_out != nullptr) conf_out[p] = valid ? conf : NAN;
-    if (!valid) tokens_out[p] = -1;
-    else if (!sampled) tokens_out[p] = acc.best_i;
-  }
-  if (!sampled) return;
-  __syncthreads();
-  if (!sValid) return;
-  // Level 2: inside chunk bestc, maximise x_v / T + g_v, g_v from (v >> 2, p, step, 0).
-  const int bestc = sChunk;
-  if (bestc < 0 || bestc >= (V + kChunk - 1) / kChunk) {  // no chunk had a comparable key
-    if (tid == 0) tokens_out[p] = -1;
-    return;
-  }
-  const int v0 = bestc * kChunk + 4 * tid;
-  const int vend = min(V, (bestc + 1) * kChunk);
-  float xv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  float s32[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  Philox4 r = {};
-  float lmax = -INFINITY;
-  if (v0 < vend) {
-    const float* row = logits + (size_t)p * V;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xv[q] = v0 + q < vend ? row[v0 + q] : -INFINITY;
-    r = philox4x32_10((uint32_t)(v0 >> 2), (uint32_t)p, step, 0u, k0, k1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (v0 + q < vend) {
-        s32[q] = xv[q] / temperature + gumbel32_from_word(r.w[q]);
-        lmax = fmaxf(lmax, s32[q]);
-      }
-    }
-  }
-  float m = wave_max(lmax);
-  if (lane_id() == 0) wmax[tid / kWave] = m;
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kFinishWaves; ++w) m = fmaxf(m, wmax[w]);
-  // Entries that may still be the fp64 argmax: within twice the fp32 error bound of the
-  // maximum (all entries when the fp32 maximum is not finite).
-  const bool all = !(fabsf(m) < 1e30f);
-  const float margin = 2e-4f + 2e-6f * fabsf(m);
-  int mask = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (v0 + q < vend && (all || s32[q] >= m - margin)) mask |= 1 << q;
-  const int holders = __syncthreads_count(mask != 0);
-  const int multi = __syncthreads_count(__builtin_popcount(mask) > 1);
-  if (holders == 1 && multi == 0) {
-    if (mask != 0) tokens_out[p] = v0 + __builtin_ctz(mask);
-    return;
-  }
-  double sbest = -INFINITY;
-  int sv = 0x7fffffff;
-  const double T = (double)temperature;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (mask & (1 << q)) {
-      const double sc = (double)xv[q] / T + gumbel_from_word(r.w[q]);
-      if (better_key(sc, v0 + q, sbest, sv)) {
-        sbest = sc;
-        sv = v0 + q;
-      }
-    }
-  }
-  block_argmax(sbest, sv, wkey, widx);
-  if (tid == 0) tokens_out[p] = sv;
+  finish_row(logits, V, p, sp, S, temperature, k0, k1, step, tokens_out,
+                             entropy_out, conf_out);
 }
 
 // ---------------------------------------------------------------- acceptance (one block)
@@ -670,20 +817,19 @@ hipError_t launch_sample_entropy(const float* logits, int P, int V, float temper
                                  int32_t* tokens_out, float* entropy_out, float* conf_out,
                                  void* workspace, hipStream_t stream) {
   const int nC = (V + kChunk - 1) / kChunk;
+  const float invT = temperature > 0.f ? 1.f / temperature : 0.f;
+  const uint32_t k0 = (uint32_t)(seed & 0xffffffffu), k1 = (uint32_t)(seed >> 32);
+  const int mode = temperature == 0.f ? 0 : (temperature == 1.f ? 1 : 2);
   const int S = sample_split_count(P, V);
   PartState* part = reinterpret_cast<PartState*>(workspace);
   const dim3 grid(S, P);
-  const float invT = temperature > 0.f ? 1.f / temperature : 0.f;
-  const uint32_t k0 = (uint32_t)(seed & 0xffffffffu), k1 = (uint32_t)(seed >> 32);
-  if (temperature == 0.f)
-    hipLaunchKernelGGL(sample_stream_kernel<0>, grid, dim3(kStreamThreads), 0, stream, logits, V,
-                       nC, S, invT, k0, k1, step, frozen, part);
-  else if (temperature == 1.f)
-    hipLaunchKernelGGL(sample_stream_kernel<1>, grid, dim3(kStreamThreads), 0, stream, logits, V,
-                       nC, S, invT, k0, k1, step, frozen, part);
-  else
-    hipLaunchKernelGGL(sample_stream_kernel<2>, grid, dim3(kStreamThreads), 0, stream, logits, V,
-                       nC, S, invT, k0, k1, step, frozen, part);
+#define BD_STREAM(M)                                                                        \
+  hipLaunchKernelGGL(sample_stream_kernel<M>, grid, dim3(kStreamThreads), 0, stream, logits, V, \
+                     nC, S, invT, k0, k1, step, frozen, part)
+  if (mode == 0) BD_STREAM(0);
+  else if (mode == 1) BD_STREAM(1);
+  else BD_STREAM(2);
+#undef BD_STREAM
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(sample_finish_kernel, dim3(P), dim3(kFinishThreads), 0, stream, logits, V, S,

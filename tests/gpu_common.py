@@ -17,11 +17,12 @@ H_REL = 1e-4
 # additions (per lane, per wave, per block, per split), each term an fp32 exp2 of an argument
 # with at most ~3.6e-6 absolute rounding; the bound on |dZ| / Z is below 5e-6.
 C_REL = 1e-5
-# Token decisions at T > 0 are excused only when the oracle's fp64 decision margin is below
-# these: level 1 compares fp32 chunk log-masses (error ~1e-6 absolute), level 2 compares
-# fp64 scores on both sides (error ~1e-15 relative).
-L1_MARGIN = 1e-5
-L2_MARGIN = 1e-10
+# Token decisions at T > 0 are taken in fp64 on both sides (the GPU rescores in fp64 every
+# chunk and every entry its fp32 pre-selection cannot rule out), so a mismatch is excused
+# only when the oracle's own fp64 decision margin is at the level where two fp64 evaluations
+# of the same definition (different exp/log implementations and summation orders) may differ.
+L1_MARGIN = 1e-12
+L2_MARGIN = 1e-12
 
 
 def say(*args):

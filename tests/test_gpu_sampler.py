@@ -3,8 +3,8 @@ the confidence-threshold variant diffusion_sample_confidence / _accept_confidenc
 _step_confidence) against the CPU oracle, through the C ABI.
 
 Bars: tokens at temperature 0 and acceptance masks bit-exact (the mask fed the GPU's
-entropies or confidences); entropies within 1e-4 relative, confidences within 1e-5; tokens at T > 0 bit-exact except where the
-oracle's own decision margin is below the rounding of the chunk log-masses.
+entropies or confidences); entropies within 1e-4 relative, confidences within 1e-5; tokens at
+T > 0 bit-exact, a mismatch excused only at an fp64-level tie of the oracle's own decision.
 """
 
 import math
@@ -89,7 +89,7 @@ def test_tiny_workload(bd, temperature):
     tok, H = run_entropy(bd, x, temperature, seed=shape.seed, step=3)
     H_ref = np.array([osamp.entropy(r) for r in x])
     check_entropy(H, H_ref)
-    assert check_tokens_sampled(x, tok, temperature, shape.seed, 3) <= 1
+    assert check_tokens_sampled(x, tok, temperature, shape.seed, 3) == 0
 
 
 @pytest.mark.parametrize("P,V", [(1, 1), (3, 7), (5, 1023), (4, 1025), (7, 4100), (6, 5003),
@@ -101,7 +101,7 @@ def test_ragged_shapes(bd, P, V, temperature):
     say("ragged", P, V, temperature)
     tok, H = run_entropy(bd, x, temperature, seed=11, step=5)
     check_entropy(H, np.array([osamp.entropy(r) for r in x]))
-    assert check_tokens_sampled(x, tok, temperature, 11, 5) <= max(1, P // 50)
+    assert check_tokens_sampled(x, tok, temperature, 11, 5) == 0
 
 
 def special_rows(V=3000):
@@ -228,7 +228,7 @@ def test_full_size_step(bd, which):
         tok_np, H_np = tok.cpu().numpy(), H.cpu().numpy()
         check_entropy(H_np, H_ref)
         ex = check_tokens_sampled(x, tok_np, temperature, shape.seed, step)
-        assert ex <= 3, f"{ex} near-tie rows excused"
+        assert ex == 0, f"{ex} fp64-tie rows excused"
         ref_mask, ref_n = osamp.accept(H_np, shape.bound)
         assert int(cnt.item()) == ref_n
         assert np.array_equal(acc.cpu().numpy(), ref_mask)
@@ -372,7 +372,7 @@ def test_full_size_step_confidence(bd, which):
         tok_np, C_np = tok.cpu().numpy(), C.cpu().numpy()
         check_confidence(C_np, np.where(frozen_np == 1, -1.0, C_ref))
         rows = [p for p in range(P) if not frozen_np[p]]
-        assert check_tokens_sampled(x, tok_np, temperature, shape.seed, step, rows=rows) <= 3
+        assert check_tokens_sampled(x, tok_np, temperature, shape.seed, step, rows=rows) == 0
         assert np.all(tok_np[frozen_np == 1] == -1)
         ref_mask, ref_n = osamp.accept_confidence(C_np, 0.9, frozen_np)
         assert int(cnt.item()) == ref_n
@@ -471,3 +471,49 @@ def test_full_size_step_repeats_bit_identical(bd):
     for other in runs[1:]:
         for a, b in zip(runs[0], other):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# ---------------------------------------------------------------- level-1 near-ties
+
+
+def near_tie_rows(P, V, temperature, seed, step, groups, base=-30.0, target=5.0, spread=3e-7):
+    """Logits whose level-1 keys tie closely: in row p every chunk of groups[p % len(groups)]
+    holds one constant value chosen so that its key L_c + G_c (G_c the oracle's chunk noise) is
+    target + i * spread (i the chunk's rank in a per-row shuffle), up to the fp32 rounding of
+    that value; every other entry is `base`, far below.  The keys are closer than the fp32
+    log-masses can separate, so only an fp64 decision reproduces the oracle's chunk."""
+    nC = V // osamp.CHUNK
+    t32 = float(np.float32(temperature))
+    rng = np.random.default_rng(1234 + P)
+    x = np.full((P, V), base, dtype=np.float32)
+    for p in range(P):
+        group = groups[p % len(groups)]
+        G = osamp.chunk_noise(p, np.arange(nC), seed, step)
+        offsets = rng.permutation(len(group)) * spread
+        for c, off in zip(group, offsets):
+            a = t32 * (target + off - G[c] - np.log(osamp.CHUNK))
+            x[p, c * osamp.CHUNK:(c + 1) * osamp.CHUNK] = np.float32(a)
+    return x
+
+
+@pytest.mark.parametrize("path,P,groups", [
+    # 64 rows: 64 chunks per row over 8 splits of 8 chunks
+    ("8 splits: one per state", 64, [[2, 20, 45], [0, 63], [9, 17, 25, 33, 41]]),
+    ("8 splits: two in a state", 64, [[8, 13], [16, 17, 40], [56, 60, 63]]),
+    # 256 rows: 4 splits of 16 chunks
+    ("4 splits: one per state", 256, [[2, 20, 45], [0, 63], [1, 17, 33, 49]]),
+    ("4 splits: two in a state", 256, [[5, 9], [16, 31, 40], [48, 50, 63]]),
+])
+def test_level1_near_ties_are_decided_in_fp64(bd, path, P, groups):
+    """Chunks whose level-1 keys tie to ~1e-7: the GPU's token matches the oracle's fp64
+    decision on every row, whether the tied chunks sit in different partial states (each
+    rescored in fp64) or two of them in one state (every chunk of the row rescored)."""
+    V, T, seed, step = 65536, 0.8, 7, 2
+    x = near_tie_rows(P, V, T, seed, step, groups)
+    say("level-1 near ties", path, P)
+    tok, H = run_entropy(bd, x, T, seed=seed, step=step)
+    for p in range(P):
+        ref, keys, _ = osamp.draw_token(x[p], T, seed, step, p)
+        assert int(tok[p]) == ref, f"row {p}: token {tok[p]} vs oracle {ref}"
+    H_ref = np.array([osamp.entropy(r) for r in x])
+    check_entropy(H, H_ref)
