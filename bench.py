@@ -1,18 +1,21 @@
 """Benchmark of the denoising-step hot path on one MI355X.
 
-One step = one denoising step of the stack workload: 30 MoE FFN layers (256-token canvas,
-d_model 2816, expert ffn 704, 128 experts top-8, W4A16 group 64, Zipf(1.2) routing), each
-as route -> gate/up (GeGLU) -> down -> fixed-order combine, followed by the sampler
-(entropy + gumbel-max over fp32 logits [256, 262144], temperature 1, then the entropy-bound
-acceptance at bound 2.0).  Accepted positions stay frozen; the canvas is reset every 48
-steps.  All inputs are seeded synthetic tensors resident in HBM before timing starts.
+One step = one step of the denoising loop of the stack workload: 30 MoE FFN layers
+(256-token canvas, d_model 2816, expert ffn 704, 128 experts top-8, W4A16 group 64,
+Zipf(1.2) routing), each as route -> gate/up (GeGLU) -> down -> fixed-order combine, then the
+sampler (entropy + gumbel-max over fp32 logits [256, 262144], temperature 1, then the
+entropy-bound acceptance at bound 2.0), then the loop driver's update (drafts into the
+canvas, the stability count, the end of the block).  A block of 48 steps starts from a
+seeded random canvas and runs as one captured HIP graph whose launches are gated on the
+driver's done flag; accepted positions stay frozen within a block.  All inputs are seeded
+synthetic tensors resident in HBM before timing starts.
 
 value = algorithmic bytes of the step (touched expert weights with their scales and
-zero-points, activations in and out, router logits, the unfrozen logits rows) / time,
-in GB/s; ms_per_step is the latency of one step, from one event pair around the timed steps
-(no other event inside); config.step_ms_p10_p50_p90 is the spread of the step latency over a
-second pass of the same length with an event between steps; the gate/up roofline comes from a
-third pass (see main).
+zero-points, activations in and out, router logits, the unfrozen logits rows; nothing for a
+step after its block has ended) / time, in GB/s; ms_per_step is the latency of one step, from
+one event pair around the timed steps (no other event inside);
+config.step_ms_p10_p50_p90_over_blocks is the spread of the per-step time over block replays;
+the gate/up roofline comes from a third pass of eager launches (see main).
 
 Two more workloads time the parts on their own configurations (--workload):
   layer    one MoE FFN layer (route, gate/up, down, combine) at the 256-token canvas with uniform
@@ -43,8 +46,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--layers", type=int, default=None, help="MoE layers per step (default 30)")
     ap.add_argument("--workload", choices=("stack", "layer", "sampler"), default="stack",
                     help="stack (default): the whole denoising step; layer: one FFN layer at the "
@@ -292,6 +295,10 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=50):
 
 
 GU_LAUNCHES = 60
+# Consecutive unchanged steps that end a block early.  The pages name the option but give no
+# default; at temperature 1 with step-keyed noise the drafts change at every step, so the
+# stack's blocks run the whole step budget whatever the value.
+LOOP_STABILITY = 2
 
 
 def gate_up_back_to_back(bd, weights, routers, x, ids, tw):
@@ -545,94 +552,115 @@ def main():
     tok = torch.empty(P, dtype=torch.int32, device="cuda")
     H = torch.empty(P, dtype=torch.float32, device="cuda")
     acc = torch.empty(P, dtype=torch.uint8, device="cuda")
-    # Every launch of the stack is marshalled once up front (bd.bind), so that a step costs
-    # the host a few microseconds per launch and the GPU's queue never runs dry: the timed
-    # region then measures the kernels, not the host.  Each timed step times the gate/up
-    # kernel of one layer (layer i mod L at step i) from its own dispatch timestamps: over the
-    # timed steps these sample the gate/up launches of every layer.
+    # The denoising loop on the device.  A block is one captured graph: the random initial
+    # canvas (which also clears the frozen set and the driver state), then STACK_STEPS steps
+    # of 30 layers (route, gate/up, down, combine) and the sampler step, each followed by the
+    # loop driver's update; every launch but the update carries the driver state as its done
+    # gate, so the steps after the block ends do no work.  K timed steps replay whole blocks
+    # and, when K is not a multiple of STACK_STEPS, a graph of the first K mod STACK_STEPS
+    # steps of a block.
+    STEPS = workloads.STACK_STEPS
+    prev = torch.empty(P, dtype=torch.int32, device="cuda")
+    state = torch.zeros(4, dtype=torch.int32, device="cuda")
+    n_acc = torch.zeros(STEPS, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def capture(n_steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            bd.diffusion_canvas_init(canvas, prev, frozen, state, V, sshape.seed, 0)
+            for s in range(n_steps):
+                for w, router in layers:
+                    bd.moe_w4a16_ffn(w, x, router, ids, tw, o, ws, loop_state=state)
+                    bd.moe_combine_fixed_order(o, tw, y, loop_state=state)
+                bd.diffusion_sample_step(logits, sshape.temperature, sshape.bound, sshape.seed, s,
+                                         frozen, canvas, tok, H, acc, n_acc[s:s + 1], sws,
+                                         loop_state=state)
+                bd.diffusion_loop_update(tok, canvas, prev, frozen, state, LOOP_STABILITY, STEPS)
+        return g
+
+    log(f"capturing the block graph ({STEPS} steps, {n_layers} layers each)")
+    graphs = {STEPS: capture(STEPS)}
+    for n in {args.steps % STEPS, args.warmup % STEPS} - {0}:
+        graphs[n] = capture(n)
+
+    def run_steps(n):
+        """Replay graphs covering n steps (whole blocks, then a partial block)."""
+        for _ in range(n // STEPS):
+            graphs[STEPS].replay()
+        if n % STEPS:
+            graphs[n % STEPS].replay()
+
+    # Warm-up (untimed), then the timed steps between one event pair.
+    run_steps(max(args.warmup, 1))
+    torch.cuda.synchronize()
+    log(f"warmup done; timing {args.steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    run_steps(args.steps)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # Work done per block (every replay of a block graph does the same work): the steps the
+    # block ran before it ended, and the rows each step's sampler read (unfrozen rows, from the
+    # device's acceptance counts).
+    counts = n_acc.cpu().numpy()
+    steps_run = int(state.cpu().numpy()[0])
+    unfrozen = np.array([P - int(counts[:s].sum()) for s in range(STEPS)], dtype=np.float64)
+    live = np.arange(STEPS) < steps_run
+    layer_bytes = sum(t * (gu_bytes + dn_bytes) for t in touched) + n_layers * (
+        2 * T * d * 2 + T * E * 4 + 2 * T * k * 4)
+    step_bytes_blk = np.where(live, layer_bytes + unfrozen * V * 4 + P * 4 * 4, 0.0)
+    timed_steps = [i % STEPS for i in range((args.steps // STEPS) * STEPS)] + list(
+        range(args.steps % STEPS))
+    step_bytes = float(np.mean(step_bytes_blk[timed_steps]))
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    # A second pass: block replays with an event between consecutive blocks, the spread of the
+    # block time (per step).
+    n_blocks = max(3, args.steps // STEPS)
+    blk_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_blocks + 1)]
+    blk_ev[0].record(stream)
+    for b in range(n_blocks):
+        graphs[STEPS].replay()
+        blk_ev[b + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in zip(blk_ev[:-1], blk_ev[1:])]) / STEPS
+
+    # A third pass, eager launches: the gate/up kernel's in-step duration by difference.  Step j
+    # of this pass brackets with one event pair the routing and gate/up launches of layer
+    # (j // 2) mod L when j is odd and the routing launch alone of the same layer when j is
+    # even.  A timing event leaves the GPU idle for several microseconds around the launches
+    # next to it (the trace shows no gap between unmarked launches), the same in both
+    # brackets, so the mean of the odd intervals minus the mean of the even ones is the
+    # gate/up launch as it runs inside the step.
     stack = []
     for w, router in layers:
         stack.append((bd.bind(bd.moe_route_topk, w, router, ids, tw, ws),
                       bd.bind(bd.moe_w4a16_gate_up, w, x, ws),
                       bd.bind(bd.moe_w4a16_down, w, T, o, ws),
                       bd.bind(bd.moe_combine_fixed_order, o, tw, y)))
-    total = args.warmup + args.steps
-    n_acc = torch.zeros(total + 2 * args.steps, dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    # The gate/up kernel's in-step duration, by difference, from a third pass after the timed
-    # region (the timed region itself holds no event but its two ends): step j of that pass
-    # brackets with one event pair the routing and gate/up launches of layer (j // 2) mod L
-    # when j is odd and the routing launch alone of the same layer when j is even.  A timing
-    # event leaves the GPU idle for several microseconds around the launches next to it (the
-    # trace shows no gap between unmarked launches), the same in both brackets, so the mean of
-    # the odd intervals minus the mean of the even ones is the gate/up launch as it runs
-    # inside the step.
     marks = [((j // 2) % len(layers), j % 2 == 1,
               (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
              for j in range(args.steps)]
-
-    def step(i, mark=None):
-        if i % workloads.STACK_STEPS == 0:
-            frozen.zero_()
+    frozen.zero_()
+    for j, (mli, with_gu, (a, b)) in enumerate(marks):
         for li, (route, gate_up, down, combine) in enumerate(stack):
-            here = mark is not None and li == mark[0]
+            here = li == mli
             if here:
-                mark[2][0].record(stream)
+                a.record(stream)
             route()
-            if here and not mark[1]:
-                mark[2][1].record(stream)
+            if here and not with_gu:
+                b.record(stream)
             gate_up()
-            if here and mark[1]:
-                mark[2][1].record(stream)
+            if here and with_gu:
+                b.record(stream)
             down()
             combine()
         bd.diffusion_sample_step(logits, sshape.temperature, sshape.bound, sshape.seed,
-                                 i % workloads.STACK_STEPS, frozen, canvas, tok, H, acc,
-                                 n_acc[i:i + 1], sws)
-
-    for i in range(args.warmup):
-        step(i)
+                                 j % STEPS, frozen, canvas, tok, H, acc, n_acc[0:1], sws)
     torch.cuda.synchronize()
-    log(f"warmup done; timing {args.steps} steps")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.warmup, total):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-
-    # A second pass of the same number of steps, with an event between consecutive steps, gives
-    # the spread of the step latency without touching the timed region above.
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    step_ev[0].record(stream)
-    for i in range(total, total + args.steps):
-        step(i)
-        step_ev[i - total + 1].record(stream)
-    torch.cuda.synchronize()
-    per_step = np.array([a.elapsed_time(b) for a, b in zip(step_ev[:-1], step_ev[1:])])
-
-    # Third pass: the gate/up difference brackets (see marks above).
-    for i in range(total + args.steps, total + 2 * args.steps):
-        step(i, marks[i - total - args.steps])
-    torch.cuda.synchronize()
-
-    # Unfrozen rows seen by each timed step's sampler, from the device's acceptance counts.
-    counts = n_acc.cpu().numpy()
-    unfrozen = []
-    fr = 0
-    for i in range(total):
-        if i % workloads.STACK_STEPS == 0:
-            fr = 0
-        if i >= args.warmup:
-            unfrozen.append(P - fr)
-        fr += int(counts[i])
-    sampler_bytes = np.array(unfrozen, dtype=np.float64) * V * 4 + P * 4 * 4
-    ffn_bytes = sum(t * (gu_bytes + dn_bytes) for t in touched) + n_layers * (
-        2 * T * d * 2 + T * E * 4 + 2 * T * k * 4)
-    step_bytes = ffn_bytes + float(sampler_bytes.mean())
-    value = step_bytes / (ms * 1e-3) / 1e9
 
     with_gu = [a.elapsed_time(b) for _, g, (a, b) in marks if g]
     route_only = [a.elapsed_time(b) for _, g, (a, b) in marks if not g]
@@ -660,12 +688,17 @@ def main():
         "dtype": "f16-mfma/f32",
         "data": "synthetic",
         "config": {
-            "workload": (f"stack: {n_layers} MoE layers (canvas {T}, d_model {d}, expert ffn {f}, "
-                         f"{E} experts top-{k}, W4A16 asym g64, Zipf(1.2) routing) + sampler "
-                         f"fp32 [{P}, {V}] T=1 bound 2.0, 48-step frozen canvas"),
-            "steps_per_block": workloads.STACK_STEPS,
+            "workload": (f"stack: the denoising loop, each step {n_layers} MoE layers (canvas "
+                         f"{T}, d_model {d}, expert ffn {f}, {E} experts top-{k}, W4A16 asym "
+                         f"g64, Zipf(1.2) routing) + sampler fp32 [{P}, {V}] T=1 bound 2.0 + "
+                         f"loop update; blocks of {STEPS} steps from a random canvas, each "
+                         f"block one captured graph with the done gate"),
+            "steps_per_block": STEPS,
+            "block_steps_run": steps_run,
+            "stability_threshold": LOOP_STABILITY,
             "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
-            "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
+            "step_ms_p10_p50_p90_over_blocks": [round(float(np.percentile(per_step, q)), 4)
+                                                for q in (10, 50, 90)],
             "step_algorithmic_bytes": int(step_bytes),
             **({"components": parts} if parts is not None else {}),
         },

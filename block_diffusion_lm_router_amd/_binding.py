@@ -63,7 +63,9 @@ SIGNATURES = {
     "moe_w4a16_gate_up": (_I, [_W, _I, _P, _P, _SZ, _P]),
     "moe_w4a16_down": (_I, [_W, _I, _P, _P, _SZ, _P]),
     "moe_w4a16_ffn": (_I, [_W, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_w4a16_ffn_gated": (_I, [_W, _I, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "moe_combine_fixed_order": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "moe_combine_fixed_order_gated": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "moe_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P, _P]),
     "moe_router_logits": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "bd_sample_workspace_size": (_SZ, [_I, _I]),
@@ -71,6 +73,8 @@ SIGNATURES = {
     "diffusion_accept_entropy_bound": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
     "diffusion_sample_step": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P, _P, _P,
                                    _SZ, _P]),
+    "diffusion_sample_step_gated": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P, _P,
+                                         _P, _SZ, _P, _P]),
     "diffusion_sample_step_noalloc": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P,
                                            _P, _P]),
     "diffusion_sample_confidence": (_I, [_P, _I, _I, _F, _U64, _U32, _P, _P, _P, _P, _P, _SZ,
@@ -78,6 +82,8 @@ SIGNATURES = {
     "diffusion_accept_confidence": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
     "diffusion_sample_step_confidence": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _P,
                                               _P, _P, _SZ, _P]),
+    "diffusion_sample_step_confidence_gated": (_I, [_P, _I, _I, _F, _F, _U64, _U32, _P, _P, _P,
+                                                    _P, _P, _P, _P, _SZ, _P, _P]),
     "bd_canvas_length": (_I, [_I, _I, _I, _I]),
     "diffusion_canvas_init": (_I, [_P, _P, _P, _P, _I, _I, _U64, _U32, _P]),
     "diffusion_loop_update": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -168,6 +174,12 @@ def _shape(t, shape, name, what):
         return
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{what}: {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _gate(loop_state, what):
+    """The marshalled loop-driver state of a gated call (int32, at least 4 elements)."""
+    _at_least(loop_state, 4, "loop_state", what)
+    return _ptr(loop_state, torch.int32, "loop_state")
 
 
 def _at_least(t, n, name, what):
@@ -291,30 +303,38 @@ def moe_w4a16_down(w, T, expert_out, workspace):
                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
 
 
-def moe_w4a16_ffn(w, x, router_logits, topk_ids, topk_weights, expert_out, workspace):
+def moe_w4a16_ffn(w, x, router_logits, topk_ids, topk_weights, expert_out, workspace,
+                  loop_state=None):
+    """loop_state (int32 [4]) selects moe_w4a16_ffn_gated: nothing runs once the loop is done."""
     T, what = x.shape[0], "moe_w4a16_ffn"
     _shape(x, (T, w.d_model), "x", what)
     _shape(router_logits, (T, w.num_experts), "router_logits", what)
     _shape(topk_ids, (T, w.top_k), "topk_ids", what)
     _shape(topk_weights, (T, w.top_k), "topk_weights", what)
     _shape(expert_out, (T, w.top_k, w.d_model), "expert_out", what)
-    return _invoke("moe_w4a16_ffn", w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
-                   _ptr(router_logits, torch.float32, "router_logits"),
-                   _ptr(topk_ids, torch.int32, "topk_ids"),
-                   _ptr(topk_weights, torch.float32, "topk_weights"),
-                   _ptr(expert_out, torch.float32, "expert_out"),
-                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    args = (w.ref(), x.shape[0], _ptr(x, torch.float16, "x"),
+            _ptr(router_logits, torch.float32, "router_logits"),
+            _ptr(topk_ids, torch.int32, "topk_ids"),
+            _ptr(topk_weights, torch.float32, "topk_weights"),
+            _ptr(expert_out, torch.float32, "expert_out"),
+            _ptr(workspace, torch.uint8, "workspace"), workspace.numel())
+    if loop_state is not None:
+        return _invoke("moe_w4a16_ffn_gated", *args, _gate(loop_state, what), _stream())
+    return _invoke("moe_w4a16_ffn", *args, _stream())
 
 
-def moe_combine_fixed_order(expert_out, topk_weights, y):
+def moe_combine_fixed_order(expert_out, topk_weights, y, loop_state=None):
     if expert_out.dim() != 3:
         raise ValueError("moe_combine_fixed_order: expert_out must be [T, k, d]")
     T, k, d = expert_out.shape
     _shape(topk_weights, (T, k), "topk_weights", "moe_combine_fixed_order")
     _shape(y, (T, d), "y", "moe_combine_fixed_order")
-    return _invoke("moe_combine_fixed_order", _ptr(expert_out, torch.float32, "expert_out"),
-                   _ptr(topk_weights, torch.float32, "topk_weights"), T, k, d,
-                   _ptr(y, torch.float16, "y"), _stream())
+    args = (_ptr(expert_out, torch.float32, "expert_out"),
+            _ptr(topk_weights, torch.float32, "topk_weights"), T, k, d, _ptr(y, torch.float16, "y"))
+    if loop_state is not None:
+        return _invoke("moe_combine_fixed_order_gated", *args,
+                       _gate(loop_state, "moe_combine_fixed_order"), _stream())
+    return _invoke("moe_combine_fixed_order", *args, _stream())
 
 
 def moe_rmsnorm(h, weight, y, eps=1e-6):
@@ -384,19 +404,23 @@ def diffusion_accept_entropy_bound(entropy, tokens, bound, frozen, canvas, accep
 
 
 def diffusion_sample_step(logits, temperature, entropy_bound, seed, step, frozen, canvas,
-                          tokens_out, entropy_out, accept_out, num_accepted, workspace):
+                          tokens_out, entropy_out, accept_out, num_accepted, workspace,
+                          loop_state=None):
     P, V = _logits_shape(logits, "diffusion_sample_step")
     _rows("diffusion_sample_step", P, frozen=frozen, canvas=canvas, tokens_out=tokens_out,
           entropy_out=entropy_out, accept_out=accept_out)
     _at_least(num_accepted, 1, "num_accepted", "diffusion_sample_step")
-    return _invoke("diffusion_sample_step", _ptr(logits, torch.float32, "logits"), P, V,
-                   float(temperature), float(entropy_bound), int(seed), int(step),
-                   _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
-                   _ptr(tokens_out, torch.int32, "tokens_out"),
-                   _ptr(entropy_out, torch.float32, "entropy_out"),
-                   _ptr(accept_out, torch.uint8, "accept_out"),
-                   _ptr(num_accepted, torch.int32, "num_accepted"),
-                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    args = (_ptr(logits, torch.float32, "logits"), P, V, float(temperature),
+            float(entropy_bound), int(seed), int(step), _ptr(frozen, torch.uint8, "frozen"),
+            _ptr(canvas, torch.int32, "canvas"), _ptr(tokens_out, torch.int32, "tokens_out"),
+            _ptr(entropy_out, torch.float32, "entropy_out"),
+            _ptr(accept_out, torch.uint8, "accept_out"),
+            _ptr(num_accepted, torch.int32, "num_accepted"),
+            _ptr(workspace, torch.uint8, "workspace"), workspace.numel())
+    if loop_state is not None:
+        return _invoke("diffusion_sample_step_gated", *args,
+                       _gate(loop_state, "diffusion_sample_step"), _stream())
+    return _invoke("diffusion_sample_step", *args, _stream())
 
 
 def diffusion_sample_step_noalloc(logits, temperature, entropy_bound, seed, step, frozen, canvas,
@@ -442,19 +466,22 @@ def diffusion_accept_confidence(confidence, tokens, threshold, frozen, canvas, a
 
 def diffusion_sample_step_confidence(logits, temperature, threshold, seed, step, frozen, canvas,
                                      tokens_out, confidence_out, accept_out, num_accepted,
-                                     workspace):
+                                     workspace, loop_state=None):
     P, V = _logits_shape(logits, "diffusion_sample_step_confidence")
     _rows("diffusion_sample_step_confidence", P, frozen=frozen, canvas=canvas,
           tokens_out=tokens_out, confidence_out=confidence_out, accept_out=accept_out)
     _at_least(num_accepted, 1, "num_accepted", "diffusion_sample_step_confidence")
-    return _invoke("diffusion_sample_step_confidence", _ptr(logits, torch.float32, "logits"), P,
-                   V, float(temperature), float(threshold), int(seed), int(step),
-                   _ptr(frozen, torch.uint8, "frozen"), _ptr(canvas, torch.int32, "canvas"),
-                   _ptr(tokens_out, torch.int32, "tokens_out"),
-                   _ptr(confidence_out, torch.float32, "confidence_out"),
-                   _ptr(accept_out, torch.uint8, "accept_out"),
-                   _ptr(num_accepted, torch.int32, "num_accepted"),
-                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    args = (_ptr(logits, torch.float32, "logits"), P, V, float(temperature), float(threshold),
+            int(seed), int(step), _ptr(frozen, torch.uint8, "frozen"),
+            _ptr(canvas, torch.int32, "canvas"), _ptr(tokens_out, torch.int32, "tokens_out"),
+            _ptr(confidence_out, torch.float32, "confidence_out"),
+            _ptr(accept_out, torch.uint8, "accept_out"),
+            _ptr(num_accepted, torch.int32, "num_accepted"),
+            _ptr(workspace, torch.uint8, "workspace"), workspace.numel())
+    if loop_state is not None:
+        return _invoke("diffusion_sample_step_confidence_gated", *args,
+                       _gate(loop_state, "diffusion_sample_step_confidence"), _stream())
+    return _invoke("diffusion_sample_step_confidence", *args, _stream())
 
 
 def canvas_length(max_canvas, min_canvas, remaining, full_canvas=False):

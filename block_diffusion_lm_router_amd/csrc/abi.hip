@@ -179,9 +179,9 @@ int moe_w4a16_down(const bd_moe_weights* w, int T, float* expert_out, void* work
                                    expert_out, ws, stream));
 }
 
-int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x, const float* router_logits,
-                  int32_t* topk_ids, float* topk_weights, float* expert_out, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream) {
+static int ffn_call(const bd_moe_weights* w, int T, const uint16_t* x, const float* router_logits,
+                    int32_t* topk_ids, float* topk_weights, float* expert_out, void* workspace,
+                    size_t workspace_bytes, const int32_t* gate, hipStream_t stream) {
   int st = check_moe_shape(w, T);
   if (st != BD_OK) return st;
   if ((st = check_gate_up_weights(w)) != BD_OK) return st;
@@ -196,23 +196,53 @@ int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x, const float
       bd::moe_workspace_carve(workspace, T, w->num_experts, w->top_k, w->d_model, w->d_ff);
   hipStream_t s = stream;
   hipError_t err = bd::launch_route(router_logits, T, w->num_experts, w->top_k, topk_ids,
-                                    topk_weights, ws, s);
+                                    topk_weights, ws, s, gate);
   if (err == hipSuccess)
     err = bd::launch_gate_up(gate_up_of(w), w->num_experts, w->d_model, w->d_ff, w->top_k, T, x,
-                             ws, s);
+                             ws, s, gate);
   if (err == hipSuccess)
     err = bd::launch_down(down_of(w), w->num_experts, w->d_model, w->d_ff, w->top_k, T,
-                          expert_out, ws, s);
+                          expert_out, ws, s, gate);
   return to_status(err);
 }
 
-int moe_combine_fixed_order(const float* expert_out, const float* topk_weights, int T, int k,
-                            int d, uint16_t* y, hipStream_t stream) {
+int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x, const float* router_logits,
+                  int32_t* topk_ids, float* topk_weights, float* expert_out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  return ffn_call(w, T, x, router_logits, topk_ids, topk_weights, expert_out, workspace,
+                  workspace_bytes, nullptr, stream);
+}
+
+int moe_w4a16_ffn_gated(const bd_moe_weights* w, int T, const uint16_t* x,
+                        const float* router_logits, int32_t* topk_ids, float* topk_weights,
+                        float* expert_out, void* workspace, size_t workspace_bytes,
+                        const int32_t* loop_state, hipStream_t stream) {
+  if (!loop_state) return BD_ERR_NULL;
+  if (!aligned4(loop_state)) return BD_ERR_ALIGN;
+  return ffn_call(w, T, x, router_logits, topk_ids, topk_weights, expert_out, workspace,
+                  workspace_bytes, loop_state, stream);
+}
+
+static int combine_call(const float* expert_out, const float* topk_weights, int T, int k, int d,
+                        uint16_t* y, const int32_t* gate, hipStream_t stream) {
   if (!expert_out || !topk_weights || !y) return BD_ERR_NULL;
   if (T < 1 || T > BD_MAX_TOKENS || k < 1 || k > BD_MAX_TOPK || d < 4 || d % 4 != 0)
     return BD_ERR_SHAPE;
   if (!aligned16(expert_out) || !aligned4(topk_weights) || !aligned16(y)) return BD_ERR_ALIGN;
-  return to_status(bd::launch_combine(expert_out, topk_weights, T, k, d, y, stream));
+  return to_status(bd::launch_combine(expert_out, topk_weights, T, k, d, y, stream, gate));
+}
+
+int moe_combine_fixed_order(const float* expert_out, const float* topk_weights, int T, int k,
+                            int d, uint16_t* y, hipStream_t stream) {
+  return combine_call(expert_out, topk_weights, T, k, d, y, nullptr, stream);
+}
+
+int moe_combine_fixed_order_gated(const float* expert_out, const float* topk_weights, int T,
+                                  int k, int d, uint16_t* y, const int32_t* loop_state,
+                                  hipStream_t stream) {
+  if (!loop_state) return BD_ERR_NULL;
+  if (!aligned4(loop_state)) return BD_ERR_ALIGN;
+  return combine_call(expert_out, topk_weights, T, k, d, y, loop_state, stream);
 }
 
 int moe_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps, uint16_t* y,
@@ -267,11 +297,11 @@ int diffusion_accept_entropy_bound(const float* entropy, const int32_t* tokens, 
                                      num_accepted, stream));
 }
 
-int diffusion_sample_step(const float* logits, int P, int V, float temperature,
-                          float entropy_bound, uint64_t seed, uint32_t step, uint8_t* frozen,
-                          int32_t* canvas, int32_t* tokens_out, float* entropy_out,
-                          uint8_t* accept_out, int32_t* num_accepted, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+static int step_call(const float* logits, int P, int V, float temperature, float entropy_bound,
+                     uint64_t seed, uint32_t step, uint8_t* frozen, int32_t* canvas,
+                     int32_t* tokens_out, float* entropy_out, uint8_t* accept_out,
+                     int32_t* num_accepted, void* workspace, size_t workspace_bytes,
+                     const int32_t* gate, hipStream_t stream) {
   int st = check_sample_shape(P, V, temperature);
   if (st != BD_OK) return st;
   if (!isfinite(entropy_bound)) return BD_ERR_SHAPE;
@@ -283,11 +313,35 @@ int diffusion_sample_step(const float* logits, int P, int V, float temperature,
   if (st != BD_OK) return st;
   hipStream_t s = stream;
   hipError_t err = bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
-                                             tokens_out, entropy_out, nullptr, workspace, s);
+                                             tokens_out, entropy_out, nullptr, workspace, s,
+                                             gate);
   if (err == hipSuccess)
     err = bd::launch_accept(entropy_out, tokens_out, P, entropy_bound, frozen, canvas, accept_out,
-                            num_accepted, s);
+                            num_accepted, s, gate);
   return to_status(err);
+}
+
+int diffusion_sample_step(const float* logits, int P, int V, float temperature,
+                          float entropy_bound, uint64_t seed, uint32_t step, uint8_t* frozen,
+                          int32_t* canvas, int32_t* tokens_out, float* entropy_out,
+                          uint8_t* accept_out, int32_t* num_accepted, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return step_call(logits, P, V, temperature, entropy_bound, seed, step, frozen, canvas,
+                   tokens_out, entropy_out, accept_out, num_accepted, workspace, workspace_bytes,
+                   nullptr, stream);
+}
+
+int diffusion_sample_step_gated(const float* logits, int P, int V, float temperature,
+                                float entropy_bound, uint64_t seed, uint32_t step,
+                                uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                                float* entropy_out, uint8_t* accept_out, int32_t* num_accepted,
+                                void* workspace, size_t workspace_bytes,
+                                const int32_t* loop_state, hipStream_t stream) {
+  if (!loop_state) return BD_ERR_NULL;
+  if (!aligned4(loop_state)) return BD_ERR_ALIGN;
+  return step_call(logits, P, V, temperature, entropy_bound, seed, step, frozen, canvas,
+                   tokens_out, entropy_out, accept_out, num_accepted, workspace, workspace_bytes,
+                   loop_state, stream);
 }
 
 int diffusion_sample_step_noalloc(const float* logits, int P, int V, float temperature,
@@ -345,12 +399,12 @@ int diffusion_accept_confidence(const float* confidence, const int32_t* tokens, 
                                                 accept_out, num_accepted, stream));
 }
 
-int diffusion_sample_step_confidence(const float* logits, int P, int V, float temperature,
-                                     float threshold, uint64_t seed, uint32_t step,
-                                     uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
-                                     float* confidence_out, uint8_t* accept_out,
-                                     int32_t* num_accepted, void* workspace,
-                                     size_t workspace_bytes, hipStream_t stream) {
+static int step_confidence_call(const float* logits, int P, int V, float temperature,
+                                float threshold, uint64_t seed, uint32_t step, uint8_t* frozen,
+                                int32_t* canvas, int32_t* tokens_out, float* confidence_out,
+                                uint8_t* accept_out, int32_t* num_accepted, void* workspace,
+                                size_t workspace_bytes, const int32_t* gate,
+                                hipStream_t stream) {
   int st = check_sample_shape(P, V, temperature);
   if (st != BD_OK) return st;
   if (!threshold_ok(threshold)) return BD_ERR_SHAPE;
@@ -363,11 +417,37 @@ int diffusion_sample_step_confidence(const float* logits, int P, int V, float te
   if (st != BD_OK) return st;
   hipStream_t s = stream;
   hipError_t err = bd::launch_sample_entropy(logits, P, V, temperature, seed, step, frozen,
-                                             tokens_out, nullptr, confidence_out, workspace, s);
+                                             tokens_out, nullptr, confidence_out, workspace, s,
+                                             gate);
   if (err == hipSuccess)
     err = bd::launch_accept_confidence(confidence_out, tokens_out, P, threshold, frozen, canvas,
-                                       accept_out, num_accepted, s);
+                                       accept_out, num_accepted, s, gate);
   return to_status(err);
+}
+
+int diffusion_sample_step_confidence(const float* logits, int P, int V, float temperature,
+                                     float threshold, uint64_t seed, uint32_t step,
+                                     uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                                     float* confidence_out, uint8_t* accept_out,
+                                     int32_t* num_accepted, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return step_confidence_call(logits, P, V, temperature, threshold, seed, step, frozen, canvas,
+                              tokens_out, confidence_out, accept_out, num_accepted, workspace,
+                              workspace_bytes, nullptr, stream);
+}
+
+int diffusion_sample_step_confidence_gated(const float* logits, int P, int V, float temperature,
+                                           float threshold, uint64_t seed, uint32_t step,
+                                           uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                                           float* confidence_out, uint8_t* accept_out,
+                                           int32_t* num_accepted, void* workspace,
+                                           size_t workspace_bytes, const int32_t* loop_state,
+                                           hipStream_t stream) {
+  if (!loop_state) return BD_ERR_NULL;
+  if (!aligned4(loop_state)) return BD_ERR_ALIGN;
+  return step_confidence_call(logits, P, V, temperature, threshold, seed, step, frozen, canvas,
+                              tokens_out, confidence_out, accept_out, num_accepted, workspace,
+                              workspace_bytes, loop_state, stream);
 }
 
 int bd_canvas_length(int max_canvas, int min_canvas, int remaining, int full_canvas) {

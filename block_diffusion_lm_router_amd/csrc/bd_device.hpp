@@ -16,6 +16,13 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// The done gate of a denoising loop: a kernel given a driver state (int32 [4]; word 2 is the
+// done flag the loop update sets) returns at once when the block is done, before touching
+// anything.  The flag was written by an earlier launch on the stream, so a plain load sees it.
+__device__ __forceinline__ bool gated_off(const int32_t* __restrict__ gate) {
+  return gate != nullptr && gate[2] != 0;
+}
+
 // ---------------------------------------------------------------- cross-lane moves
 // DPP moves inside a 16-lane row.  After the xor-1, xor-2, xor-4 (half-row mirror)
 // and xor-8 (row mirror) steps every lane of a row holds the row's reduction; the

@@ -47,11 +47,14 @@ MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_model, i
 
 // Top-k ids and weights (the ids also into ws.ids), then the stable grouping of the
 // assignments by expert and the work list into ws (a second, one-block launch).
+// Every launcher below that takes `gate` (NULL: always run) launches kernels that return at
+// once when gate[2] (a loop driver's done flag) is set.
 hipError_t launch_route(const float* router_logits, int T, int E, int k, int32_t* topk_ids,
-                        float* topk_weights, const MoeWorkspace& ws, hipStream_t stream);
+                        float* topk_weights, const MoeWorkspace& ws, hipStream_t stream,
+                        const int32_t* gate = nullptr);
 // x permuted into ws.xp (the k-order of the dequantised nibbles), for the tile kernel.
 hipError_t launch_permute(int T, const uint16_t* x, int d_model, const MoeWorkspace& ws,
-                          hipStream_t stream);
+                          hipStream_t stream, const int32_t* gate = nullptr);
 
 struct W4A16Matrix {
   const uint8_t* q;
@@ -68,11 +71,13 @@ hipError_t launch_pack(const W4A16Matrix& m, bool gated, int E, int d_model, int
                        uint8_t* out, hipStream_t stream);
 
 hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, int top_k, int T,
-                          const uint16_t* x, const MoeWorkspace& ws, hipStream_t stream);
+                          const uint16_t* x, const MoeWorkspace& ws, hipStream_t stream,
+                          const int32_t* gate = nullptr);
 hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int top_k, int T,
-                       float* expert_out, const MoeWorkspace& ws, hipStream_t stream);
+                       float* expert_out, const MoeWorkspace& ws, hipStream_t stream,
+                       const int32_t* gate = nullptr);
 hipError_t launch_combine(const float* expert_out, const float* topk_weights, int T, int k, int d,
-                          uint16_t* y, hipStream_t stream);
+                          uint16_t* y, hipStream_t stream, const int32_t* gate = nullptr);
 
 // RMS norm of fp16 rows (one wave per row) and the router projection (MFMA, split-K).
 hipError_t launch_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps,
@@ -86,17 +91,19 @@ size_t sample_workspace_bytes(int P, int V);
 hipError_t launch_sample_entropy(const float* logits, int P, int V, float temperature,
                                  uint64_t seed, uint32_t step, const uint8_t* frozen,
                                  int32_t* tokens_out, float* entropy_out, float* conf_out,
-                                 void* workspace, hipStream_t stream);
+                                 void* workspace, hipStream_t stream,
+                                 const int32_t* gate = nullptr);
 // The per-device address of the static split-state array (for the allocation-free entry
 // point); hipErrorInvalidValue if `need` bytes do not fit it.
 hipError_t static_sample_scratch(size_t need, void** out);
 hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, float bound,
                          uint8_t* frozen, int32_t* canvas, uint8_t* accept_out,
-                         int32_t* num_accepted, hipStream_t stream);
+                         int32_t* num_accepted, hipStream_t stream,
+                         const int32_t* gate = nullptr);
 hipError_t launch_accept_confidence(const float* conf, const int32_t* tokens, int P,
                                     float threshold, uint8_t* frozen, int32_t* canvas,
                                     uint8_t* accept_out, int32_t* num_accepted,
-                                    hipStream_t stream);
+                                    hipStream_t stream, const int32_t* gate = nullptr);
 
 // ---------------------------------------------------------------- denoising-loop driver
 hipError_t launch_canvas_init(int32_t* canvas, int32_t* prev, uint8_t* frozen, int32_t* state,

@@ -18,7 +18,9 @@ constexpr int kCombineThreads = 256;
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ o,
                                                                   const float* __restrict__ w,
                                                                   int T, int k, int d,
-                                                                  uint16_t* __restrict__ y) {
+                                                                  uint16_t* __restrict__ y,
+                                                                  const int32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   const int d4 = d >> 2;
   const int64_t i = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
   if (i >= (int64_t)T * d4) return;
@@ -92,11 +94,11 @@ __global__ __launch_bounds__(kCopyThreads) void read_finish_kernel(uint32_t* __r
 }  // namespace
 
 hipError_t launch_combine(const float* expert_out, const float* topk_weights, int T, int k, int d,
-                          uint16_t* y, hipStream_t stream) {
+                          uint16_t* y, hipStream_t stream, const int32_t* gate) {
   const int64_t n = (int64_t)T * (d / 4);
   const int blocks = (int)((n + kCombineThreads - 1) / kCombineThreads);
   hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(kCombineThreads), 0, stream, expert_out,
-                     topk_weights, T, k, d, y);
+                     topk_weights, T, k, d, y, gate);
   return hipGetLastError();
 }
 

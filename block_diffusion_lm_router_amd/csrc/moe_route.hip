@@ -39,7 +39,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
                                                             int T, int E, int k,
                                                             int32_t* __restrict__ ids,
                                                             int32_t* __restrict__ ids_copy,
-                                                            float* __restrict__ weights) {
+                                                            float* __restrict__ weights,
+                                                            const int32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   __shared__ __attribute__((aligned(16))) unsigned long long keys[kMaxE];
   __shared__ int part_rank[kTopkThreads];
   __shared__ int sel_id[kMaxTopk];
@@ -97,6 +99,7 @@ struct BucketArgs {
   int32_t* offsets;        // [E + 1]
   int32_t* items;          // [0] = count, then (expert, first position, tokens)
   int32_t* perm;           // [T * k]
+  const int32_t* gate;     // loop driver state or NULL (see gated_off)
 };
 
 // Expert id of an assignment, clamped into [0, E) so that no value read can index past the
@@ -278,6 +281,7 @@ __device__ void bucket_all(const BucketArgs& g, BucketShared& sh) {
 }
 
 __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(BucketArgs g) {
+  if (gated_off(g.gate)) return;
   __shared__ BucketShared sh;
   bucket_all(g, sh);
 }
@@ -285,7 +289,9 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(BucketArgs g) {
 // x -> xp with every 8 consecutive halves in the GEMMs' k-order (for the tile kernel, which
 // moves activations HBM -> LDS without passing through registers).
 __global__ __launch_bounds__(kBucketThreads) void permute_kernel(const u32x4_t* __restrict__ x,
-                                                                 u32x4_t* __restrict__ xp, int n8) {
+                                                                 u32x4_t* __restrict__ xp, int n8,
+                                                                 const int32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   const int i = blockIdx.x * kBucketThreads + threadIdx.x;
   if (i < n8) xp[i] = permute8(x[i]);
 }
@@ -324,9 +330,10 @@ MoeWorkspace moe_workspace_carve(void* base, int T, int E, int k, int d_model, i
 }
 
 hipError_t launch_route(const float* router_logits, int T, int E, int k, int32_t* topk_ids,
-                        float* topk_weights, const MoeWorkspace& ws, hipStream_t stream) {
+                        float* topk_weights, const MoeWorkspace& ws, hipStream_t stream,
+                        const int32_t* gate) {
   hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(kTopkThreads), 0, stream, router_logits, T, E, k,
-                     topk_ids, ws.ids, topk_weights);
+                     topk_ids, ws.ids, topk_weights, gate);
   BucketArgs g;
   g.ids = ws.ids;
   g.T = T;
@@ -335,16 +342,17 @@ hipError_t launch_route(const float* router_logits, int T, int E, int k, int32_t
   g.offsets = ws.offsets;
   g.items = ws.items;
   g.perm = ws.perm;
+  g.gate = gate;
   hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, g);
   return hipGetLastError();
 }
 
 hipError_t launch_permute(int T, const uint16_t* x, int d_model, const MoeWorkspace& ws,
-                          hipStream_t stream) {
+                          hipStream_t stream, const int32_t* gate) {
   const int n8 = T * d_model / 8;
   hipLaunchKernelGGL(permute_kernel, dim3((n8 + kBucketThreads - 1) / kBucketThreads),
                      dim3(kBucketThreads), 0, stream, reinterpret_cast<const u32x4_t*>(x),
-                     reinterpret_cast<u32x4_t*>(ws.xp), n8);
+                     reinterpret_cast<u32x4_t*>(ws.xp), n8, gate);
   return hipGetLastError();
 }
 

@@ -116,6 +116,7 @@ struct GemmArgs {
   int E;                   // experts
   int A;                   // assignments T * top_k of this call
   int max_items;           // capacity of the work list
+  const int32_t* gate;     // loop driver state or NULL (see gated_off)
 };
 
 // Work item `item` of the list: (expert, first bucket position, tokens), every value clamped
@@ -445,6 +446,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& a, char* lds, int e, i
 
 template <bool GATED>
 __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(GemmArgs a) {
+  if (gated_off(a.gate)) return;
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int b = blockIdx.x;
   const int local = b / kXcds;
@@ -717,6 +719,7 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
 // NSC > 0: compiled for exactly NSC stages (the caller checks); 0: any number of stages.
 template <bool GATED, int NSC, bool AFF>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
+  if (gated_off(a.gate)) return;
   __shared__ __attribute__((aligned(16))) char lds[2 * kPkXSlot];
   // XCD b % 8 owns a contiguous range of work items (the items of one expert are consecutive,
   // so a hot expert's items mostly share an XCD) and walks it tile-major: the blocks of one
@@ -895,6 +898,7 @@ __device__ __forceinline__ void down_resident_item(const GemmArgs& a, char* lds,
 
 template <bool AFF>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_down_resident_kernel(GemmArgs a) {
+  if (gated_off(a.gate)) return;
   extern __shared__ __attribute__((aligned(16))) char lds_dyn[];
   // Same XCD-aware order as the staged kernel, over (item, group of tiles).
   const int b = blockIdx.x;
@@ -1030,7 +1034,8 @@ hipError_t launch_pack(const W4A16Matrix& m, bool gated, int E, int d_model, int
 }
 
 hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, int top_k, int T,
-                          const uint16_t* x, const MoeWorkspace& ws, hipStream_t stream) {
+                          const uint16_t* x, const MoeWorkspace& ws, hipStream_t stream,
+                          const int32_t* gate) {
   GemmArgs a;
   a.q = gu.q;
   a.scale = gu.scale;
@@ -1051,13 +1056,14 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.E = E;
   a.A = T * top_k;
   a.max_items = ws.max_items;
+  a.gate = gate;
   // The expert buckets and the work list are in ws from the routing launch.  The packed
   // kernel reorders x in registers; the tile kernel needs a reordered copy first.
   if (gu.pk) {
     a.tiles = pk_tiles(true, d_model, d_ff);
     launch_packed<true>(a, ws.max_items, stream);
   } else {
-    hipError_t err = launch_permute(T, x, d_model, ws, stream);
+    hipError_t err = launch_permute(T, x, d_model, ws, stream, gate);
     if (err != hipSuccess) return err;
     a.act = ws.xp;
     hipLaunchKernelGGL(w4a16_gemm_kernel<true>, dim3(grid_blocks(ws.max_items, a.tiles)),
@@ -1067,7 +1073,8 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
 }
 
 hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int top_k, int T,
-                       float* expert_out, const MoeWorkspace& ws, hipStream_t stream) {
+                       float* expert_out, const MoeWorkspace& ws, hipStream_t stream,
+                       const int32_t* gate) {
   GemmArgs a;
   a.q = dn.q;
   a.scale = dn.scale;
@@ -1088,6 +1095,7 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
   a.E = E;
   a.A = T * top_k;
   a.max_items = ws.max_items;
+  a.gate = gate;
   if (dn.pk) {
     a.tiles = pk_tiles(false, d_model, d_ff);
     launch_packed<false>(a, ws.max_items, stream);

@@ -336,7 +336,8 @@ template <int MODE>
 __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
     const float* __restrict__ logits, int V, int nC, int S, float invT, uint32_t k0,
     uint32_t k1, uint32_t step, const uint8_t* __restrict__ frozen,
-    PartState* __restrict__ part) {
+    PartState* __restrict__ part, const int32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   const int p = blockIdx.y;
   const int s = blockIdx.x;
   if (frozen != nullptr && frozen[p]) return;
@@ -596,7 +597,8 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     const float* __restrict__ logits, int V, int S, float temperature, uint32_t k0, uint32_t k1,
     uint32_t step, const uint8_t* __restrict__ frozen, const PartState* __restrict__ part,
     int32_t* __restrict__ tokens_out, float* __restrict__ entropy_out,
-    float* __restrict__ conf_out) {
+    float* __restrict__ conf_out, const int32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   const int p = blockIdx.x;
   const int tid = threadIdx.x;
   if (frozen != nullptr && frozen[p]) {
@@ -651,7 +653,8 @@ constexpr int kSelectSteps = 8;  // positions taken by selection before the full
 __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const float* __restrict__ entropy, const int32_t* __restrict__ tokens, int P, float bound,
     uint8_t* __restrict__ frozen, int32_t* __restrict__ canvas, uint8_t* __restrict__ accept_out,
-    int32_t* __restrict__ num_accepted) {
+    int32_t* __restrict__ num_accepted, const int32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   __shared__ uint64_t keys[kAcceptThreads];
   __shared__ unsigned long long wmin[2][kAcceptThreads / kWave];
   __shared__ int sCount;
@@ -759,7 +762,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
 __global__ __launch_bounds__(kAcceptThreads) void accept_conf_kernel(
     const float* __restrict__ conf, const int32_t* __restrict__ tokens, int P, float threshold,
     uint8_t* __restrict__ frozen, int32_t* __restrict__ canvas, uint8_t* __restrict__ accept_out,
-    int32_t* __restrict__ num_accepted) {
+    int32_t* __restrict__ num_accepted, const int32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   __shared__ uint64_t wbest[kAcceptThreads / kWave];
   __shared__ int sPick;
   const int tid = threadIdx.x;
@@ -815,7 +819,7 @@ int sample_split_count(int P, int V) {
 hipError_t launch_sample_entropy(const float* logits, int P, int V, float temperature,
                                  uint64_t seed, uint32_t step, const uint8_t* frozen,
                                  int32_t* tokens_out, float* entropy_out, float* conf_out,
-                                 void* workspace, hipStream_t stream) {
+                                 void* workspace, hipStream_t stream, const int32_t* gate) {
   const int nC = (V + kChunk - 1) / kChunk;
   const float invT = temperature > 0.f ? 1.f / temperature : 0.f;
   const uint32_t k0 = (uint32_t)(seed & 0xffffffffu), k1 = (uint32_t)(seed >> 32);
@@ -825,7 +829,7 @@ hipError_t launch_sample_entropy(const float* logits, int P, int V, float temper
   const dim3 grid(S, P);
 #define BD_STREAM(M)                                                                        \
   hipLaunchKernelGGL(sample_stream_kernel<M>, grid, dim3(kStreamThreads), 0, stream, logits, V, \
-                     nC, S, invT, k0, k1, step, frozen, part)
+                     nC, S, invT, k0, k1, step, frozen, part, gate)
   if (mode == 0) BD_STREAM(0);
   else if (mode == 1) BD_STREAM(1);
   else BD_STREAM(2);
@@ -833,7 +837,8 @@ hipError_t launch_sample_entropy(const float* logits, int P, int V, float temper
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(sample_finish_kernel, dim3(P), dim3(kFinishThreads), 0, stream, logits, V, S,
-                     temperature, k0, k1, step, frozen, part, tokens_out, entropy_out, conf_out);
+                     temperature, k0, k1, step, frozen, part, tokens_out, entropy_out, conf_out,
+                     gate);
   return hipGetLastError();
 }
 
@@ -844,20 +849,20 @@ size_t sample_workspace_bytes(int P, int V) {
 
 hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, float bound,
                          uint8_t* frozen, int32_t* canvas, uint8_t* accept_out,
-                         int32_t* num_accepted, hipStream_t stream) {
+                         int32_t* num_accepted, hipStream_t stream, const int32_t* gate) {
   int n = kWave;
   while (n < P) n <<= 1;
   hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(n), 0, stream, entropy, tokens, P, bound, frozen,
-                     canvas, accept_out, num_accepted);
+                     canvas, accept_out, num_accepted, gate);
   return hipGetLastError();
 }
 
 hipError_t launch_accept_confidence(const float* conf, const int32_t* tokens, int P,
                                     float threshold, uint8_t* frozen, int32_t* canvas,
                                     uint8_t* accept_out, int32_t* num_accepted,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, const int32_t* gate) {
   hipLaunchKernelGGL(accept_conf_kernel, dim3(1), dim3(kAcceptThreads), 0, stream, conf, tokens,
-                     P, threshold, frozen, canvas, accept_out, num_accepted);
+                     P, threshold, frozen, canvas, accept_out, num_accepted, gate);
   return hipGetLastError();
 }
 

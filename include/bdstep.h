@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 9
+#define BD_ABI_VERSION 10
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -240,6 +240,18 @@ int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x,
                   float* expert_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The same, gated by a denoising loop's driver state (see diffusion_loop_update): when
+ * loop_state[2] (done) is nonzero as the launches run, every kernel returns at once and no
+ * output or workspace byte is written.  So a fixed sequence of steps captured in one graph
+ * does no work after its block has ended.  loop_state: int32 [4], device, required.
+ * Source: DiffusionGemma block-diffusion page, "How it works" (the block ends early).
+ */
+int moe_w4a16_ffn_gated(const bd_moe_weights* w, int T, const uint16_t* x,
+                        const float* router_logits, int32_t* topk_ids, float* topk_weights,
+                        float* expert_out, void* workspace, size_t workspace_bytes,
+                        const int32_t* loop_state, hipStream_t stream);
+
+/*
  * Fixed-order weighted combine: y[t] = fp16( sum_{j=0}^{k-1} w[t][j] * o[t][j] ), the
  * sum taken in fp32 as acc = fma(w[t][j], o[t][j], acc) for j = 0, 1, ..., k-1 from
  * acc = 0, then rounded once to fp16 (round to nearest even).  No atomics: results are
@@ -253,6 +265,11 @@ int moe_w4a16_ffn(const bd_moe_weights* w, int T, const uint16_t* x,
  */
 int moe_combine_fixed_order(const float* expert_out, const float* topk_weights,
                             int T, int k, int d, uint16_t* y, hipStream_t stream);
+
+/* moe_combine_fixed_order gated like moe_w4a16_ffn_gated (nothing written once done). */
+int moe_combine_fixed_order_gated(const float* expert_out, const float* topk_weights, int T,
+                                  int k, int d, uint16_t* y, const int32_t* loop_state,
+                                  hipStream_t stream);
 
 /* ------------------------------------------------------------------ layer neighbours */
 
@@ -348,6 +365,15 @@ int diffusion_sample_step(const float* logits, int P, int V, float temperature,
                           float* entropy_out, uint8_t* accept_out, int32_t* num_accepted,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* diffusion_sample_step gated like moe_w4a16_ffn_gated: once loop_state[2] (done) is set,
+ * nothing is read or written (tokens, entropies, mask, count, canvas and frozen set stay). */
+int diffusion_sample_step_gated(const float* logits, int P, int V, float temperature,
+                                float entropy_bound, uint64_t seed, uint32_t step,
+                                uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                                float* entropy_out, uint8_t* accept_out, int32_t* num_accepted,
+                                void* workspace, size_t workspace_bytes,
+                                const int32_t* loop_state, hipStream_t stream);
+
 /*
  * diffusion_sample_step without a workspace argument, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
@@ -411,6 +437,15 @@ int diffusion_sample_step_confidence(const float* logits, int P, int V, float te
                                      float* confidence_out, uint8_t* accept_out,
                                      int32_t* num_accepted, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
+
+/* diffusion_sample_step_confidence gated like diffusion_sample_step_gated. */
+int diffusion_sample_step_confidence_gated(const float* logits, int P, int V, float temperature,
+                                           float threshold, uint64_t seed, uint32_t step,
+                                           uint8_t* frozen, int32_t* canvas, int32_t* tokens_out,
+                                           float* confidence_out, uint8_t* accept_out,
+                                           int32_t* num_accepted, void* workspace,
+                                           size_t workspace_bytes, const int32_t* loop_state,
+                                           hipStream_t stream);
 
 /* ------------------------------------------------------------------ denoising-loop driver */
 

@@ -273,3 +273,27 @@ def test_noalloc_sampler_step_validation(lib):
     assert call(P, 8, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, None, None) == 1
     assert call(ctypes.c_void_p(0x1004), 8, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, P,
                 None) == 3
+
+
+def test_gated_entry_points_validate_the_gate(lib):
+    """The gated variants need a device loop state (NULL or misaligned is refused before any
+    device work) and otherwise validate like their ungated forms."""
+    P = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1002)
+    w = _weights()
+    need = lib.bd_moe_workspace_size(256, ctypes.byref(w))
+    ffn = lib.moe_w4a16_ffn_gated
+    assert ffn(ctypes.byref(w), 256, P, P, P, P, P, P, need, None, None) == 1
+    assert ffn(ctypes.byref(w), 256, P, P, P, P, P, P, need, odd, None) == 3
+    assert ffn(ctypes.byref(w), 0, P, P, P, P, P, P, need, P, None) == 2
+    comb = lib.moe_combine_fixed_order_gated
+    assert comb(P, P, 4, 8, 2816, P, None, None) == 1
+    assert comb(P, P, 4, 8, 2818, P, P, None) == 2
+    n = lib.bd_sample_workspace_size(64, 4096)
+    step = lib.diffusion_sample_step_gated
+    assert step(P, 64, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, P, P, n, None, None) == 1
+    assert step(P, 64, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, P, P, n, odd, None) == 3
+    assert step(P, 0, 4096, 1.0, 2.0, 0, 0, None, None, P, P, P, P, P, n, P, None) == 2
+    conf = lib.diffusion_sample_step_confidence_gated
+    assert conf(P, 64, 4096, 1.0, 0.9, 0, 0, None, None, P, P, P, P, P, n, None, None) == 1
+    assert conf(P, 64, 4096, 1.0, 1.5, 0, 0, None, None, P, P, P, P, P, n, P, None) == 2
