@@ -25,7 +25,8 @@ Two more workloads time the parts on their own configurations (--workload):
 Each reports the same fields; its roofline covers its dominant launch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--workload stack|layer|sampler]
+                       [--workload stack|layer|sampler] [--no-components] [--no-graph]
+                       [--eager-only]
 """
 
 import argparse
@@ -55,6 +56,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true",
                     help="skip the one-launch-at-a-time part timings (e.g. for counter runs)")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="stack workload: run only the eager pass of pre-marshalled launches (the "
+                         "gate/up roofline; value and ms_per_step are null), for counter "
+                         "collection")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="stack workload: issue each block's launches eagerly instead of replaying "
+                         "its captured graph (for counter collection, which does not follow "
+                         "graph launches)")
     return ap.parse_args()
 
 
@@ -354,6 +363,10 @@ def timed_loop(fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def _round(v, n):
+    return None if v is None else round(v, n)
+
+
 def base_record(args, value, ms, workload, extra_config):
     cfg = {"workload": workload}
     cfg.update(extra_config)
@@ -565,68 +578,93 @@ def main():
     n_acc = torch.zeros(STEPS, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
+    def issue(n_steps):
+        """Enqueue the first n_steps steps of a block: the initial canvas, then per step the
+        gated layers, the gated sampler and the loop driver's update."""
+        bd.diffusion_canvas_init(canvas, prev, frozen, state, V, sshape.seed, 0)
+        for s in range(n_steps):
+            for w, router in layers:
+                bd.moe_w4a16_ffn(w, x, router, ids, tw, o, ws, loop_state=state)
+                bd.moe_combine_fixed_order(o, tw, y, loop_state=state)
+            bd.diffusion_sample_step(logits, sshape.temperature, sshape.bound, sshape.seed, s,
+                                     frozen, canvas, tok, H, acc, n_acc[s:s + 1], sws,
+                                     loop_state=state)
+            bd.diffusion_loop_update(tok, canvas, prev, frozen, state, LOOP_STABILITY, STEPS)
+
     def capture(n_steps):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            bd.diffusion_canvas_init(canvas, prev, frozen, state, V, sshape.seed, 0)
-            for s in range(n_steps):
-                for w, router in layers:
-                    bd.moe_w4a16_ffn(w, x, router, ids, tw, o, ws, loop_state=state)
-                    bd.moe_combine_fixed_order(o, tw, y, loop_state=state)
-                bd.diffusion_sample_step(logits, sshape.temperature, sshape.bound, sshape.seed, s,
-                                         frozen, canvas, tok, H, acc, n_acc[s:s + 1], sws,
-                                         loop_state=state)
-                bd.diffusion_loop_update(tok, canvas, prev, frozen, state, LOOP_STABILITY, STEPS)
+            issue(n_steps)
         return g
 
-    log(f"capturing the block graph ({STEPS} steps, {n_layers} layers each)")
-    graphs = {STEPS: capture(STEPS)}
-    for n in {args.steps % STEPS, args.warmup % STEPS} - {0}:
-        graphs[n] = capture(n)
+    class Eager:
+        """Stands in for a block graph under --no-graph: replay() issues the launches."""
 
-    def run_steps(n):
-        """Replay graphs covering n steps (whole blocks, then a partial block)."""
-        for _ in range(n // STEPS):
+        def __init__(self, n_steps):
+            self.n_steps = n_steps
+
+        def replay(self):
+            issue(self.n_steps)
+
+    def graph_passes():
+        """The timed block replays and the block-time spread; returns (ms per step, GB/s,
+        steps a block ran, per-step ms of each block replay, bytes per timed step)."""
+        make = Eager if args.no_graph else capture
+        log(f"{'preparing eager blocks' if args.no_graph else 'capturing the block graph'} "
+            f"({STEPS} steps, {n_layers} layers each)")
+        graphs = {STEPS: make(STEPS)}
+        for n in {args.steps % STEPS, args.warmup % STEPS} - {0}:
+            graphs[n] = make(n)
+
+        def run_steps(n):
+            """Replay graphs covering n steps (whole blocks, then a partial block)."""
+            for _ in range(n // STEPS):
+                graphs[STEPS].replay()
+            if n % STEPS:
+                graphs[n % STEPS].replay()
+
+        # Warm-up (untimed), then the timed steps between one event pair.
+        run_steps(max(args.warmup, 1))
+        torch.cuda.synchronize()
+        log(f"warmup done; timing {args.steps} steps")
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        run_steps(args.steps)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+
+        # Work done per block (every replay of a block graph does the same work): the steps
+        # the block ran before it ended, and the rows each step's sampler read (unfrozen rows,
+        # from the device's acceptance counts).
+        counts = n_acc.cpu().numpy()
+        steps_run = int(state.cpu().numpy()[0])
+        unfrozen = np.array([P - int(counts[:s].sum()) for s in range(STEPS)], dtype=np.float64)
+        live = np.arange(STEPS) < steps_run
+        layer_bytes = sum(t * (gu_bytes + dn_bytes) for t in touched) + n_layers * (
+            2 * T * d * 2 + T * E * 4 + 2 * T * k * 4)
+        step_bytes_blk = np.where(live, layer_bytes + unfrozen * V * 4 + P * 4 * 4, 0.0)
+        timed_steps = [i % STEPS for i in range((args.steps // STEPS) * STEPS)] + list(
+            range(args.steps % STEPS))
+        step_bytes = float(np.mean(step_bytes_blk[timed_steps]))
+        value = step_bytes / (ms * 1e-3) / 1e9
+
+        # A second pass: block replays with an event between consecutive blocks, the spread of
+        # the block time (per step).
+        n_blocks = max(3, args.steps // STEPS)
+        blk_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_blocks + 1)]
+        blk_ev[0].record(stream)
+        for b in range(n_blocks):
             graphs[STEPS].replay()
-        if n % STEPS:
-            graphs[n % STEPS].replay()
+            blk_ev[b + 1].record(stream)
+        torch.cuda.synchronize()
+        per_step = np.array([a.elapsed_time(b) for a, b in zip(blk_ev[:-1], blk_ev[1:])]) / STEPS
+        return ms, value, steps_run, per_step, step_bytes
 
-    # Warm-up (untimed), then the timed steps between one event pair.
-    run_steps(max(args.warmup, 1))
-    torch.cuda.synchronize()
-    log(f"warmup done; timing {args.steps} steps")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    run_steps(args.steps)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-
-    # Work done per block (every replay of a block graph does the same work): the steps the
-    # block ran before it ended, and the rows each step's sampler read (unfrozen rows, from the
-    # device's acceptance counts).
-    counts = n_acc.cpu().numpy()
-    steps_run = int(state.cpu().numpy()[0])
-    unfrozen = np.array([P - int(counts[:s].sum()) for s in range(STEPS)], dtype=np.float64)
-    live = np.arange(STEPS) < steps_run
-    layer_bytes = sum(t * (gu_bytes + dn_bytes) for t in touched) + n_layers * (
-        2 * T * d * 2 + T * E * 4 + 2 * T * k * 4)
-    step_bytes_blk = np.where(live, layer_bytes + unfrozen * V * 4 + P * 4 * 4, 0.0)
-    timed_steps = [i % STEPS for i in range((args.steps // STEPS) * STEPS)] + list(
-        range(args.steps % STEPS))
-    step_bytes = float(np.mean(step_bytes_blk[timed_steps]))
-    value = step_bytes / (ms * 1e-3) / 1e9
-
-    # A second pass: block replays with an event between consecutive blocks, the spread of the
-    # block time (per step).
-    n_blocks = max(3, args.steps // STEPS)
-    blk_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_blocks + 1)]
-    blk_ev[0].record(stream)
-    for b in range(n_blocks):
-        graphs[STEPS].replay()
-        blk_ev[b + 1].record(stream)
-    torch.cuda.synchronize()
-    per_step = np.array([a.elapsed_time(b) for a, b in zip(blk_ev[:-1], blk_ev[1:])]) / STEPS
+    if args.eager_only:
+        ms = value = steps_run = per_step = step_bytes = None
+    else:
+        ms, value, steps_run, per_step, step_bytes = graph_passes()
 
     # A third pass, eager launches: the gate/up kernel's in-step duration by difference.  Step j
     # of this pass brackets with one event pair the routing and gate/up launches of layer
@@ -634,7 +672,9 @@ def main():
     # even.  A timing event leaves the GPU idle for several microseconds around the launches
     # next to it (the trace shows no gap between unmarked launches), the same in both
     # brackets, so the mean of the odd intervals minus the mean of the even ones is the
-    # gate/up launch as it runs inside the step.
+    # gate/up launch as it runs inside the step.  The pass runs at least 2 L steps, so every
+    # layer is bracketed both ways whatever --steps is.
+    n_eager = max(args.steps + args.steps % 2, 2 * len(layers))
     stack = []
     for w, router in layers:
         stack.append((bd.bind(bd.moe_route_topk, w, router, ids, tw, ws),
@@ -643,7 +683,7 @@ def main():
                       bd.bind(bd.moe_combine_fixed_order, o, tw, y)))
     marks = [((j // 2) % len(layers), j % 2 == 1,
               (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-             for j in range(args.steps)]
+             for j in range(n_eager)]
     frozen.zero_()
     for j, (mli, with_gu, (a, b)) in enumerate(marks):
         for li, (route, gate_up, down, combine) in enumerate(stack):
@@ -676,12 +716,12 @@ def main():
 
     result = {
         "metric": "denoising-step MoE+sampler latency (ms) and achieved HBM GB/s vs peak, 1 GPU",
-        "value": round(value, 2),
+        "value": _round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": _round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -692,14 +732,18 @@ def main():
                          f"{T}, d_model {d}, expert ffn {f}, {E} experts top-{k}, W4A16 asym "
                          f"g64, Zipf(1.2) routing) + sampler fp32 [{P}, {V}] T=1 bound 2.0 + "
                          f"loop update; blocks of {STEPS} steps from a random canvas, each "
-                         f"block one captured graph with the done gate"),
+                         + ("block's launches issued eagerly (--no-graph) with the done gate"
+                            if args.no_graph else
+                            "block one captured graph with the done gate")),
             "steps_per_block": STEPS,
             "block_steps_run": steps_run,
             "stability_threshold": LOOP_STABILITY,
-            "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
-            "step_ms_p10_p50_p90_over_blocks": [round(float(np.percentile(per_step, q)), 4)
-                                                for q in (10, 50, 90)],
-            "step_algorithmic_bytes": int(step_bytes),
+            "hbm_frac_of_peak": None if value is None else round(value / HBM_PEAK_GBS, 4),
+            "step_ms_p10_p50_p90_over_blocks": (
+                None if per_step is None else
+                [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)]),
+            "step_algorithmic_bytes": None if step_bytes is None else int(step_bytes),
+            **({"eager_only": True} if args.eager_only else {}),
             **({"components": parts} if parts is not None else {}),
         },
         "roofline": {
@@ -711,11 +755,12 @@ def main():
             "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "avg_launch_us": round(gu_us, 2),
+            "intervals_each_way": n_eager // 2,
             "alg_bytes_per_launch": int(gu_alg),
             "read_ceiling": read_ceiling(gu_gbs),
         },
     }
-    result["config"]["frac_of_read_ceiling"] = round(
+    result["config"]["frac_of_read_ceiling"] = None if value is None else round(
         value / result["roofline"]["read_ceiling"]["GB/s"], 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

@@ -53,33 +53,37 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const u32x4_t* __res
     __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// Streaming read: XOR of every 32-bit word, one 16-byte load per thread per iteration over a
-// grid-stride sweep.  Each block folds its threads (wave shuffles, then LDS) and writes one
-// partial to part[blockIdx.x]; a one-block pass folds the partials into part[-1].  No two
-// blocks write the same word, so the read is not serialised behind same-address atomics.
-constexpr int kReadBlocks = 2048;
+// Streaming read: XOR of every 32-bit word, one nontemporal 16-byte load per thread per
+// iteration over a grid-stride sweep by 1024 blocks of 512 threads (the fastest of the
+// thread/block/unroll shapes tried for plain and nontemporal loads).  Each block folds its
+// threads (wave shuffles, then LDS) and writes one partial to part[blockIdx.x]; a one-block
+// pass folds the partials into part[-1].  No two blocks write the same word, so the read is
+// not serialised behind same-address atomics.
+constexpr int kReadBlocks = 1024;
+constexpr int kReadThreads = 512;
 
+template <int THREADS>
 __device__ __forceinline__ uint32_t block_xor(uint32_t v) {
-  __shared__ uint32_t w[kCopyThreads / 64];
+  __shared__ uint32_t w[THREADS / 64];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v ^= (uint32_t)__shfl_xor((int)v, off, 64);
   if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = v;
   __syncthreads();
   v = 0;
 #pragma unroll
-  for (int i = 0; i < kCopyThreads / 64; ++i) v ^= w[i];
+  for (int i = 0; i < THREADS / 64; ++i) v ^= w[i];
   return v;
 }
 
-__global__ __launch_bounds__(kCopyThreads) void read_kernel(const u32x4_t* __restrict__ src, size_t n,
+__global__ __launch_bounds__(kReadThreads) void read_kernel(const u32x4_t* __restrict__ src, size_t n,
                                                             uint32_t* __restrict__ part) {
-  const size_t stride = (size_t)gridDim.x * kCopyThreads;
+  const size_t stride = (size_t)gridDim.x * kReadThreads;
   uint32_t acc = 0;
-  for (size_t i = (size_t)blockIdx.x * kCopyThreads + threadIdx.x; i < n; i += stride) {
-    const u32x4_t v = src[i];
+  for (size_t i = (size_t)blockIdx.x * kReadThreads + threadIdx.x; i < n; i += stride) {
+    const u32x4_t v = __builtin_nontemporal_load(src + i);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
-  acc = block_xor(acc);
+  acc = block_xor<kReadThreads>(acc);
   if (threadIdx.x == 0) part[blockIdx.x] = acc;
 }
 
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(kCopyThreads) void read_finish_kernel(uint32_t* __r
                                                                    int nparts) {
   uint32_t acc = 0;
   for (int i = threadIdx.x; i < nparts; i += kCopyThreads) acc ^= out[1 + i];
-  acc = block_xor(acc);
+  acc = block_xor<kCopyThreads>(acc);
   if (threadIdx.x == 0) out[0] = acc;
 }
 
@@ -114,10 +118,10 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t str
 
 hipError_t launch_read(const void* src, size_t bytes, uint32_t* checksum, hipStream_t stream) {
   const size_t n = bytes / 16;
-  size_t blocks = (n + kCopyThreads - 1) / kCopyThreads;
+  size_t blocks = (n + kReadThreads - 1) / kReadThreads;
   if (blocks > kReadBlocks) blocks = kReadBlocks;
   if (blocks > 0)
-    hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream,
+    hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(kReadThreads), 0, stream,
                        reinterpret_cast<const u32x4_t*>(src), n, checksum + 1);
   hipLaunchKernelGGL(read_finish_kernel, dim3(1), dim3(kCopyThreads), 0, stream, checksum,
                      (int)blocks);

@@ -505,8 +505,9 @@ int bd_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
  * both device memory): checksum points to BD_HBM_READ_WORDS uint32 words; word 0 receives
  * the XOR of all 32-bit words of src (0 for bytes == 0) and the others are scratch.  The read
  * cannot be optimised away and can be checked on the host.  The achievable read-only
- * bandwidth beside the copy figure.  Two launches on `stream` (read, then a one-block fold of
- * the per-block partials); the caller owns both buffers.  src may be NULL when bytes == 0.
+ * bandwidth beside the copy figure: nontemporal 16-byte loads, the form the weight and logits
+ * streams use.  Two launches on `stream` (read, then a one-block fold of the per-block
+ * partials); the caller owns both buffers.  src may be NULL when bytes == 0.
  */
 #define BD_HBM_READ_WORDS 2049
 int bd_hbm_read(const void* src, size_t bytes, uint32_t* checksum, hipStream_t stream);
