@@ -671,9 +671,11 @@ def main():
     # (j // 2) mod L when j is odd and the routing launch alone of the same layer when j is
     # even.  A timing event leaves the GPU idle for several microseconds around the launches
     # next to it (the trace shows no gap between unmarked launches), the same in both
-    # brackets, so the mean of the odd intervals minus the mean of the even ones is the
+    # brackets, so the median of the odd intervals minus the median of the even ones is the
     # gate/up launch as it runs inside the step.  The pass runs at least 2 L steps, so every
-    # layer is bracketed both ways whatever --steps is.
+    # layer is bracketed both ways whatever --steps is, after one unmarked step (the first
+    # interval after the switch from graph replays to eager launches carries a start-up delay
+    # of tens of microseconds, which the medians would also reject).
     n_eager = max(args.steps + args.steps % 2, 2 * len(layers))
     stack = []
     for w, router in layers:
@@ -685,6 +687,11 @@ def main():
               (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
              for j in range(n_eager)]
     frozen.zero_()
+    for route, gate_up, down, combine in stack:   # one unmarked step first
+        route()
+        gate_up()
+        down()
+        combine()
     for j, (mli, with_gu, (a, b)) in enumerate(marks):
         for li, (route, gate_up, down, combine) in enumerate(stack):
             here = li == mli
@@ -704,7 +711,7 @@ def main():
 
     with_gu = [a.elapsed_time(b) for _, g, (a, b) in marks if g]
     route_only = [a.elapsed_time(b) for _, g, (a, b) in marks if not g]
-    gu_us = (float(np.mean(with_gu)) - float(np.mean(route_only))) * 1e3
+    gu_us = (float(np.median(with_gu)) - float(np.median(route_only))) * 1e3
     gu_alg = float(np.mean([touched[li] * gu_bytes + T * d * 2 + T * k * f * 2
                             for li, g, _ in marks if g]))
     gu_gbs = gu_alg / (gu_us * 1e-6) / 1e9

@@ -260,12 +260,22 @@ __device__ __forceinline__ PartState stream_chunks(const float* __restrict__ row
   int bC = 0;
   int nb = 0;
   Top2 top = top2_empty();
+  // Noise of the chunk lane b will hold in the current batch, drawn ahead of the chunk
+  // (its counter depends only on the chunk id), so the draw at a batch's end is one add.
+  double bG = 0.0;
+  int batch0 = c_begin + wave;                  // first chunk of the current batch
+  auto noise = [&]() {
+    const int c = batch0 + lane * WAVES;
+    if (MODE != 0 && c < c_end) {
+      const Philox4 r = philox4x32_10((uint32_t)c, (uint32_t)p, step, 1u, k0, k1);
+      bG = gumbel_from_word(r.w[0]);
+    }
+  };
   auto draw = [&]() {
     double key = -INFINITY;
     int kc = 0x7fffffff;
     if (lane < nb && bL != -INFINITY) {
-      const Philox4 r = philox4x32_10((uint32_t)bC, (uint32_t)p, step, 1u, k0, k1);
-      key = (double)bL + gumbel_from_word(r.w[0]);
+      key = (double)bL + bG;
       kc = bC;
     }
     double ka = key;
@@ -277,6 +287,8 @@ __device__ __forceinline__ PartState stream_chunks(const float* __restrict__ row
     top2_insert(top, ka, ca);
     top2_insert(top, kb, cb);
     nb = 0;
+    batch0 += kWave * WAVES;
+    noise();
   };
   auto fold = [&](float L, int c) {
     if (MODE == 0) return;
@@ -301,6 +313,7 @@ __device__ __forceinline__ PartState stream_chunks(const float* __restrict__ row
 #pragma unroll
   for (int r = 0; r < kRing; ++r)
     if (c0 + r * WAVES < c_end) load_chunk(row, V, c0 + r * WAVES, vec, x[r]);
+  if (MODE != 0) noise();
   for (int base = c0; base < c_end; base += kRing * WAVES) {
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
@@ -450,6 +463,19 @@ __device__ double chunk_key64(const float* __restrict__ row, int V, int c, doubl
 // again in fp64 (the definition) and the fp64 argmax decides.
 constexpr int kFinishThreads = 256;
 
+// Entries v0 .. v0 + 3 of a row (v0 % 4 == 0), -inf past V.
+__device__ __forceinline__ void load4(const float* __restrict__ row, int V, int v0,
+                                      float (&x)[4]) {
+  if ((V & 3) == 0 && v0 + 3 < V) {
+    const float4_t v = *reinterpret_cast<const float4_t*>(row + v0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = v[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = v0 + q < V ? row[v0 + q] : -INFINITY;
+  }
+}
+
 __device__ __forceinline__ void finish_row(const float* __restrict__ logits, int V, int p,
                                            const PartState* st, int nst, float temperature,
                                            uint32_t k0, uint32_t k1, uint32_t step,
@@ -470,6 +496,7 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ logits, int
   const int wave = tid / kWave;
   const bool sampled = temperature != 0.f;
   const float* row = logits + (size_t)p * V;
+  const int nC = (V + kChunk - 1) / kChunk;
   if (tid == 0) {
     PartState acc = st[0];
     for (int s = 1; s < nst; ++s) merge_state(acc, st[s]);
@@ -501,7 +528,6 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ logits, int
     if (tid == 0) tokens_out[p] = -1;   // valid row without a comparable chunk key
     return;
   }
-  const int nC = (V + kChunk - 1) / kChunk;
   int bestc = sChunk;
   if (sRescore) {
     // Level 1: the chunks whose fp32 key may still be the fp64 best.
@@ -544,8 +570,7 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ logits, int
   Philox4 r = {};
   float lmax = -INFINITY;
   if (v0 < vend) {
-#pragma unroll
-    for (int q = 0; q < EPT; ++q) xv[q] = v0 + q < vend ? row[v0 + q] : -INFINITY;
+    load4(row, V, v0, xv);
     r = philox4x32_10((uint32_t)(v0 >> 2), (uint32_t)p, step, 0u, k0, k1);
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
@@ -601,7 +626,12 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
   if (gated_off(gate)) return;
   const int p = blockIdx.x;
   const int tid = threadIdx.x;
-  if (frozen != nullptr && frozen[p]) {
+  // The frozen flag and the split states are read together (one memory round trip); a
+  // frozen row's states were not written by the streaming pass and are not used.
+  const bool is_frozen = frozen != nullptr && frozen[p] != 0;
+  __shared__ PartState sp[kMaxSplits];
+  for (int s = tid; s < S; s += kFinishThreads) sp[s] = part[(size_t)p * S + s];
+  if (is_frozen) {
     if (tid == 0) {
       tokens_out[p] = -1;
       if (entropy_out != nullptr) entropy_out[p] = INFINITY;
@@ -609,8 +639,6 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     }
     return;
   }
-  __shared__ PartState sp[kMaxSplits];
-  for (int s = tid; s < S; s += kFinishThreads) sp[s] = part[(size_t)p * S + s];
   __syncthreads();
   finish_row(logits, V, p, sp, S, temperature, k0, k1, step, tokens_out,
                              entropy_out, conf_out);
