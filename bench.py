@@ -21,11 +21,14 @@ Two more workloads time the parts on their own configurations (--workload):
   layer    one MoE FFN layer (route, gate/up, down, combine) at the 256-token canvas with uniform
            N(0, 1) router logits (every expert touched), two independently seeded layers in turn;
   sampler  the sampler step alone over fp32 logits [256, 262144] (every row unfrozen), two copies
-           of the logits in turn.
-Each reports the same fields; its roofline covers its dominant launch.
+           of the logits in turn;
+  chain    the stack's loop with the layers chained on the device: per layer RMS norm, router
+           projection, routing, FFN and combine, the output feeding the next layer (routing
+           from the router itself, not given logits).
+Each reports the same fields; its roofline covers its dominant launch (the chain: the step).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--workload stack|layer|sampler] [--no-components] [--no-graph]
+                       [--workload stack|layer|sampler|chain] [--no-components] [--no-graph]
                        [--eager-only]
 """
 
@@ -50,9 +53,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=48)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--layers", type=int, default=None, help="MoE layers per step (default 30)")
-    ap.add_argument("--workload", choices=("stack", "layer", "sampler"), default="stack",
+    ap.add_argument("--workload", choices=("stack", "layer", "sampler", "chain"), default="stack",
                     help="stack (default): the whole denoising step; layer: one FFN layer at the "
-                         "256-token canvas with uniform routing; sampler: the sampler alone")
+                         "256-token canvas with uniform routing; sampler: the sampler alone; "
+                         "chain: the denoising step with the layers chained through the RMS norm "
+                         "and the router projection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true",
                     help="skip the one-launch-at-a-time part timings (e.g. for counter runs)")
@@ -506,6 +511,138 @@ def main_sampler(args):
     print(json.dumps(rec), flush=True)
 
 
+def main_chain(args):
+    """The denoising loop with the layers chained on the device: in every step, layer l takes
+    the RMS norm of the running hidden state, projects it onto the router, routes it (top-k
+    and bucketing), runs the W4A16 FFN and combines; the combined output is layer l + 1's
+    hidden state.  Then the sampler step and the loop update, as in the stack; a block of 48
+    steps is one captured graph whose launches carry the done gate.  The routing is the
+    router's own (data-dependent) instead of given Zipf(1.2) logits."""
+    import torch
+    from block_diffusion_lm_router_amd import _binding as bd, workloads
+    torch.cuda.set_device(0)
+    shape = workloads.STACK_LAYER
+    n_layers = args.layers or workloads.STACK_LAYERS
+    sshape = workloads.SAMPLER
+    T, d, f, E, k = shape.tokens, shape.d_model, shape.d_ff, shape.experts, shape.top_k
+    P, V = sshape.positions, sshape.vocab
+    gu_bytes, dn_bytes = workloads.expert_bytes(shape)
+    log(f"generating {n_layers} chained layers")
+    h0_np, _, _ = workloads.make_norm_router(shape)
+    layers = []
+    for l in range(n_layers):
+        _, wn_np, wr_np = workloads.make_norm_router(shape, l)
+        layers.append((bd.MoeWeights.from_numpy(workloads.make_weights(shape, l), k, prepare=True,
+                                                drop_raw=True),
+                       torch.from_numpy(wn_np).cuda(), torch.from_numpy(wr_np).cuda()))
+    logits = torch.from_numpy(workloads.make_logits(sshape)).cuda()
+    h0 = torch.from_numpy(h0_np).cuda()
+    hs = [torch.empty((T, d), dtype=torch.float16, device="cuda") for _ in range(2)]
+    xn = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    rl = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    o = torch.empty((T, k, d), dtype=torch.float32, device="cuda")
+    ws = bd.moe_workspace(T, layers[0][0])
+    sws = bd.sample_workspace(P, V)
+    frozen = torch.zeros(P, dtype=torch.uint8, device="cuda")
+    canvas = torch.zeros(P, dtype=torch.int32, device="cuda")
+    prev = torch.empty(P, dtype=torch.int32, device="cuda")
+    tok = torch.empty(P, dtype=torch.int32, device="cuda")
+    H = torch.empty(P, dtype=torch.float32, device="cuda")
+    acc = torch.empty(P, dtype=torch.uint8, device="cuda")
+    state = torch.zeros(4, dtype=torch.int32, device="cuda")
+    STEPS = workloads.STACK_STEPS
+    n_acc = torch.zeros(STEPS, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def layer_chain(gate):
+        h = h0
+        for l, (w, wn, wr) in enumerate(layers):
+            out = hs[l % 2]
+            bd.moe_rmsnorm(h, wn, xn, loop_state=gate)
+            bd.moe_router_logits(xn, wr, rl, loop_state=gate)
+            bd.moe_w4a16_ffn(w, xn, rl, ids, tw, o, ws, loop_state=gate)
+            bd.moe_combine_fixed_order(o, tw, out, loop_state=gate)
+            h = out
+
+    # Experts each layer touches (the routing is the same in every step: every step starts
+    # from the same hidden state), from one eager pass of the chain.
+    touched = []
+    h = h0
+    for l, (w, wn, wr) in enumerate(layers):
+        bd.moe_rmsnorm(h, wn, xn)
+        bd.moe_router_logits(xn, wr, rl)
+        bd.moe_w4a16_ffn(w, xn, rl, ids, tw, o, ws)
+        bd.moe_combine_fixed_order(o, tw, hs[l % 2])
+        touched.append(int(torch.unique(ids).numel()))
+        h = hs[l % 2]
+    torch.cuda.synchronize()
+
+    def capture(n_steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            bd.diffusion_canvas_init(canvas, prev, frozen, state, V, sshape.seed, 0)
+            for s in range(n_steps):
+                layer_chain(state)
+                bd.diffusion_sample_step(logits, sshape.temperature, sshape.bound, sshape.seed, s,
+                                         frozen, canvas, tok, H, acc, n_acc[s:s + 1], sws,
+                                         loop_state=state)
+                bd.diffusion_loop_update(tok, canvas, prev, frozen, state, LOOP_STABILITY, STEPS)
+        return g
+
+    log(f"capturing the chained block graph ({STEPS} steps, {n_layers} layers each)")
+    graphs = {STEPS: capture(STEPS)}
+    for n in {args.steps % STEPS, args.warmup % STEPS} - {0}:
+        graphs[n] = capture(n)
+
+    def run_steps(n):
+        for _ in range(n // STEPS):
+            graphs[STEPS].replay()
+        if n % STEPS:
+            graphs[n % STEPS].replay()
+
+    run_steps(max(args.warmup, 1))
+    torch.cuda.synchronize()
+    log(f"warmup done; timing {args.steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    run_steps(args.steps)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    counts = n_acc.cpu().numpy()
+    steps_run = int(state.cpu().numpy()[0])
+    unfrozen = np.array([P - int(counts[:s].sum()) for s in range(STEPS)], dtype=np.float64)
+    live = np.arange(STEPS) < steps_run
+    # Per layer: the FFN's bytes as in the stack, plus the norm (h in, normed rows out, the
+    # weight) and the router projection (normed rows, router matrix, logits out).
+    layer_bytes = sum(t * (gu_bytes + dn_bytes) for t in touched) + n_layers * (
+        2 * T * d * 2 + T * E * 4 + 2 * T * k * 4) + n_layers * (
+        2 * T * d * 2 + d * 2 + T * d * 2 + E * d * 2 + T * E * 4)
+    step_bytes_blk = np.where(live, layer_bytes + unfrozen * V * 4 + P * 4 * 4, 0.0)
+    timed_steps = [i % STEPS for i in range((args.steps // STEPS) * STEPS)] + list(
+        range(args.steps % STEPS))
+    step_bytes = float(np.mean(step_bytes_blk[timed_steps]))
+    value = step_bytes / (ms * 1e-3) / 1e9
+    rec = base_record(
+        args, value, ms,
+        (f"chain: the denoising loop, each step {n_layers} chained MoE layers (canvas {T}, "
+         f"d_model {d}, expert ffn {f}, {E} experts top-{k}, W4A16 asym g64; per layer RMS "
+         f"norm, router projection, routing, FFN, combine, the output feeding the next layer) "
+         f"+ sampler fp32 [{P}, {V}] T=1 bound 2.0 + loop update; blocks of {STEPS} steps, "
+         f"each one captured graph with the done gate"),
+        {"steps_per_block": STEPS, "block_steps_run": steps_run,
+         "experts_touched_min_max": [min(touched), max(touched)],
+         "step_algorithmic_bytes": int(step_bytes)})
+    rec["roofline"] = {"kernel": "whole step (every launch of the chained step)", "bound": "hbm",
+                       "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+                       "avg_launch_us": round(ms * 1e3, 2), "alg_bytes_per_launch": int(step_bytes),
+                       "read_ceiling": read_ceiling(value)}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -520,6 +657,8 @@ def main():
         return main_layer(args)
     if args.workload == "sampler":
         return main_sampler(args)
+    if args.workload == "chain":
+        return main_chain(args)
     import torch
     from block_diffusion_lm_router_amd import _binding as bd, workloads
 

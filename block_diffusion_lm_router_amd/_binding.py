@@ -67,7 +67,9 @@ SIGNATURES = {
     "moe_combine_fixed_order": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "moe_combine_fixed_order_gated": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "moe_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P, _P]),
+    "moe_rmsnorm_gated": (_I, [_P, _P, _I, _I, _F, _P, _P, _P]),
     "moe_router_logits": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "moe_router_logits_gated": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "bd_sample_workspace_size": (_SZ, [_I, _I]),
     "diffusion_sample_entropy": (_I, [_P, _I, _I, _F, _U64, _U32, _P, _P, _P, _P, _SZ, _P]),
     "diffusion_accept_entropy_bound": (_I, [_P, _P, _I, _F, _P, _P, _P, _P, _P]),
@@ -337,22 +339,28 @@ def moe_combine_fixed_order(expert_out, topk_weights, y, loop_state=None):
     return _invoke("moe_combine_fixed_order", *args, _stream())
 
 
-def moe_rmsnorm(h, weight, y, eps=1e-6):
+def moe_rmsnorm(h, weight, y, eps=1e-6, loop_state=None):
     T, d = h.shape
     if weight.numel() != d or tuple(y.shape) != (T, d):
         raise ValueError("moe_rmsnorm: weight must be [d] and y [T, d]")
-    return _invoke("moe_rmsnorm", _ptr(h, torch.float16, "h"), _ptr(weight, torch.float16, "weight"),
-                   T, d, float(eps), _ptr(y, torch.float16, "y"), _stream())
+    args = (_ptr(h, torch.float16, "h"), _ptr(weight, torch.float16, "weight"), T, d, float(eps),
+            _ptr(y, torch.float16, "y"))
+    if loop_state is not None:
+        return _invoke("moe_rmsnorm_gated", *args, _gate(loop_state, "moe_rmsnorm"), _stream())
+    return _invoke("moe_rmsnorm", *args, _stream())
 
 
-def moe_router_logits(x, w_router, logits):
+def moe_router_logits(x, w_router, logits, loop_state=None):
     T, d = x.shape
     E = w_router.shape[0]
     if w_router.shape[1] != d or tuple(logits.shape) != (T, E):
         raise ValueError("moe_router_logits: w_router must be [E, d] and logits [T, E]")
-    return _invoke("moe_router_logits", _ptr(x, torch.float16, "x"),
-                   _ptr(w_router, torch.float16, "w_router"), T, d, E,
-                   _ptr(logits, torch.float32, "logits"), _stream())
+    args = (_ptr(x, torch.float16, "x"), _ptr(w_router, torch.float16, "w_router"), T, d, E,
+            _ptr(logits, torch.float32, "logits"))
+    if loop_state is not None:
+        return _invoke("moe_router_logits_gated", *args, _gate(loop_state, "moe_router_logits"),
+                       _stream())
+    return _invoke("moe_router_logits", *args, _stream())
 
 
 def sample_workspace_size(P, V):

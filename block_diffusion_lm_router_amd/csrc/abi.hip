@@ -245,24 +245,48 @@ int moe_combine_fixed_order_gated(const float* expert_out, const float* topk_wei
   return combine_call(expert_out, topk_weights, T, k, d, y, loop_state, stream);
 }
 
-int moe_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps, uint16_t* y,
-                hipStream_t stream) {
+static int rmsnorm_call(const uint16_t* h, const uint16_t* weight, int T, int d, float eps,
+                        uint16_t* y, const int32_t* gate, hipStream_t stream) {
   if (T < 1 || T > BD_MAX_TOKENS || d < 8 || d > BD_MAX_FEATURES || d % 8 != 0 ||
       !isfinite(eps) || eps < 0.f)
     return BD_ERR_SHAPE;
   if (!h || !weight || !y) return BD_ERR_NULL;
   if (!aligned16(h) || !aligned16(weight) || !aligned16(y)) return BD_ERR_ALIGN;
-  return to_status(bd::launch_rmsnorm(h, weight, T, d, eps, y, stream));
+  return to_status(bd::launch_rmsnorm(h, weight, T, d, eps, y, stream, gate));
 }
 
-int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
-                      float* logits, hipStream_t stream) {
+int moe_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps, uint16_t* y,
+                hipStream_t stream) {
+  return rmsnorm_call(h, weight, T, d, eps, y, nullptr, stream);
+}
+
+int moe_rmsnorm_gated(const uint16_t* h, const uint16_t* weight, int T, int d, float eps,
+                      uint16_t* y, const int32_t* loop_state, hipStream_t stream) {
+  if (!loop_state) return BD_ERR_NULL;
+  if (!aligned4(loop_state)) return BD_ERR_ALIGN;
+  return rmsnorm_call(h, weight, T, d, eps, y, loop_state, stream);
+}
+
+static int router_call(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                       float* logits, const int32_t* gate, hipStream_t stream) {
   if (T < 1 || T > BD_MAX_TOKENS || E < 1 || E > BD_MAX_EXPERTS || d < 128 ||
       d > BD_MAX_FEATURES || d % 128 != 0)
     return BD_ERR_SHAPE;
   if (!x || !w_router || !logits) return BD_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_router) || !aligned4(logits)) return BD_ERR_ALIGN;
-  return to_status(bd::launch_router(x, w_router, T, d, E, logits, stream));
+  return to_status(bd::launch_router(x, w_router, T, d, E, logits, stream, gate));
+}
+
+int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                      float* logits, hipStream_t stream) {
+  return router_call(x, w_router, T, d, E, logits, nullptr, stream);
+}
+
+int moe_router_logits_gated(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                            float* logits, const int32_t* loop_state, hipStream_t stream) {
+  if (!loop_state) return BD_ERR_NULL;
+  if (!aligned4(loop_state)) return BD_ERR_ALIGN;
+  return router_call(x, w_router, T, d, E, logits, loop_state, stream);
 }
 
 size_t bd_sample_workspace_size(int P, int V) {

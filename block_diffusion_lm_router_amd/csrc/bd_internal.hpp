@@ -81,9 +81,9 @@ hipError_t launch_combine(const float* expert_out, const float* topk_weights, in
 
 // RMS norm of fp16 rows (one wave per row) and the router projection (MFMA, split-K).
 hipError_t launch_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps,
-                          uint16_t* y, hipStream_t stream);
+                          uint16_t* y, hipStream_t stream, const int32_t* gate = nullptr);
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
-                         float* logits, hipStream_t stream);
+                         float* logits, hipStream_t stream, const int32_t* gate = nullptr);
 
 // ---------------------------------------------------------------- sampler
 int sample_split_count(int P, int V);

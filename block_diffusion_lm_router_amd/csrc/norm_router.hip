@@ -37,7 +37,8 @@ __device__ __forceinline__ u32x4_t as_u32x4(half8_t v) { return __builtin_bit_ca
 
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w, int T, int d, float eps,
-    uint16_t* __restrict__ y) {
+    uint16_t* __restrict__ y, const int32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   const int row = blockIdx.x * kNormRows + (int)(threadIdx.x / kWave);
   if (row >= T) return;  // wave-uniform
   const int lane = lane_id();
@@ -82,7 +83,8 @@ constexpr int kRouterWaves = kRouterThreads / kWave;  // contraction quarters
 
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int E, int d,
-    float* __restrict__ logits) {
+    float* __restrict__ logits, const int32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   __shared__ float4_t part[kRouterWaves][kWave];
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -127,18 +129,18 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 }  // namespace
 
 hipError_t launch_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps,
-                          uint16_t* y, hipStream_t stream) {
+                          uint16_t* y, hipStream_t stream, const int32_t* gate) {
   const int blocks = (T + kNormRows - 1) / kNormRows;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(blocks), dim3(kNormThreads), 0, stream, h, weight, T,
-                     d, eps, y);
+                     d, eps, y, gate);
   return hipGetLastError();
 }
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
-                         float* logits, hipStream_t stream) {
+                         float* logits, hipStream_t stream, const int32_t* gate) {
   const dim3 grid((T + 15) / 16, (E + 15) / 16);
   hipLaunchKernelGGL(router_kernel, grid, dim3(kRouterThreads), 0, stream, x, w_router, T, E, d,
-                     logits);
+                     logits, gate);
   return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 10
+#define BD_ABI_VERSION 11
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -300,6 +300,19 @@ int moe_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float e
  */
 int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
                       float* logits, hipStream_t stream);
+
+/*
+ * moe_rmsnorm and moe_router_logits gated like moe_w4a16_ffn_gated: the kernel reads
+ * loop_state[2] (done) when it starts and writes nothing once it is set, so that a captured
+ * graph of a whole block can chain the layers (norm -> router -> FFN -> combine -> next
+ * layer) and do no work after the block has ended.  loop_state: int32 [4], device, 4-byte
+ * aligned, the state diffusion_loop_update keeps (NULL -> BD_ERR_NULL).  Otherwise the
+ * arguments, checks and results are those of the plain entry points.
+ */
+int moe_rmsnorm_gated(const uint16_t* h, const uint16_t* weight, int T, int d, float eps,
+                      uint16_t* y, const int32_t* loop_state, hipStream_t stream);
+int moe_router_logits_gated(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                            float* logits, const int32_t* loop_state, hipStream_t stream);
 
 /* ------------------------------------------------------------------ sampler */
 

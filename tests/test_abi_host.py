@@ -297,3 +297,13 @@ def test_gated_entry_points_validate_the_gate(lib):
     conf = lib.diffusion_sample_step_confidence_gated
     assert conf(P, 64, 4096, 1.0, 0.9, 0, 0, None, None, P, P, P, P, P, n, None, None) == 1
     assert conf(P, 64, 4096, 1.0, 1.5, 0, 0, None, None, P, P, P, P, P, n, P, None) == 2
+    norm = lib.moe_rmsnorm_gated
+    assert norm(P, P, 256, 2816, ctypes.c_float(1e-6), P, None, None) == 1
+    assert norm(P, P, 256, 2816, ctypes.c_float(1e-6), P, odd, None) == 3
+    assert norm(P, P, 256, 2817, ctypes.c_float(1e-6), P, P, None) == 2
+    assert norm(P, P, 256, 2816, ctypes.c_float(-1.0), P, P, None) == 2
+    router = lib.moe_router_logits_gated
+    assert router(P, P, 256, 2816, 128, P, None, None) == 1
+    assert router(P, P, 256, 2816, 128, P, odd, None) == 3
+    assert router(P, P, 256, 2880, 128, P, P, None) == 2
+    assert router(None, P, 256, 2816, 128, P, P, None) == 1

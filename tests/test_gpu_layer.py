@@ -136,3 +136,88 @@ def test_repeat_runs_bit_identical(bd):
         b = run(bd, h, wn, wr)
         assert np.array_equal(a[0].view(np.uint16), b[0].view(np.uint16))
         assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_gated_norm_and_router(bd):
+    """The gated forms: with the driver's done flag clear they write exactly what the plain
+    forms write; with it set they write nothing."""
+    import torch
+    shape = workloads.LAYER
+    h_np, wn_np, wr_np = workloads.make_norm_router(shape)
+    T, d, E = shape.tokens, shape.d_model, shape.experts
+    h = torch.from_numpy(h_np).cuda()
+    wn = torch.from_numpy(wn_np).cuda()
+    wr = torch.from_numpy(wr_np).cuda()
+    y0 = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    l0 = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    bd.moe_rmsnorm(h, wn, y0)
+    bd.moe_router_logits(y0, wr, l0)
+    state = torch.zeros(4, dtype=torch.int32, device="cuda")
+    y1 = torch.full((T, d), 7.0, dtype=torch.float16, device="cuda")
+    l1 = torch.full((T, E), 7.0, dtype=torch.float32, device="cuda")
+    say("gated norm+router: running")
+    bd.moe_rmsnorm(h, wn, y1, loop_state=state)
+    bd.moe_router_logits(y1, wr, l1, loop_state=state)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l0.view(torch.int32))
+    state[2] = 1
+    y2 = torch.full((T, d), 7.0, dtype=torch.float16, device="cuda")
+    l2 = torch.full((T, E), 7.0, dtype=torch.float32, device="cuda")
+    say("gated norm+router: done")
+    bd.moe_rmsnorm(h, wn, y2, loop_state=state)
+    bd.moe_router_logits(y0, wr, l2, loop_state=state)
+    torch.cuda.synchronize()
+    assert bool((y2 == 7.0).all()) and bool((l2 == 7.0).all())
+
+
+@pytest.mark.parametrize("which,n_layers", [("tiny", 3), ("layer", 2)])
+def test_chained_layers(bd, which, n_layers):
+    """Layers chained on the device as the chain workload runs them: RMS norm, router
+    projection, the one-call FFN (routing, gate/up, down) and the combine, whose output is the
+    next layer's input.  Every stage is checked against the oracle fed that stage's GPU inputs
+    (a routing decision taken from slightly different upstream values would otherwise be
+    compared with a different one): the norm and router bars above, top-k ids bit-exact,
+    expert outputs and combined outputs to the FFN bars."""
+    import torch
+    from test_gpu_moe import Layer, check_layer
+    shape = {"tiny": workloads.TINY_LAYER, "layer": workloads.LAYER}[which]
+    T, d, f, E, k = shape.tokens, shape.d_model, shape.d_ff, shape.experts, shape.top_k
+    h0, _, _ = workloads.make_norm_router(shape)
+    weights, norms, routers = [], [], []
+    for l in range(n_layers):
+        w_np = workloads.make_weights(shape, l)
+        _, wn, wr = workloads.make_norm_router(shape, l)
+        weights.append((w_np, bd.MoeWeights.from_numpy(w_np, k, prepare=True)))
+        norms.append(torch.from_numpy(wn).cuda())
+        routers.append(torch.from_numpy(wr).cuda())
+    ws = bd.moe_workspace(T, weights[0][1])
+    h = [torch.from_numpy(h0).cuda()] + [torch.empty((T, d), dtype=torch.float16, device="cuda")
+                                          for _ in range(n_layers)]
+    xs, lgs, got = [], [], []
+    say("chained layers", which, n_layers)
+    for l in range(n_layers):
+        x = torch.empty((T, d), dtype=torch.float16, device="cuda")
+        lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        o = torch.full((T, k, d), float("nan"), dtype=torch.float32, device="cuda")
+        bd.moe_rmsnorm(h[l], norms[l], x)
+        bd.moe_router_logits(x, routers[l], lg)
+        bd.moe_w4a16_ffn(weights[l][1], x, lg, ids, tw, o, ws)
+        bd.moe_combine_fixed_order(o, tw, h[l + 1])
+        xs.append(x)
+        lgs.append(lg)
+        got.append((ids, tw, o))
+    torch.cuda.synchronize()
+    for l in range(n_layers):
+        h_l = h[l].cpu().numpy()
+        x_l = xs[l].cpu().numpy()
+        lg_l = lgs[l].cpu().numpy()
+        check_norm(x_l, h_l, norms[l].cpu().numpy())
+        check_router(lg_l, x_l, routers[l].cpu().numpy())
+        layer = Layer(bd, shape, x=x_l, logits=lg_l, weights=weights[l][0], layer=l)
+        ids, tw, o = got[l]
+        check_layer(layer, (ids.cpu().numpy(), tw.cpu().numpy(), o.cpu().numpy(),
+                            h[l + 1].cpu().numpy()))
+        assert np.isfinite(h[l + 1].cpu().numpy().astype(np.float32)).all()
