@@ -29,6 +29,7 @@ Each reports the same fields; its roofline covers its dominant launch (the chain
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload stack|layer|sampler|chain] [--no-components] [--no-graph]
+                       [--checkpoint-format]
                        [--eager-only]
 """
 
@@ -59,6 +60,9 @@ def parse():
                          "chain: the denoising step with the layers chained through the RMS norm "
                          "and the router projection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--checkpoint-format", action="store_true",
+                    help="layer workload: gate/up grouped at 128 and down at 64, the format of "
+                         "the model card's checkpoint")
     ap.add_argument("--no-components", action="store_true",
                     help="skip the one-launch-at-a-time part timings (e.g. for counter runs)")
     ap.add_argument("--eager-only", action="store_true",
@@ -392,14 +396,16 @@ def main_layer(args):
     torch.cuda.set_device(0)
     shape = workloads.LAYER
     T, d, f, E, k = shape.tokens, shape.d_model, shape.d_ff, shape.experts, shape.top_k
-    gu_b, dn_b = workloads.expert_bytes(shape)
+    # --checkpoint-format: gate/up grouped at 128, down at 64 (the model card's checkpoint)
+    groups = dict(gate_up_group=128, down_group=64) if args.checkpoint_format else {}
+    gu_b, dn_b = workloads.expert_bytes(shape, **groups)
     x_np = workloads.make_activations(shape)
     r_np = workloads.make_router_logits(shape)
     x, router = torch.from_numpy(x_np).cuda(), torch.from_numpy(r_np).cuda()
-    w0_np = workloads.make_weights(shape, 0)
+    w0_np = workloads.make_weights(shape, 0, **groups)
     layers = [bd.MoeWeights.from_numpy(w0_np, k, prepare=True, drop_raw=True),
-              bd.MoeWeights.from_numpy(workloads.make_weights(shape, 1), k, prepare=True,
-                                       drop_raw=True)]
+              bd.MoeWeights.from_numpy(workloads.make_weights(shape, 1, **groups), k,
+                                       prepare=True, drop_raw=True)]
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
     o = torch.empty((T, k, d), dtype=torch.float32, device="cuda")
@@ -427,8 +433,11 @@ def main_layer(args):
     gu_gbs = gu_alg / (gu_us * 1e-6) / 1e9
     rec = base_record(args, value, ms,
                       f"layer: one MoE FFN layer (canvas {T}, d_model {d}, expert ffn {f}, {E} experts "
-                      f"top-{k}, W4A16 asym g64, uniform N(0,1) router logits), route + gate/up + "
-                      f"down + combine", {"experts_touched": touched, "step_algorithmic_bytes": int(alg)})
+                      f"top-{k}, W4A16 asym "
+                      + ("gate/up g128 down g64 (checkpoint format)" if args.checkpoint_format
+                         else "g64")
+                      + f", uniform N(0,1) router logits), route + gate/up + down + combine",
+                      {"experts_touched": touched, "step_algorithmic_bytes": int(alg)})
     rec["roofline"] = {"kernel": "moe_w4a16_gate_up (w4a16_packed_kernel<true, 22, false>)", "bound": "hbm",
                        "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
@@ -442,7 +451,7 @@ def main_layer(args):
         secs = 0.0
         with threadpool_limits(limits=threads):
             for l in range(BASELINE_LAYERS):
-                w_np = w0_np if l == 0 else workloads.make_weights(shape, l)
+                w_np = w0_np if l == 0 else workloads.make_weights(shape, l, **groups)
                 t0 = time.perf_counter()
                 omoe.moe_ffn(x_np, r_np, w_np, k)
                 secs += time.perf_counter() - t0

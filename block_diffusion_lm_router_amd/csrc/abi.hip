@@ -102,7 +102,9 @@ const char* bd_status_string(int status) {
 
 size_t bd_moe_packed_size(const bd_moe_weights* w, int matrix) {
   if (check_moe_shape(w, 1) != BD_OK || (matrix != 0 && matrix != 1)) return 0;
-  return bd::pk_bytes(matrix == 0, w->num_experts, w->d_model, w->d_ff);
+  const bool gated = matrix == 0;
+  return bd::pk_bytes(gated, w->num_experts, w->d_model, w->d_ff,
+                      bd::pk_compact(gated, gated ? w->group_size : down_group(w)));
 }
 
 int moe_w4a16_prepare(const bd_moe_weights* w, uint8_t* gate_up_packed, uint8_t* down_packed,

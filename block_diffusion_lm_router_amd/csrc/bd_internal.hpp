@@ -66,7 +66,9 @@ struct W4A16Matrix {
 };
 
 int pk_tiles(bool gated, int d_model, int d_ff);
-size_t pk_bytes(bool gated, int E, int d_model, int d_ff);
+// The gate/up stream of a matrix grouped at 128 holds one (scale, zero) pair per row and stage.
+bool pk_compact(bool gated, int group);
+size_t pk_bytes(bool gated, int E, int d_model, int d_ff, bool compact);
 hipError_t launch_pack(const W4A16Matrix& m, bool gated, int E, int d_model, int d_ff,
                        uint8_t* out, hipStream_t stream);
 

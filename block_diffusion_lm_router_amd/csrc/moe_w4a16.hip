@@ -117,6 +117,7 @@ struct GemmArgs {
   int A;                   // assignments T * top_k of this call
   int max_items;           // capacity of the work list
   const int32_t* gate;     // loop driver state or NULL (see gated_off)
+  int sz_compact;          // packed stream with one (scale, zero) pair per row and stage
 };
 
 // Work item `item` of the list: (expert, first bucket position, tokens), every value clamped
@@ -488,6 +489,11 @@ constexpr int kPkWBytes = kPkRows * kWRowBytes;                 // 16 KB of nibb
 constexpr int kPkSZBytes = kPkRows * 8;                         // 2 KB of scales/zero-points
 constexpr int kPkStage = kPkWBytes + kPkSZBytes;                // 18 KB
 constexpr int kPkChunks = kPkStage / 16;
+// A gate/up matrix grouped at 128 has one group per stage, so its stage holds one (scale,
+// zero) pair per row: 1 KB instead of 2 KB (see pack_kernel).
+constexpr int kPkSZBytesC = kPkRows * 4;
+constexpr int kPkStageC = kPkWBytes + kPkSZBytesC;              // 17 KB
+constexpr int kPkChunksC = kPkStageC / 16;
 constexpr int kPkDepth = 3;                                     // stages in registers ahead
 constexpr int kPkXSlot = kItemTokens * kXRowBytes;              // 8 KB
 static_assert(kSG == 2 && kItemTokens == 32 && kXRowBytes == 256, "packed stage geometry");
@@ -575,12 +581,22 @@ __device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return __builtin_bit_cast(u32x4_t,
                             __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
 }
+template <int AUX>
+__device__ __forceinline__ u32x2_t bload64(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                           uint32_t soff) {
+  return __builtin_bit_cast(u32x2_t,
+                            __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, AUX));
+}
+// Both halves of a word set to its low (high) half: (s, z) of a 128-group becomes the
+// (s, s) and (z, z) pairs of its two 64-groups.
+__device__ __forceinline__ uint32_t dup_lo(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x01000100u); }
+__device__ __forceinline__ uint32_t dup_hi(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x03020302u); }
 
 struct PkStage {
   u32x4_t wa, wb, sz, x;
 };
 
-template <bool GATED, int NMT, int NSC, bool AFF, bool NT>
+template <bool GATED, int NMT, int NSC, bool AFF, bool NT, bool CSZ>
 __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e, int pos0,
                                             int mcount, int tile) {
   const int tid = threadIdx.x;
@@ -596,11 +612,12 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
   const bool valid = GATED ? wave * 16 < rows_here : wave * 32 < rows_here;
   const int lw = valid ? wave : wave - 4;              // whose stream this wave loads
   // The (expert, tile) stream: one descriptor, the lane's offsets within a stage.
-  const uint32_t stream_bytes = (uint32_t)NS * kPkStage;
+  constexpr int kStage = CSZ ? kPkStageC : kPkStage;
+  const uint32_t stream_bytes = (uint32_t)NS * kStage;
   const __amdgpu_buffer_rsrc_t wrs =
       make_rsrc(a.pk + ((size_t)e * a.tiles + tile) * stream_bytes, stream_bytes);
   const uint32_t wa_off = ((lw * 2 + 0) * 64 + lane) * 16;
-  const uint32_t sz_off = kPkWBytes + (lw * 16 + n) * 16;
+  const uint32_t sz_off = kPkWBytes + (lw * 16 + n) * (CSZ ? 8 : 16);
 
   // Activation share: thread tid loads the 16-byte chunk tid % 16 of row (tid / 16) mod
   // 16*NMT of the stage; with NMT = 1 the upper 256 threads repeat the lower ones' loads and
@@ -626,12 +643,17 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
   constexpr int kAux = NT ? 2 : 0;
 
   auto load = [&](int c) {
-    const uint32_t st = (uint32_t)min(c, NS - 1) * kPkStage;
+    const uint32_t st = (uint32_t)min(c, NS - 1) * kStage;
     PkStage r;
     r.x = bload<0>(xrs, x_off, (uint32_t)min(c, NS - 1) * kStageK * 2);
     r.wa = bload<kAux>(wrs, wa_off, st);
     r.wb = bload<kAux>(wrs, wa_off + 1024, st);
-    r.sz = bload<kAux>(wrs, sz_off, st);
+    if constexpr (CSZ) {
+      const u32x2_t v = bload64<kAux>(wrs, sz_off, st);
+      r.sz = u32x4_t{v[0], v[1], 0u, 0u};
+    } else {
+      r.sz = bload<kAux>(wrs, sz_off, st);
+    }
     return r;
   };
   auto put_x = [&](const PkStage& r, int slot) {
@@ -647,8 +669,10 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
   auto compute = [&](const PkStage& r, int c, int slot) {
     const char* xt = lds + slot * kPkXSlot;
     // [scale g0, scale g1, zero g0, zero g1] of the lane's row in set A, then set B
-    const half4_t szA = __builtin_bit_cast(half4_t, u32x2_t{r.sz[0], r.sz[1]});
-    const half4_t szB = __builtin_bit_cast(half4_t, u32x2_t{r.sz[2], r.sz[3]});
+    const half4_t szA = CSZ ? __builtin_bit_cast(half4_t, u32x2_t{dup_lo(r.sz[0]), dup_hi(r.sz[0])})
+                            : __builtin_bit_cast(half4_t, u32x2_t{r.sz[0], r.sz[1]});
+    const half4_t szB = CSZ ? __builtin_bit_cast(half4_t, u32x2_t{dup_lo(r.sz[1]), dup_hi(r.sz[1])})
+                            : __builtin_bit_cast(half4_t, u32x2_t{r.sz[2], r.sz[3]});
     const ZeroPairs zpA = zero_pairs(szA), zpB = zero_pairs(szB);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -716,6 +740,24 @@ __device__ __forceinline__ void packed_item(const GemmArgs& a, char* lds, int e,
   }
 }
 
+// The item's path: two 16-token tiles above 16 tokens, nontemporal weight loads when this
+// block reads the expert's stream alone, the compact scale/zero layout of 128-groups.
+template <bool GATED, int NSC, bool AFF, bool CSZ>
+__device__ __forceinline__ void packed_dispatch(const GemmArgs& a, char* lds, int e, int pos0,
+                                                int mcount, int tile, bool alone) {
+  if (mcount > 16) {
+    if (alone)
+      packed_item<GATED, 2, NSC, AFF, true, CSZ>(a, lds, e, pos0, mcount, tile);
+    else
+      packed_item<GATED, 2, NSC, AFF, false, CSZ>(a, lds, e, pos0, mcount, tile);
+  } else {
+    if (alone)
+      packed_item<GATED, 1, NSC, AFF, true, CSZ>(a, lds, e, pos0, mcount, tile);
+    else
+      packed_item<GATED, 1, NSC, AFF, false, CSZ>(a, lds, e, pos0, mcount, tile);
+  }
+}
+
 // NSC > 0: compiled for exactly NSC stages (the caller checks); 0: any number of stages.
 template <bool GATED, int NSC, bool AFF>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
@@ -739,16 +781,10 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_packed_kernel(GemmArgs a) {
   // other items' blocks on the same XCD read the stream from L2.
   const bool alone = (item == 0 || a.items[1 + 3 * (item - 1)] != a.items[1 + 3 * item]) &&
                      (item + 1 >= n_items || a.items[1 + 3 * (item + 1)] != a.items[1 + 3 * item]);
-  if (mcount > 16) {
-    if (alone)
-      packed_item<GATED, 2, NSC, AFF, true>(a, lds, e, pos0, mcount, tile);
-    else
-      packed_item<GATED, 2, NSC, AFF, false>(a, lds, e, pos0, mcount, tile);
+  if (GATED && a.sz_compact) {
+    if constexpr (GATED) packed_dispatch<GATED, NSC, AFF, true>(a, lds, e, pos0, mcount, tile, alone);
   } else {
-    if (alone)
-      packed_item<GATED, 1, NSC, AFF, true>(a, lds, e, pos0, mcount, tile);
-    else
-      packed_item<GATED, 1, NSC, AFF, false>(a, lds, e, pos0, mcount, tile);
+    packed_dispatch<GATED, NSC, AFF, false>(a, lds, e, pos0, mcount, tile, alone);
   }
 }
 
@@ -955,12 +991,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ q
                                                    const uint16_t* __restrict__ scale,
                                                    const uint16_t* __restrict__ zero, int R, int K,
                                                    int tiles, int gated, int d_ff, int gshift,
-                                                   size_t chunks, u32x4_t* __restrict__ out) {
+                                                   int compact, size_t chunks,
+                                                   u32x4_t* __restrict__ out) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= chunks) return;
   const int G = K / 64, NS = (G + 1) / 2;
-  const int ch = (int)(i % kPkChunks);
-  const size_t qs = i / kPkChunks;
+  const int stage_chunks = compact ? kPkChunksC : kPkChunks;
+  const int ch = (int)(i % stage_chunks);
+  const size_t qs = i / stage_chunks;
   const int s = (int)(qs % NS);
   const int tile = (int)((qs / NS) % tiles);
   const size_t e = qs / ((size_t)NS * tiles);
@@ -991,6 +1029,22 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ q
         v[3] = src[(g1 * 32 + kbl * 8) / 4 + 1];
       }
     }
+  } else if (compact) {
+    // One group of 128 per stage (group s): chunk idx holds, for (w, n) = 2 idx and
+    // 2 idx + 1 in turn, scale | zero << 16 of tile row R(w, 0, n), then of R(w, 1, n).
+    const int idx = ch - kPkWBytes / 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int wn = 2 * idx + h;
+      const int w = wn / 16, nn = wn & 15;
+#pragma unroll
+      for (int set = 0; set < 2; ++set) {
+        const int row = mrow(tile_row(w, set, nn));
+        if (row < 0) continue;
+        const size_t at = ((size_t)e * R + row) * (G >> 1) + s;
+        v[2 * h + set] = (uint32_t)scale[at] | ((uint32_t)zero[at] << 16);
+      }
+    }
   } else {
     const int idx = ch - kPkWBytes / 16;
     const int w = idx / 16, nn = idx & 15;
@@ -1012,24 +1066,28 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ q
 
 }  // namespace
 
+bool pk_compact(bool gated, int group) { return gated && group == 128; }
+
 int pk_tiles(bool gated, int d_model, int d_ff) {
   return gated ? (d_ff + 127) / 128 : (d_model + kPkRows - 1) / kPkRows;
 }
 
-size_t pk_bytes(bool gated, int E, int d_model, int d_ff) {
+size_t pk_bytes(bool gated, int E, int d_model, int d_ff, bool compact) {
   const int K = gated ? d_model : d_ff;
   const int NS = (K / 64 + 1) / 2;
-  return (size_t)E * pk_tiles(gated, d_model, d_ff) * NS * kPkStage;
+  return (size_t)E * pk_tiles(gated, d_model, d_ff) * NS * (compact ? kPkStageC : kPkStage);
 }
 
 hipError_t launch_pack(const W4A16Matrix& m, bool gated, int E, int d_model, int d_ff,
                        uint8_t* out, hipStream_t stream) {
   const int K = gated ? d_model : d_ff;
   const int R = gated ? 2 * d_ff : d_model;
-  const size_t chunks = pk_bytes(gated, E, d_model, d_ff) / 16;
+  const bool compact = pk_compact(gated, m.group);
+  const size_t chunks = pk_bytes(gated, E, d_model, d_ff, compact) / 16;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
                      m.q, m.scale, m.zero, R, K, pk_tiles(gated, d_model, d_ff), gated ? 1 : 0,
-                     d_ff, m.group == 128 ? 1 : 0, chunks, reinterpret_cast<u32x4_t*>(out));
+                     d_ff, m.group == 128 ? 1 : 0, compact ? 1 : 0, chunks,
+                     reinterpret_cast<u32x4_t*>(out));
   return hipGetLastError();
 }
 
@@ -1050,6 +1108,7 @@ hipError_t launch_gate_up(const W4A16Matrix& gu, int E, int d_model, int d_ff, i
   a.items = ws.items;
   a.pk = gu.pk;
   a.affine = gu.affine;
+  a.sz_compact = gu.pk != nullptr && pk_compact(true, gu.group) ? 1 : 0;
   a.h_out = ws.h;
   a.o_out = nullptr;
   a.out_ld = d_ff;
@@ -1089,6 +1148,7 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
   a.items = ws.items;
   a.pk = dn.pk;
   a.affine = dn.affine;
+  a.sz_compact = 0;
   a.h_out = nullptr;
   a.o_out = expert_out;
   a.out_ld = d_model;

@@ -190,9 +190,11 @@ def make_logits(shape: SamplerShape, seed: int = None):
     return x
 
 
-def expert_bytes(shape: LayerShape):
-    """Packed bytes of one expert: nibbles plus fp16 scale and zero of both matrices."""
-    d, f, g = shape.d_model, shape.d_ff, shape.group
-    gate_up = 2 * f * (d // 2) + 2 * (2 * f * (d // g) * 2)
-    down = d * (f // 2) + 2 * (d * (f // g) * 2)
+def expert_bytes(shape: LayerShape, gate_up_group: int = None, down_group: int = None):
+    """Packed bytes of one expert: nibbles plus fp16 scale and zero of both matrices (at the
+    shape's group size, or the given per-matrix group sizes)."""
+    d, f = shape.d_model, shape.d_ff
+    gg, gd = gate_up_group or shape.group, down_group or shape.group
+    gate_up = 2 * f * (d // 2) + 2 * (2 * f * (d // gg) * 2)
+    down = d * (f // 2) + 2 * (d * (f // gd) * 2)
     return gate_up, down

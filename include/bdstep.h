@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 11
+#define BD_ABI_VERSION 12
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -87,10 +87,11 @@ typedef enum {
  * rounded to the nearest integer first.
  * Supported: d_model % 128 == 0, d_ff % 64 == 0, d_model and d_ff <= 4096; g and gd each 64
  * or 128 and dividing that matrix's contraction dim (d_model for gate/up, d_ff for down).
- * A group of 128 is used through the packed stream only (moe_w4a16_prepare spreads its
- * scale and zero-point over the stream's two 64-group slots); a GEMM over raw arrays with a
- * group of 128 returns BD_ERR_UNSUPPORTED.  The model card's checkpoint format
- * ("requirements") is g = 128, gd = 64.
+ * A group of 128 is used through the packed stream only (moe_w4a16_prepare keeps one scale
+ * and zero-point per 128-group in the gate/up stream and spreads them over the two 64-group
+ * slots of the down stream); a GEMM over raw arrays with a group of 128 returns
+ * BD_ERR_UNSUPPORTED.  The model card's checkpoint format ("requirements") is g = 128,
+ * gd = 64.
  *
  * format BD_FORMAT_AFFINE: the *_zero arrays hold a free fp16 bias b per group and the weight
  * is w = q * scale + b (the MLX-style affine 4-bit form, named on the TensorFold XPU page).
@@ -155,6 +156,10 @@ size_t bd_moe_packed_size(const bd_moe_weights* w, int matrix);
  *   bytes 16384..18431: for w = 0..7, n = 0..15, at 16384 + (16w + n) * 16: the fp16 values
  *     scale[2s], scale[2s+1], zero[2s], zero[2s+1] of tile row R(w, 0, n), then the same four
  *     of tile row R(w, 1, n).
+ * The gate/up stream of a matrix grouped at 128 (g = 128) has stages of 17408 bytes instead:
+ * the same 16384 bytes of nibbles, then for w = 0..7, n = 0..15, at 16384 + (16w + n) * 8,
+ * scale and zero of the stage's 128-group (group s) of tile row R(w, 0, n), then of tile row
+ * R(w, 1, n).  bd_moe_packed_size accounts for it.
  * Store the results in gate_up_packed and down_packed of the weights struct for the GEMM
  * entry points to use them.
  */

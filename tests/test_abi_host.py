@@ -240,9 +240,10 @@ def test_prepare_sizes_and_validation(lib):
     assert lib.moe_w4a16_prepare(ctypes.byref(bad), p, p, None) == 5   # BD_ERR_UNSUPPORTED
     bad = _weights(g=128)                                              # down at 128: 704 % 128
     assert lib.moe_w4a16_prepare(ctypes.byref(bad), p, p, None) == 2   # BD_ERR_SHAPE
-    # the checkpoint format (gate/up 128, down 64) packs into the same stream sizes
+    # the checkpoint format (gate/up 128, down 64): the gate/up stream keeps one scale and
+    # zero-point per 128-group (17,408-byte stages), the down stream is the 64-group one
     ck = _weights(g=128, gd=64)
-    assert lib.bd_moe_packed_size(ctypes.byref(ck), 0) == 128 * 6 * 22 * 18432
+    assert lib.bd_moe_packed_size(ctypes.byref(ck), 0) == 128 * 6 * 22 * 17408
     assert lib.bd_moe_packed_size(ctypes.byref(ck), 1) == 128 * 11 * 6 * 18432
     # a 128-group over raw arrays is refused by the GEMMs; with the packed stream it is not
     ws = ctypes.c_void_p(0x10000)

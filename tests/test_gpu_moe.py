@@ -397,9 +397,13 @@ def test_widest_routing(bd, prepared):
 # ---------------------------------------------------------------- checkpoint format groups
 
 
-def test_group128_packs_to_the_same_stream_as_duplicated_group64(bd):
-    """Repacking 128-groups gives the stream of the same weights written as 64-groups whose
-    pairs share a scale and zero-point (byte for byte), so the GEMMs need no other path."""
+def test_group128_packed_streams(bd):
+    """Repacking 128-groups.  Down: the stream of the same weights written as 64-groups whose
+    pairs share a scale and zero-point, byte for byte.  Gate/up: the compact stream, whose
+    17,408-byte stages hold the same 16 KB of nibbles and then, for (w, n) = 0..127, the
+    (scale, zero) of tile row R(w, 0, n) and of R(w, 1, n), i.e. the duplicated stream with
+    each 128-group's scale and zero-point kept once."""
+    import torch
     shape = workloads.LayerShape(8, 512, 256, 3, 2)
     w128 = workloads.make_weights(shape, 3, gate_up_group=128, down_group=128)
     w64 = dict(w128)
@@ -409,10 +413,17 @@ def test_group128_packs_to_the_same_stream_as_duplicated_group64(bd):
     a = bd.MoeWeights.from_numpy(w128, 2, prepare=True)
     b = bd.MoeWeights.from_numpy(w64, 2, prepare=True)
     assert (a.group_size, a.down_group_size, b.group_size) == (128, 128, 64)
-    import torch
     torch.cuda.synchronize()
-    for pa, pb in zip(a.packed, b.packed):
-        assert torch.equal(pa, pb)
+    assert torch.equal(a.packed[1], b.packed[1])
+    dup = b.packed[0].cpu().numpy().reshape(-1, 18432)
+    got = a.packed[0].cpu().numpy()
+    assert got.size == dup.shape[0] * 17408
+    got = got.reshape(-1, 17408)
+    assert np.array_equal(got[:, :16384], dup[:, :16384])
+    sz = dup[:, 16384:].view(np.uint16).reshape(-1, 128, 8)     # (w, n): A s0 s1 z0 z1, B ...
+    want = sz[:, :, [0, 2, 4, 6]]                                # A s z, B s z
+    assert np.array_equal(got[:, 16384:].view(np.uint16).reshape(-1, 128, 4), want)
+    assert np.array_equal(sz[:, :, [1, 3, 5, 7]], want)          # the duplicates it drops
 
 
 @pytest.mark.parametrize("which", ["tiny", "layer"])
