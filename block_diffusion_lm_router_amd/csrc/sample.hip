@@ -395,19 +395,23 @@ __device__ __forceinline__ void block_argmax(double& key, int& idx, double* wkey
 
 // Standard Gumbel draw from one Philox word in fp32, for the level-2 pre-selection only.
 // u = ((r >> 8) + 0.5) 2^-24; w = -ln u is formed without cancellation: from u itself when
-// u < 1/2 (exact in fp32), else as -log1p(-(1 - u)) with 1 - u = (2^24 - 1 - (r >> 8) + 0.5)
-// 2^-24 (exact in fp32).  g = -ln w.  With logf and log1pf within 2 ulp, |g - g_exact| is
-// below 2^-21 + 2^-22, and w >= 2^-25 never reaches the fp32 subnormals.
+// u < 1/2 (exact in fp32), else as -log1p(-v) with v = 1 - u = (2^24 - 1 - (r >> 8) + 0.5)
+// 2^-24 (exact in fp32), by Goldberg's correction log1p(x) = ln(1 + x) x / ((1 + x) - 1)
+// (y = 1 + x rounded, y - 1 exact; x itself when y rounds to 1).  g = -ln w.  The logarithms
+// are the hardware log2 (v_log_f32, within a few ulp for these normal inputs) times ln 2,
+// so |g - g_exact| stays below 1e-5 (|log2| <= 25, w >= 2^-25); the pre-selection margin
+// (2e-4 + 2e-6 |max|) is twenty times that, and the published decision is the fp64 one.
 __device__ __forceinline__ float gumbel32_from_word(uint32_t r) {
   const uint32_t k = r >> 8;
   float w;
   if (k < (1u << 23)) {
-    w = -logf(((float)k + 0.5f) * 0x1p-24f);
+    w = -__builtin_amdgcn_logf(((float)k + 0.5f) * 0x1p-24f) * kLn2;
   } else {
-    const uint32_t m = (1u << 24) - 1u - k;
-    w = -log1pf(-(((float)m + 0.5f) * 0x1p-24f));
+    const float v = ((float)((1u << 24) - 1u - k) + 0.5f) * 0x1p-24f;
+    const float y = 1.f - v;
+    w = y == 1.f ? v : __builtin_amdgcn_logf(y) * kLn2 * v * __builtin_amdgcn_rcpf(y - 1.f);
   }
-  return -logf(w);
+  return -__builtin_amdgcn_logf(w) * kLn2;
 }
 
 // How far a level-1 key formed from fp32 chunk sums can sit from the fp64 key of the same
@@ -458,7 +462,7 @@ __device__ double chunk_key64(const float* __restrict__ row, int V, int c, doubl
 // are rescored in fp64 by chunk_key64 and the fp64 best wins; if some state's second key is
 // also within the margin, that state may hold further candidates, and every chunk of the row
 // is rescored.  Level 2 re-reads the winning chunk: its scores x_v / T + g_v are first formed
-// in fp32 (error below 1.2e-5 + 2.4e-7 |score|); when a single entry is within the margin of
+// in fp32 (error below 2e-5 + 2.4e-7 |score|); when a single entry is within the margin of
 // the fp32 maximum it is the fp64 argmax, otherwise the entries within the margin are scored
 // again in fp64 (the definition) and the fp64 argmax decides.
 constexpr int kFinishThreads = 256;
@@ -593,9 +597,17 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ logits, int
 #pragma unroll
   for (int q = 0; q < EPT; ++q)
     if (v0 + q < vend && (everything || s32[q] >= m - margin)) mask |= 1 << q;
-  const int holders = __syncthreads_count(mask != 0);
-  const int multi = __syncthreads_count(__builtin_popcount(mask) > 1);
-  if (holders == 1 && multi == 0) {
+  // Candidates in the block, one barrier: per-wave counts from ballots of each entry slot.
+  __shared__ int wcand[NW];
+  int wc = 0;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) wc += __popcll(__ballot((mask >> q) & 1));
+  if (lane_id() == 0) wcand[wave] = wc;
+  __syncthreads();
+  int cands = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) cands += wcand[w];
+  if (cands == 1) {
     if (mask != 0) tokens_out[p] = v0 + __builtin_ctz(mask);
     return;
   }
