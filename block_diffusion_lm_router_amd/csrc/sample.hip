@@ -702,15 +702,17 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
   const int tid = threadIdx.x;
   const int n = blockDim.x;
   unsigned long long key = ~0ull;  // non-candidates sort last
+  int32_t my_token = 0;            // read with the entropy: the selection takes its own position
   if (tid < P) {
     const float h = entropy[tid];
     const bool is_frozen = frozen != nullptr && frozen[tid];
+    if (canvas != nullptr) my_token = tokens[tid];
     if (!is_frozen && !(h != h)) key = ((uint64_t)float_order_key(h) << 32) | (uint32_t)tid;
     accept_out[tid] = 0;
   }
   auto take = [&](int pos) {  // run by the thread that holds position pos
     accept_out[pos] = 1;
-    if (canvas != nullptr) canvas[pos] = tokens[pos];
+    if (canvas != nullptr) canvas[pos] = pos == tid ? my_token : tokens[pos];
     if (frozen != nullptr) frozen[pos] = 1;
   };
   // Selection: the smallest remaining key, block-wide, one at a time; every thread runs the
@@ -807,11 +809,14 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_conf_kernel(
   __shared__ uint64_t wbest[kAcceptThreads / kWave];
   __shared__ int sPick;
   const int tid = threadIdx.x;
+  const int nw = (int)(blockDim.x / kWave);
   bool cand = false, pass = false;
   uint64_t key = 0;
+  int32_t my_token = 0;
   if (tid < P) {
     const float c = conf[tid];
     const bool is_frozen = frozen != nullptr && frozen[tid];
+    if (canvas != nullptr) my_token = tokens[tid];
     cand = !is_frozen && c >= 0.f;  // false for NaN
     pass = cand && c > threshold;
     if (cand) key = ((uint64_t)float_order_key(c) << 32) | (uint32_t)(0xffffffffu - (uint32_t)tid);
@@ -828,7 +833,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_conf_kernel(
     __syncthreads();
     if (tid == 0) {
       uint64_t b = 0;
-      for (int w = 0; w < kAcceptThreads / kWave; ++w) b = wbest[w] > b ? wbest[w] : b;
+      for (int w = 0; w < nw; ++w) b = wbest[w] > b ? wbest[w] : b;
       sPick = b == 0 ? -1 : (int)(0xffffffffu - (uint32_t)b);
     }
     __syncthreads();
@@ -838,7 +843,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_conf_kernel(
   if (tid < P) {
     accept_out[tid] = take ? 1 : 0;
     if (take) {
-      if (canvas != nullptr) canvas[tid] = tokens[tid];
+      if (canvas != nullptr) canvas[tid] = my_token;
       if (frozen != nullptr) frozen[tid] = 1;
     }
   }
@@ -901,7 +906,9 @@ hipError_t launch_accept_confidence(const float* conf, const int32_t* tokens, in
                                     float threshold, uint8_t* frozen, int32_t* canvas,
                                     uint8_t* accept_out, int32_t* num_accepted,
                                     hipStream_t stream, const int32_t* gate) {
-  hipLaunchKernelGGL(accept_conf_kernel, dim3(1), dim3(kAcceptThreads), 0, stream, conf, tokens,
+  int n = kWave;
+  while (n < P) n <<= 1;
+  hipLaunchKernelGGL(accept_conf_kernel, dim3(1), dim3(n), 0, stream, conf, tokens,
                      P, threshold, frozen, canvas, accept_out, num_accepted, gate);
   return hipGetLastError();
 }
