@@ -78,14 +78,15 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
   }
 }
 
-constexpr int kRouterThreads = 256;
-constexpr int kRouterWaves = kRouterThreads / kWave;  // contraction quarters
-
-__global__ __launch_bounds__(kRouterThreads) void router_kernel(
+// One 16 x 16 (token x expert) tile per block; WAVES waves split the contraction dim into
+// equal parts (8 when d % 256 == 0, else 4), each a chain of MFMA steps with its loads eight
+// steps ahead, and the parts are summed in a fixed order through LDS.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void router_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int E, int d,
     float* __restrict__ logits, const int32_t* __restrict__ gate) {
   if (gated_off(gate)) return;
-  __shared__ float4_t part[kRouterWaves][kWave];
+  __shared__ float4_t part[WAVES][kWave];
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int m = lane & 15;
@@ -95,14 +96,14 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
   // Rows past the ends are clamped onto the last row: their sums are computed and dropped.
   const int t = min(t0 + m, T - 1);
   const int e = min(e0 + m, E - 1);
-  const int kq = d / kRouterWaves;
+  const int kq = d / WAVES;
   const int steps = kq / 32;
   const half8_t* __restrict__ xa =
       reinterpret_cast<const half8_t*>(x + (size_t)t * d + wave * kq + kb * 8);
   const half8_t* __restrict__ wb =
       reinterpret_cast<const half8_t*>(wr + (size_t)e * d + wave * kq + kb * 8);
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll 8
   for (int s = 0; s < steps; ++s)
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s * 4], wb[s * 4], acc, 0, 0, 0);
   part[wave][lane] = acc;
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
   if (wave != 0) return;
   float4_t sum = part[0][lane];
 #pragma unroll
-  for (int q = 1; q < kRouterWaves; ++q) {
+  for (int q = 1; q < WAVES; ++q) {
     const float4_t p = part[q][lane];
     sum[0] += p[0];
     sum[1] += p[1];
@@ -139,8 +140,12 @@ hipError_t launch_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int 
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
                          float* logits, hipStream_t stream, const int32_t* gate) {
   const dim3 grid((T + 15) / 16, (E + 15) / 16);
-  hipLaunchKernelGGL(router_kernel, grid, dim3(kRouterThreads), 0, stream, x, w_router, T, E, d,
-                     logits, gate);
+  if (d % 256 == 0)
+    hipLaunchKernelGGL(router_kernel<8>, grid, dim3(8 * kWave), 0, stream, x, w_router, T, E, d,
+                       logits, gate);
+  else
+    hipLaunchKernelGGL(router_kernel<4>, grid, dim3(4 * kWave), 0, stream, x, w_router, T, E, d,
+                       logits, gate);
   return hipGetLastError();
 }
 
