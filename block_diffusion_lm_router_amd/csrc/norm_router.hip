@@ -14,8 +14,8 @@
 //
 // Router projection.  logits[t][e] = sum_k x[t][k] W_r[e][k] on v_mfma_f32_16x16x32_f16:
 // fp16 products are exact and accumulate in fp32.  A block owns one 16-token x 16-expert tile
-// and its four waves split the contraction dim into quarters; the quarters' 16 x 16 sums meet
-// in LDS and are added in wave order, so the result is reproducible.  Each lane streams its
+// and its eight waves (four when d % 256 != 0) split the contraction dim into equal parts; the
+// parts' 16 x 16 sums meet in LDS and are added in wave order, so the result is reproducible.  Each lane streams its
 // 16-byte fragments of x and W_r straight from memory (both stay in L2: 1.4 MB and 0.7 MB at
 // the layer's shape).  Fragment layout as in the expert GEMMs: lane (m, kb) = (lane % 16,
 // lane / 16) supplies row m at k-slots 8kb..8kb+7 of A (tokens) and of B (experts), and
