@@ -343,8 +343,8 @@ __device__ __forceinline__ PartState stream_chunks(const float* __restrict__ row
   return ws;
 }
 
-// Block (s, p) streams split s of row p with kStreamWaves waves and writes their
-// merged state (waves in order) to part[p][s].
+// Block (s, p) streams split s of row p with kStreamWaves waves; wave w writes its state to
+// part[p][s][w] (no barrier at the end of the pass: the finish merges the states in order).
 template <int MODE>
 __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
     const float* __restrict__ logits, int V, int nC, int S, float invT, uint32_t k0,
@@ -358,19 +358,41 @@ __global__ __launch_bounds__(kStreamThreads) void sample_stream_kernel(
   const int c_end = (int)((int64_t)(s + 1) * nC / S);
   const PartState ws = stream_chunks<MODE, kStreamWaves>(logits + (size_t)p * V, V, p, c_begin,
                                                          c_end, invT, k0, k1, step);
-  __shared__ PartState wstate[kStreamWaves];
-  if (lane_id() == 0) wstate[threadIdx.x / kWave] = ws;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    PartState acc = wstate[0];
-    for (int w = 1; w < kStreamWaves; ++w) merge_state(acc, wstate[w]);
-    part[(size_t)p * S + s] = acc;
-  }
+  if (lane_id() == 0) part[((size_t)p * S + s) * kStreamWaves + threadIdx.x / kWave] = ws;
 }
 
 // ---------------------------------------------------------------- finishing a row
 
-constexpr int kMaxSplits = BD_SAMPLE_BLOCKS;  // sample_split_count never exceeds this
+// The identity of merge_state: no entries, no keys.
+__device__ __forceinline__ PartState empty_state() {
+  PartState e;
+  e.m = -INFINITY;
+  e.n = e.s = e.t = 0.f;
+  e.best_v = -INFINITY;
+  e.best_i = 0x7fffffff;
+  e.nan = 0;
+  e.best_c = e.second_c = 0x7fffffff;
+  e.best_key = e.second_key = -INFINITY;
+  return e;
+}
+
+// The state held by the lane `d` above (every field).
+__device__ __forceinline__ PartState shfl_down_state(const PartState& a, int d) {
+  PartState b;
+  b.m = __shfl_down(a.m, d);
+  b.n = __shfl_down(a.n, d);
+  b.s = __shfl_down(a.s, d);
+  b.t = __shfl_down(a.t, d);
+  b.best_v = __shfl_down(a.best_v, d);
+  b.best_i = __shfl_down(a.best_i, d);
+  b.nan = __shfl_down(a.nan, d);
+  b.best_c = __shfl_down(a.best_c, d);
+  b.second_c = __shfl_down(a.second_c, d);
+  b.best_key = __shfl_down(a.best_key, d);
+  b.second_key = __shfl_down(a.second_key, d);
+  return b;
+}
+
 constexpr int kMaxCand = 64;                   // level-1 candidates rescored one by one
 
 // Block-wide argmax of (key, index) by better_key; uniform result, one barrier.
@@ -481,8 +503,9 @@ __device__ __forceinline__ void load4(const float* __restrict__ row, int V, int 
 }
 
 __device__ __forceinline__ void finish_row(const float* __restrict__ logits, int V, int p,
-                                           const PartState* st, int nst, float temperature,
-                                           uint32_t k0, uint32_t k1, uint32_t step,
+                                           const PartState* __restrict__ st, int nst,
+                                           bool is_frozen, float temperature, uint32_t k0,
+                                           uint32_t k1, uint32_t step,
                                            int32_t* __restrict__ tokens_out,
                                            float* __restrict__ entropy_out,
                                            float* __restrict__ conf_out) {
@@ -496,14 +519,40 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ logits, int
   __shared__ int sValid, sChunk, sRescore, sFallback, sCand;
   __shared__ double sLim;
   __shared__ int cand[kMaxCand];
+  __shared__ PartState wst[NW];
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
+  const int lane = lane_id();
   const bool sampled = temperature != 0.f;
   const float* row = logits + (size_t)p * V;
   const int nC = (V + kChunk - 1) / kChunk;
+  // The row's states merged in a fixed order: thread t left-folds states [t q, (t + 1) q),
+  // then pairs of neighbouring threads (lower first) within each wave, level by level, then
+  // the waves in order.  Empty states are identities, so lanes past the end need no care.
+  const int q = (nst + NT - 1) / NT;
+  const int sb = tid * q, se = min(sb + q, nst);
+  PartState acc = sb < nst ? st[sb] : empty_state();
+  if (is_frozen) {
+    if (tid == 0) {
+      tokens_out[p] = -1;
+      if (entropy_out != nullptr) entropy_out[p] = INFINITY;
+      if (conf_out != nullptr) conf_out[p] = -1.f;
+    }
+    return;
+  }
+  for (int s = sb + 1; s < se; ++s) merge_state(acc, st[s]);
+  const int active = (nst + q - 1) / q;   // threads holding states
+  for (int d = 1; d < kWave && d < active; d <<= 1) {
+    const PartState o = shfl_down_state(acc, d);
+    if ((lane & (2 * d - 1)) == 0) merge_state(acc, o);
+  }
+  if (active > kWave) {
+    if (lane == 0) wst[wave] = acc;
+    __syncthreads();
+  }
   if (tid == 0) {
-    PartState acc = st[0];
-    for (int s = 1; s < nst; ++s) merge_state(acc, st[s]);
+    if (active > kWave)
+      for (int w = 1; w < NW; ++w) merge_state(acc, wst[w]);
     float H = NAN, conf = NAN;
     bool valid = !acc.nan && acc.m != -INFINITY;
     if (valid) {
@@ -637,23 +686,12 @@ __global__ __launch_bounds__(kFinishThreads) void sample_finish_kernel(
     float* __restrict__ conf_out, const int32_t* __restrict__ gate) {
   if (gated_off(gate)) return;
   const int p = blockIdx.x;
-  const int tid = threadIdx.x;
-  // The frozen flag and the split states are read together (one memory round trip); a
+  // The frozen flag and the first split states are read together (one memory round trip); a
   // frozen row's states were not written by the streaming pass and are not used.
   const bool is_frozen = frozen != nullptr && frozen[p] != 0;
-  __shared__ PartState sp[kMaxSplits];
-  for (int s = tid; s < S; s += kFinishThreads) sp[s] = part[(size_t)p * S + s];
-  if (is_frozen) {
-    if (tid == 0) {
-      tokens_out[p] = -1;
-      if (entropy_out != nullptr) entropy_out[p] = INFINITY;
-      if (conf_out != nullptr) conf_out[p] = -1.f;
-    }
-    return;
-  }
-  __syncthreads();
-  finish_row(logits, V, p, sp, S, temperature, k0, k1, step, tokens_out,
-                             entropy_out, conf_out);
+  const int nst = S * kStreamWaves;
+  finish_row(logits, V, p, part + (size_t)p * nst, nst, is_frozen, temperature, k0, k1, step,
+             tokens_out, entropy_out, conf_out);
 }
 
 // ---------------------------------------------------------------- acceptance (one block)
@@ -889,7 +927,7 @@ hipError_t launch_sample_entropy(const float* logits, int P, int V, float temper
 
 size_t sample_workspace_bytes(int P, int V) {
   const int S = sample_split_count(P, V);
-  return align_up((size_t)P * S * sizeof(PartState));
+  return align_up((size_t)P * S * kStreamWaves * sizeof(PartState));
 }
 
 hipError_t launch_accept(const float* entropy, const int32_t* tokens, int P, float bound,
@@ -926,11 +964,12 @@ hipError_t launch_accept_confidence(const float* conf, const int32_t* tokens, in
 // that overlap on one GPU race.
 
 namespace {
-constexpr size_t kStaticScratchBytes = 128 * 1024;
+constexpr size_t kStaticScratchBytes = 512 * 1024;
 constexpr int kMaxScratchDevices = 64;
-// The largest workspace: P * S states with S = min(ceil(1024 / P), ...) gives at most
-// 1024 + P - 1 <= 2047 states, 256-byte aligned.
-static_assert(2047 * sizeof(PartState) + 256 <= kStaticScratchBytes, "static sampler scratch");
+// The largest workspace: P * S * kStreamWaves states with S = min(ceil(1024 / P), ...) gives
+// at most (1024 + P - 1) * kStreamWaves <= 2047 * 4 states, 256-byte aligned.
+static_assert(2047 * kStreamWaves * sizeof(PartState) + 256 <= kStaticScratchBytes,
+              "static sampler scratch");
 __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 std::mutex scratch_mu;
 void* scratch_ptr[kMaxScratchDevices] = {};

@@ -396,7 +396,7 @@ int diffusion_sample_step_gated(const float* logits, int P, int V, float tempera
  * diffusion_sample_step without a workspace argument, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments (less the workspace), same results bit for bit.  The streaming pass's split
- * states live in a static device array of the library (128 KiB per GPU, held until the
+ * states live in a static device array of the library (512 KiB per GPU, held until the
  * process ends; every valid P, V fits, else BD_ERR_WORKSPACE); the call allocates nothing.
  * All calls on one GPU share that array: calls that overlap on a GPU (other streams, other
  * threads) race and must not be issued; calls ordered on one stream are safe.  The first call
