@@ -14,6 +14,8 @@ namespace bd {
 namespace {
 
 constexpr int kCombineThreads = 256;
+constexpr int kUnrolledK = 8;                 // top-k with the slots' loads issued together
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ o,
                                                                   const float* __restrict__ w,
@@ -27,13 +29,30 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   const int t = (int)(i / d4);
   const int c = (int)(i % d4) * 4;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(size_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(o + ((size_t)t * k + j) * d + c);
+  auto term = [&](float wj, const float4& v) {
     a0 = fmaf(wj, v.x, a0);
     a1 = fmaf(wj, v.y, a1);
     a2 = fmaf(wj, v.z, a2);
     a3 = fmaf(wj, v.w, a3);
+  };
+  const float* wt = w + (size_t)t * k;
+  const float* ot = o + (size_t)t * k * d + c;
+  if (k == kUnrolledK) {
+    // Every slot's row read before the first product (one memory round trip, not k), then
+    // the sum in ascending j as below.
+    // The expert outputs are read once: nontemporal loads.
+    float wj[kUnrolledK];
+    float4 v[kUnrolledK];
+#pragma unroll
+    for (int j = 0; j < kUnrolledK; ++j) {
+      wj[j] = wt[j];
+      const f32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(ot + (size_t)j * d));
+      v[j] = make_float4(q[0], q[1], q[2], q[3]);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnrolledK; ++j) term(wj[j], v[j]);
+  } else {
+    for (int j = 0; j < k; ++j) term(wt[j], *reinterpret_cast<const float4*>(ot + (size_t)j * d));
   }
   const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1, h2 = (_Float16)a2, h3 = (_Float16)a3;
   uint2 out;
