@@ -206,6 +206,8 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=50):
       the 128 experts touched, most with a handful of tokens: the latency-bound case);
     * sampler_entropy_bound / sampler_confidence: one sampler step over all rows unfrozen;
     * rmsnorm / router: the layer neighbours at the same shape;
+    * combine / combine_rmsnorm: the fixed-order combine alone, and with the next layer's RMS
+      norm in the same launch (the chain workload's form);
     * canvas_init / loop_update: the denoising-loop driver's two launches at the canvas size.
     """
     import torch
@@ -300,6 +302,12 @@ def components(bd, workloads, layers, x, logits, sshape, ws, sws, n=50):
     rl = torch.empty((T, E), dtype=torch.float32, device="cuda")
     timed("rmsnorm", [bd.bind(bd.moe_rmsnorm, hh, wn, xn) for hh in hs], 2 * T * d * 2 + d * 2)
     timed("router", [bd.bind(bd.moe_router_logits, xn, wr, rl)], T * d * 2 + E * d * 2 + T * E * 4)
+    o2 = o.clone()
+    timed("combine", [bd.bind(bd.moe_combine_fixed_order, oo, tw, y) for oo in (o, o2)],
+          T * k * d * 4 + T * k * 4 + T * d * 2)
+    timed("combine_rmsnorm", [bd.bind(bd.moe_combine_rmsnorm, oo, tw, wn, y, xn) for oo in (o, o2)],
+          T * k * d * 4 + T * k * 4 + 2 * T * d * 2 + d * 2)
+    del o2
 
     prev = torch.empty(P, dtype=torch.int32, device="cuda")
     state = torch.zeros(4, dtype=torch.int32, device="cuda")
@@ -534,7 +542,8 @@ def main_chain(args):
     """The denoising loop with the layers chained on the device: in every step, layer l takes
     the RMS norm of the running hidden state, projects it onto the router, routes it (top-k
     and bucketing), runs the W4A16 FFN and combines; the combined output is layer l + 1's
-    hidden state.  Then the sampler step and the loop update, as in the stack; a block of 48
+    hidden state, and its RMS norm is taken by the same launch as the combine
+    (moe_combine_rmsnorm; layer 0 normalises the initial hidden state on its own).  Then the sampler step and the loop update, as in the stack; a block of 48
     steps is one captured graph whose launches carry the done gate.  The routing is the
     router's own (data-dependent) instead of given Zipf(1.2) logits."""
     import torch
@@ -576,26 +585,27 @@ def main_chain(args):
     stream = torch.cuda.current_stream()
 
     def layer_chain(gate):
-        h = h0
+        bd.moe_rmsnorm(h0, layers[0][1], xn, loop_state=gate)
         for l, (w, wn, wr) in enumerate(layers):
-            out = hs[l % 2]
-            bd.moe_rmsnorm(h, wn, xn, loop_state=gate)
             bd.moe_router_logits(xn, wr, rl, loop_state=gate)
             bd.moe_w4a16_ffn(w, xn, rl, ids, tw, o, ws, loop_state=gate)
-            bd.moe_combine_fixed_order(o, tw, out, loop_state=gate)
-            h = out
+            if l + 1 < len(layers):
+                bd.moe_combine_rmsnorm(o, tw, layers[l + 1][1], hs[l % 2], xn, loop_state=gate)
+            else:
+                bd.moe_combine_fixed_order(o, tw, hs[l % 2], loop_state=gate)
 
     # Experts each layer touches (the routing is the same in every step: every step starts
     # from the same hidden state), from one eager pass of the chain.
     touched = []
-    h = h0
+    bd.moe_rmsnorm(h0, layers[0][1], xn)
     for l, (w, wn, wr) in enumerate(layers):
-        bd.moe_rmsnorm(h, wn, xn)
         bd.moe_router_logits(xn, wr, rl)
         bd.moe_w4a16_ffn(w, xn, rl, ids, tw, o, ws)
-        bd.moe_combine_fixed_order(o, tw, hs[l % 2])
+        if l + 1 < len(layers):
+            bd.moe_combine_rmsnorm(o, tw, layers[l + 1][1], hs[l % 2], xn)
+        else:
+            bd.moe_combine_fixed_order(o, tw, hs[l % 2])
         touched.append(int(torch.unique(ids).numel()))
-        h = hs[l % 2]
     torch.cuda.synchronize()
 
     def capture(n_steps):
@@ -634,11 +644,12 @@ def main_chain(args):
     steps_run = int(state.cpu().numpy()[0])
     unfrozen = np.array([P - int(counts[:s].sum()) for s in range(STEPS)], dtype=np.float64)
     live = np.arange(STEPS) < steps_run
-    # Per layer: the FFN's bytes as in the stack, plus the norm (h in, normed rows out, the
-    # weight) and the router projection (normed rows, router matrix, logits out).
+    # Per layer: the FFN's bytes as in the stack, plus the norm (normed rows out and the
+    # weight; layer 0 also reads the hidden state in, later layers take it from the combine's
+    # registers) and the router projection (normed rows, router matrix, logits out).
     layer_bytes = sum(t * (gu_bytes + dn_bytes) for t in touched) + n_layers * (
-        2 * T * d * 2 + T * E * 4 + 2 * T * k * 4) + n_layers * (
-        2 * T * d * 2 + d * 2 + T * d * 2 + E * d * 2 + T * E * 4)
+        2 * T * d * 2 + T * E * 4 + 2 * T * k * 4) + T * d * 2 + n_layers * (
+        T * d * 2 + d * 2 + T * d * 2 + E * d * 2 + T * E * 4)
     step_bytes_blk = np.where(live, layer_bytes + unfrozen * V * 4 + P * 4 * 4, 0.0)
     timed_steps = [i % STEPS for i in range((args.steps // STEPS) * STEPS)] + list(
         range(args.steps % STEPS))
@@ -648,7 +659,8 @@ def main_chain(args):
         args, value, ms,
         (f"chain: the denoising loop, each step {n_layers} chained MoE layers (canvas {T}, "
          f"d_model {d}, expert ffn {f}, {E} experts top-{k}, W4A16 asym g64; per layer RMS "
-         f"norm, router projection, routing, FFN, combine, the output feeding the next layer) "
+         f"norm, router projection, routing, FFN, combine, the output feeding the next layer; "
+         f"each combine and the next layer's norm in one launch) "
          f"+ sampler fp32 [{P}, {V}] T=1 bound 2.0 + loop update; blocks of {STEPS} steps, "
          f"each one captured graph with the done gate"),
         {"steps_per_block": STEPS, "block_steps_run": steps_run,

@@ -66,6 +66,8 @@ SIGNATURES = {
     "moe_w4a16_ffn_gated": (_I, [_W, _I, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "moe_combine_fixed_order": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "moe_combine_fixed_order_gated": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+    "moe_combine_rmsnorm": (_I, [_P, _P, _I, _I, _I, _P, _F, _P, _P, _P]),
+    "moe_combine_rmsnorm_gated": (_I, [_P, _P, _I, _I, _I, _P, _F, _P, _P, _P, _P]),
     "moe_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P, _P]),
     "moe_rmsnorm_gated": (_I, [_P, _P, _I, _I, _F, _P, _P, _P]),
     "moe_router_logits": (_I, [_P, _P, _I, _I, _I, _P, _P]),
@@ -337,6 +339,26 @@ def moe_combine_fixed_order(expert_out, topk_weights, y, loop_state=None):
         return _invoke("moe_combine_fixed_order_gated", *args,
                        _gate(loop_state, "moe_combine_fixed_order"), _stream())
     return _invoke("moe_combine_fixed_order", *args, _stream())
+
+
+def moe_combine_rmsnorm(expert_out, topk_weights, weight, y, xn, eps=1e-6, loop_state=None):
+    """y = moe_combine_fixed_order(expert_out, topk_weights); xn = moe_rmsnorm(y, weight)."""
+    if expert_out.dim() != 3:
+        raise ValueError("moe_combine_rmsnorm: expert_out must be [T, k, d]")
+    T, k, d = expert_out.shape
+    _shape(topk_weights, (T, k), "topk_weights", "moe_combine_rmsnorm")
+    _shape(y, (T, d), "y", "moe_combine_rmsnorm")
+    _shape(xn, (T, d), "xn", "moe_combine_rmsnorm")
+    if weight.numel() != d:
+        raise ValueError("moe_combine_rmsnorm: weight must be [d]")
+    args = (_ptr(expert_out, torch.float32, "expert_out"),
+            _ptr(topk_weights, torch.float32, "topk_weights"), T, k, d,
+            _ptr(weight, torch.float16, "weight"), float(eps), _ptr(y, torch.float16, "y"),
+            _ptr(xn, torch.float16, "xn"))
+    if loop_state is not None:
+        return _invoke("moe_combine_rmsnorm_gated", *args,
+                       _gate(loop_state, "moe_combine_rmsnorm"), _stream())
+    return _invoke("moe_combine_rmsnorm", *args, _stream())
 
 
 def moe_rmsnorm(h, weight, y, eps=1e-6, loop_state=None):

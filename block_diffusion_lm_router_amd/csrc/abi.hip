@@ -269,6 +269,35 @@ int moe_rmsnorm_gated(const uint16_t* h, const uint16_t* weight, int T, int d, f
   return rmsnorm_call(h, weight, T, d, eps, y, loop_state, stream);
 }
 
+static int combine_norm_call(const float* expert_out, const float* topk_weights, int T, int k,
+                             int d, const uint16_t* weight, float eps, uint16_t* y, uint16_t* xn,
+                             const int32_t* gate, hipStream_t stream) {
+  if (!expert_out || !topk_weights || !weight || !y || !xn) return BD_ERR_NULL;
+  if (T < 1 || T > BD_MAX_TOKENS || k < 1 || k > BD_MAX_TOPK || d < 8 || d > BD_MAX_FEATURES ||
+      d % 8 != 0 || !isfinite(eps) || eps < 0.f)
+    return BD_ERR_SHAPE;
+  if (!aligned16(expert_out) || !aligned4(topk_weights) || !aligned16(weight) || !aligned16(y) ||
+      !aligned16(xn))
+    return BD_ERR_ALIGN;
+  return to_status(
+      bd::launch_combine_norm(expert_out, topk_weights, T, k, d, weight, eps, y, xn, stream, gate));
+}
+
+int moe_combine_rmsnorm(const float* expert_out, const float* topk_weights, int T, int k, int d,
+                        const uint16_t* weight, float eps, uint16_t* y, uint16_t* xn,
+                        hipStream_t stream) {
+  return combine_norm_call(expert_out, topk_weights, T, k, d, weight, eps, y, xn, nullptr, stream);
+}
+
+int moe_combine_rmsnorm_gated(const float* expert_out, const float* topk_weights, int T, int k,
+                              int d, const uint16_t* weight, float eps, uint16_t* y, uint16_t* xn,
+                              const int32_t* loop_state, hipStream_t stream) {
+  if (!loop_state) return BD_ERR_NULL;
+  if (!aligned4(loop_state)) return BD_ERR_ALIGN;
+  return combine_norm_call(expert_out, topk_weights, T, k, d, weight, eps, y, xn, loop_state,
+                           stream);
+}
+
 static int router_call(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
                        float* logits, const int32_t* gate, hipStream_t stream) {
   if (T < 1 || T > BD_MAX_TOKENS || E < 1 || E > BD_MAX_EXPERTS || d < 128 ||

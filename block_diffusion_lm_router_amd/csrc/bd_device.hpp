@@ -16,6 +16,15 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// The fp32 value v as such, for a conversion to fp16 that must round this fp32 value: without
+// the barrier the compiler may fuse the multiply or multiply-add that produced v into one
+// mixed-precision instruction (v_fma_mixlo_f16) that rounds the exact result to fp16 once,
+// which differs from fp32-then-fp16 rounding near ties.
+__device__ __forceinline__ float keep_f32(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // The done gate of a denoising loop: a kernel given a driver state (int32 [4]; word 2 is the
 // done flag the loop update sets) returns at once when the block is done, before touching
 // anything.  The flag was written by an earlier launch on the stream, so a plain load sees it.

@@ -80,6 +80,11 @@ hipError_t launch_down(const W4A16Matrix& dn, int E, int d_model, int d_ff, int 
                        const int32_t* gate = nullptr);
 hipError_t launch_combine(const float* expert_out, const float* topk_weights, int T, int k, int d,
                           uint16_t* y, hipStream_t stream, const int32_t* gate = nullptr);
+// The combine, then the RMS norm of its output rows with `weight` into xn (one block per row,
+// d % 8 == 0, d <= 4096); both outputs equal launch_combine followed by launch_rmsnorm.
+hipError_t launch_combine_norm(const float* expert_out, const float* topk_weights, int T, int k,
+                               int d, const uint16_t* weight, float eps, uint16_t* y, uint16_t* xn,
+                               hipStream_t stream, const int32_t* gate);
 
 // RMS norm of fp16 rows (one wave per row) and the router projection (MFMA, split-K).
 hipError_t launch_rmsnorm(const uint16_t* h, const uint16_t* weight, int T, int d, float eps,

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
       const half8_t gw = as_half8(g[i]);
       half8_t o;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) o[q] = (_Float16)(((float)x[q] * r) * (float)gw[q]);
+      for (int q = 0; q < 8; ++q) o[q] = (_Float16)keep_f32(((float)x[q] * r) * (float)gw[q]);
       dst[j] = as_u32x4(o);
     }
   }

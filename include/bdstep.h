@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 12
+#define BD_ABI_VERSION 13
 /* Entries per chunk of the two-level gumbel-max draw (see diffusion_sample_entropy). */
 #define BD_SAMPLE_CHUNK 1024
 /* Limits checked on the host. */
@@ -318,6 +318,31 @@ int moe_rmsnorm_gated(const uint16_t* h, const uint16_t* weight, int T, int d, f
                       uint16_t* y, const int32_t* loop_state, hipStream_t stream);
 int moe_router_logits_gated(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
                             float* logits, const int32_t* loop_state, hipStream_t stream);
+
+/*
+ * The combine of layer l and the RMS norm that starts layer l + 1, one launch: y is exactly
+ * moe_combine_fixed_order(expert_out, topk_weights) and xn exactly moe_rmsnorm(y, weight,
+ * eps), bit for bit, but y is not read back from memory for the norm (each row's sum of
+ * squares is taken in the norm's own order from the row the same block has just combined).
+ * Sources: axe-diffusion-ksl-xe model card, "the kernels we built" (the fixed-order combine;
+ * the RMS norm as one launch) and "what the model is" (a layer's output is the next layer's
+ * input).
+ *
+ *   expert_out, topk_weights, T, k: as moe_combine_fixed_order (k in 1..BD_MAX_TOPK)
+ *   weight  fp16 [d], the next layer's norm weight, 16-byte aligned
+ *   y       fp16 [T][d] out, the layer output, 16-byte aligned
+ *   xn      fp16 [T][d] out, the next layer's FFN and router input, 16-byte aligned
+ *   d in 8..BD_MAX_FEATURES with d % 8 == 0; eps finite, >= 0.  No output may overlap an
+ *   input or the other output.
+ */
+int moe_combine_rmsnorm(const float* expert_out, const float* topk_weights, int T, int k, int d,
+                        const uint16_t* weight, float eps, uint16_t* y, uint16_t* xn,
+                        hipStream_t stream);
+
+/* moe_combine_rmsnorm gated like moe_rmsnorm_gated (nothing written once the block is done). */
+int moe_combine_rmsnorm_gated(const float* expert_out, const float* topk_weights, int T, int k,
+                              int d, const uint16_t* weight, float eps, uint16_t* y, uint16_t* xn,
+                              const int32_t* loop_state, hipStream_t stream);
 
 /* ------------------------------------------------------------------ sampler */
 

@@ -201,6 +201,30 @@ def test_norm_router_validation(lib):
     assert rt(ctypes.c_void_p(0x1002), P, 4, 2816, 128, P, None) == 3
 
 
+def test_combine_rmsnorm_validation(lib):
+    """Every case fails a host check, so no kernel is launched on the placeholder pointers."""
+    P = ctypes.c_void_p(0x1000)
+    cn = lib.moe_combine_rmsnorm
+    assert cn(P, P, 0, 8, 2816, P, 1e-6, P, P, None) == 2
+    assert cn(P, P, 4, 0, 2816, P, 1e-6, P, P, None) == 2
+    assert cn(P, P, 4, 17, 2816, P, 1e-6, P, P, None) == 2
+    assert cn(P, P, 4, 8, 2820, P, 1e-6, P, P, None) == 2
+    assert cn(P, P, 4, 8, 4104, P, 1e-6, P, P, None) == 2
+    assert cn(P, P, 4, 8, 0, P, 1e-6, P, P, None) == 2
+    assert cn(P, P, 4, 8, 2816, P, -1.0, P, P, None) == 2
+    assert cn(P, P, 4, 8, 2816, P, float("nan"), P, P, None) == 2
+    assert cn(None, P, 4, 8, 2816, P, 1e-6, P, P, None) == 1
+    assert cn(P, P, 4, 8, 2816, None, 1e-6, P, P, None) == 1
+    assert cn(P, P, 4, 8, 2816, P, 1e-6, P, None, None) == 1
+    assert cn(ctypes.c_void_p(0x1004), P, 4, 8, 2816, P, 1e-6, P, P, None) == 3
+    assert cn(P, P, 4, 8, 2816, ctypes.c_void_p(0x1008), 1e-6, P, P, None) == 3
+    assert cn(P, P, 4, 8, 2816, P, 1e-6, P, ctypes.c_void_p(0x1008), None) == 3
+    cg = lib.moe_combine_rmsnorm_gated
+    assert cg(P, P, 4, 8, 2816, P, 1e-6, P, P, None, None) == 1
+    assert cg(P, P, 4, 8, 2816, P, 1e-6, P, P, ctypes.c_void_p(0x1002), None) == 3
+    assert cg(P, P, 0, 8, 2816, P, 1e-6, P, P, P, None) == 2
+
+
 def test_loop_driver_validation(lib):
     from oracle import loop
     for args in [(256, 64, 0, 0), (256, 64, 12, 0), (256, 64, 100, 0), (256, 64, 999, 0),

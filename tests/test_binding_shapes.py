@@ -47,6 +47,12 @@ def test_moe_wrappers_check_shapes():
     expect(bd.moe_combine_fixed_order, o, t(T, 3), t(T, 256, dtype=torch.float16))
     expect(bd.moe_combine_fixed_order, o, tw, t(T, 255, dtype=torch.float16))
     expect(bd.moe_combine_fixed_order, t(T, 256), tw, t(T, 256, dtype=torch.float16))
+    h16, wn = t(T, 256, dtype=torch.float16), t(256, dtype=torch.float16)
+    expect(bd.moe_combine_rmsnorm, o, t(T, 3), wn, h16, h16)                 # weights [T, k]
+    expect(bd.moe_combine_rmsnorm, o, tw, wn, t(T, 255, dtype=torch.float16), h16)
+    expect(bd.moe_combine_rmsnorm, o, tw, wn, h16, t(T + 1, 256, dtype=torch.float16))
+    expect(bd.moe_combine_rmsnorm, o, tw, t(255, dtype=torch.float16), h16, h16)
+    expect(bd.moe_combine_rmsnorm, t(T, 256), tw, wn, h16, h16)
 
 
 def test_moe_weights_check_array_shapes():

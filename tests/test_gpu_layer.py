@@ -175,7 +175,7 @@ def test_gated_norm_and_router(bd):
 def test_chained_layers(bd, which, n_layers):
     """Layers chained on the device as the chain workload runs them: RMS norm, router
     projection, the one-call FFN (routing, gate/up, down) and the combine, whose output is the
-    next layer's input.  Every stage is checked against the oracle fed that stage's GPU inputs
+    next layer's input (the combine and the next layer's norm in one launch).  Every stage is checked against the oracle fed that stage's GPU inputs
     (a routing decision taken from slightly different upstream values would otherwise be
     compared with a different one): the norm and router bars above, top-k ids bit-exact,
     expert outputs and combined outputs to the FFN bars."""
@@ -196,17 +196,21 @@ def test_chained_layers(bd, which, n_layers):
                                           for _ in range(n_layers)]
     xs, lgs, got = [], [], []
     say("chained layers", which, n_layers)
+    x = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    bd.moe_rmsnorm(h[0], norms[0], x)
     for l in range(n_layers):
-        x = torch.empty((T, d), dtype=torch.float16, device="cuda")
         lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
         ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
         tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
         o = torch.full((T, k, d), float("nan"), dtype=torch.float32, device="cuda")
-        bd.moe_rmsnorm(h[l], norms[l], x)
         bd.moe_router_logits(x, routers[l], lg)
         bd.moe_w4a16_ffn(weights[l][1], x, lg, ids, tw, o, ws)
-        bd.moe_combine_fixed_order(o, tw, h[l + 1])
         xs.append(x)
+        if l + 1 < n_layers:       # the combine and the next layer's norm in one launch
+            x = torch.empty((T, d), dtype=torch.float16, device="cuda")
+            bd.moe_combine_rmsnorm(o, tw, norms[l + 1], h[l + 1], x)
+        else:
+            bd.moe_combine_fixed_order(o, tw, h[l + 1])
         lgs.append(lg)
         got.append((ids, tw, o))
     torch.cuda.synchronize()
@@ -221,3 +225,69 @@ def test_chained_layers(bd, which, n_layers):
         check_layer(layer, (ids.cpu().numpy(), tw.cpu().numpy(), o.cpu().numpy(),
                             h[l + 1].cpu().numpy()))
         assert np.isfinite(h[l + 1].cpu().numpy().astype(np.float32)).all()
+
+
+def _combine_norm_inputs(T, k, d, seed):
+    rng = np.random.default_rng(seed)
+    o = (rng.standard_normal((T, k, d)) * rng.uniform(0.1, 30)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    wn = (1 + 0.2 * rng.standard_normal(d)).astype(np.float16)
+    return o, w, wn
+
+
+@pytest.mark.parametrize("T,k,d", [(256, 8, 2816), (1, 8, 8), (5, 1, 8), (7, 3, 4096),
+                                   (64, 16, 1024), (33, 8, 4088), (300, 2, 2816),
+                                   (64, 8, 4096), (3, 8, 1032)])
+def test_combine_rmsnorm_matches_combine_then_norm(bd, T, k, d):
+    """moe_combine_rmsnorm against the two launches it replaces (bit for bit, both outputs)
+    and against the oracle: y to the combine's bar (one fp16 rounding plus k fp32 roundings),
+    xn to the norm's bar from the GPU's y."""
+    import torch
+    o_np, w_np, wn_np = _combine_norm_inputs(T, k, d, T * 7 + k * 3 + d)
+    o, w, wn = (torch.from_numpy(a).cuda() for a in (o_np, w_np, wn_np))
+    y2 = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    x2 = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    bd.moe_combine_fixed_order(o, w, y2)
+    bd.moe_rmsnorm(y2, wn, x2)
+    y1 = torch.full((T, d), float("nan"), dtype=torch.float16, device="cuda")
+    x1 = torch.full((T, d), float("nan"), dtype=torch.float16, device="cuda")
+    say("combine+norm one launch", T, k, d)
+    bd.moe_combine_rmsnorm(o, w, wn, y1, x1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(x1.view(torch.int16), x2.view(torch.int16))
+    y = y1.cpu().numpy()
+    ref = omoe.combine(o_np.astype(np.float64), w_np.astype(np.float64))
+    half_ulp = 0.5 * np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    fp32_sum = 2.0 ** -24 * k * np.einsum("tj,tjd->td", np.abs(w_np.astype(np.float64)),
+                                          np.abs(o_np.astype(np.float64)))
+    assert np.all(np.abs(y.astype(np.float64) - ref) <= half_ulp * 1.0001 + fp32_sum)
+    check_norm(x1.cpu().numpy(), y, wn_np)
+
+
+def test_combine_rmsnorm_gated(bd):
+    """The gated form writes what the plain one writes while the block runs, nothing once the
+    driver state says done."""
+    import torch
+    T, k, d = 64, 8, 2816
+    o_np, w_np, wn_np = _combine_norm_inputs(T, k, d, 11)
+    o, w, wn = (torch.from_numpy(a).cuda() for a in (o_np, w_np, wn_np))
+    y0 = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    x0 = torch.empty((T, d), dtype=torch.float16, device="cuda")
+    bd.moe_combine_rmsnorm(o, w, wn, y0, x0)
+    state = torch.zeros(4, dtype=torch.int32, device="cuda")
+    y1 = torch.full((T, d), 7.0, dtype=torch.float16, device="cuda")
+    x1 = torch.full((T, d), 7.0, dtype=torch.float16, device="cuda")
+    say("gated combine+norm: running")
+    bd.moe_combine_rmsnorm(o, w, wn, y1, x1, loop_state=state)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+    assert torch.equal(x1.view(torch.int16), x0.view(torch.int16))
+    state[2] = 1
+    y2 = torch.full((T, d), 7.0, dtype=torch.float16, device="cuda")
+    x2 = torch.full((T, d), 7.0, dtype=torch.float16, device="cuda")
+    say("gated combine+norm: done")
+    bd.moe_combine_rmsnorm(o, w, wn, y2, x2, loop_state=state)
+    torch.cuda.synchronize()
+    assert bool((y2 == 7.0).all()) and bool((x2 == 7.0).all())
