@@ -1,6 +1,7 @@
 """The entry points under HIP graph capture, as the benchmark replays them.
 
-A captured MoE layer (route, gate/up, down, combine) and a captured sampler step are
+A captured MoE layer (route, gate/up, down, combine), a captured sampler step and two
+chained layers (norm, router, FFN, the combine with the next norm) are
 replayed several times, with other eager work and synchronisations between the replays;
 every replay must reproduce the eager result bit for bit (all kernels are deterministic),
 and outputs are poisoned before each replay so that a launch missing from the graph shows.
@@ -134,3 +135,62 @@ def test_sampler_step_graph_replays(bd):
         torch.cuda.synchronize()
     assert np.array_equal(b["frozen"].cpu().numpy() > 0,
                           (frozen0.cpu().numpy() > 0) | (b["acc"].cpu().numpy() > 0))
+
+
+def test_chained_layers_graph_replays(bd):
+    """Two chained layers as the chain workload captures them (gated launches: RMS norm, router
+    projection, the one-call FFN, the combine with the next layer's norm, then the last
+    combine): every replay reproduces the eager chain bit for bit."""
+    import torch
+    shape = workloads.TINY_LAYER
+    T, d, E, k = shape.tokens, shape.d_model, shape.experts, shape.top_k
+    say("graph chained layers", T, d, E, k)
+    h0_np, _, _ = workloads.make_norm_router(shape)
+    h0 = torch.from_numpy(h0_np).cuda()
+    layers = []
+    for l in range(2):
+        _, wn, wr = workloads.make_norm_router(shape, l)
+        layers.append((bd.MoeWeights.from_numpy(workloads.make_weights(shape, l), k, prepare=True),
+                       torch.from_numpy(wn).cuda(), torch.from_numpy(wr).cuda()))
+    ws = bd.moe_workspace(T, layers[0][0])
+    state = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def make():
+        return dict(xn=torch.empty((T, d), dtype=torch.float16, device="cuda"),
+                    rl=torch.empty((T, E), dtype=torch.float32, device="cuda"),
+                    ids=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+                    tw=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+                    o=torch.empty((T, k, d), dtype=torch.float32, device="cuda"),
+                    y0=torch.empty((T, d), dtype=torch.float16, device="cuda"),
+                    y1=torch.empty((T, d), dtype=torch.float16, device="cuda"))
+
+    def chain(b):
+        bd.moe_rmsnorm(h0, layers[0][1], b["xn"], loop_state=state)
+        for l, (w, wn, wr) in enumerate(layers):
+            bd.moe_router_logits(b["xn"], wr, b["rl"], loop_state=state)
+            bd.moe_w4a16_ffn(w, b["xn"], b["rl"], b["ids"], b["tw"], b["o"], ws, loop_state=state)
+            if l == 0:
+                bd.moe_combine_rmsnorm(b["o"], b["tw"], layers[1][1], b["y0"], b["xn"],
+                                       loop_state=state)
+            else:
+                bd.moe_combine_fixed_order(b["o"], b["tw"], b["y1"], loop_state=state)
+
+    eager = make()
+    chain(eager)
+    torch.cuda.synchronize()
+    b = make()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain(b)
+    other = make()
+    for r in range(REPLAYS):
+        for key, t in b.items():
+            t.fill_(-3 if t.dtype == torch.int32 else float("nan"))
+        torch.cuda.synchronize()
+        say("replay", r)
+        g.replay()
+        torch.cuda.synchronize()
+        for key in eager:
+            assert torch.equal(b[key], eager[key]), f"replay {r}: {key} differs from eager"
+        chain(other)                                 # eager work on the shared workspace
+        torch.cuda.synchronize()
