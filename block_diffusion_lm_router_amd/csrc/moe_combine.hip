@@ -1,10 +1,12 @@
-// Fixed-order weighted combine of the per-assignment expert outputs, and the plain
-// streaming copy used to calibrate HBM traffic counters.
+// Fixed-order weighted combine of the per-assignment expert outputs, the same combine
+// followed by the next layer's RMS norm in one launch, and the plain streaming copy and read
+// used to calibrate HBM traffic counters and to measure the achievable read rate.
 //
 // Source: axe-diffusion-ksl-xe model card, "the kernels we built": the weighted combine
 // is a fixed-order reduction instead of index_add_ with atomics, because a 1-ulp
-// difference can flip an acceptance threshold.  Here every output element has exactly
-// one writer, which sums its k slots in ascending j with fp32 fma and rounds once.
+// difference can flip an acceptance threshold; the RMS norm is one fused launch.  Here every
+// output element has exactly one writer, which sums its k slots in ascending j with fp32 fma
+// and rounds the fp32 sum to fp16 once.
 
 #include "bd_device.hpp"
 #include "bd_internal.hpp"
