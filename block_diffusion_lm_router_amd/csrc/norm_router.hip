@@ -10,7 +10,9 @@
 // the squares in fp32 (each square of an fp16 value is exact in fp32; lanes sum in element
 // order, then one fixed-order wave reduction), loading its share of w alongside, and writes
 //     y = fp16_rne(x * (1 / sqrt(sum / d + eps)) * w)
-// from the same registers.  HBM traffic is the row in and the row out, plus w from L2.
+// from the same registers.  HBM traffic is the row in and the row out, plus w from L2.  The
+// row moves through buffer loads and stores whose range check zero-fills (and drops) the
+// lanes past a short row, so no vector of the row needs a branch of its own.
 //
 // Router projection.  logits[t][e] = sum_k x[t][k] W_r[e][k] on v_mfma_f32_16x16x32_f16:
 // fp16 products are exact and accumulate in fp32.  A block owns one 16-token x 16-expert tile
@@ -35,6 +37,13 @@ constexpr int kNormMaxVec = 8;  // 8 vectors x 8 halves x 64 lanes = 4096 featur
 __device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
 __device__ __forceinline__ u32x4_t as_u32x4(half8_t v) { return __builtin_bit_cast(u32x4_t, v); }
 
+// Buffer loads and stores over one row: a read past the row's byte range returns zeros and a
+// write past it is dropped, so the lanes past the end of a row need no branch (a zero adds
+// nothing to the sum of squares).  Word 3 of a gfx9 descriptor: raw 32-bit data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w, int T, int d, float eps,
     uint16_t* __restrict__ y, const int32_t* __restrict__ gate) {
@@ -42,39 +51,38 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
   const int row = blockIdx.x * kNormRows + (int)(threadIdx.x / kWave);
   if (row >= T) return;  // wave-uniform
   const int lane = lane_id();
-  const int nv = d / 8;
-  const u32x4_t* __restrict__ src = reinterpret_cast<const u32x4_t*>(h + (size_t)row * d);
-  const u32x4_t* __restrict__ wv = reinterpret_cast<const u32x4_t*>(w);
+  const uint32_t bytes = (uint32_t)d * 2u;
+  const __amdgpu_buffer_rsrc_t src = row_rsrc(h + (size_t)row * d, bytes);
+  const __amdgpu_buffer_rsrc_t wsrc = row_rsrc(w, bytes);
+  const __amdgpu_buffer_rsrc_t dst = row_rsrc(y + (size_t)row * d, bytes);
   u32x4_t v[kNormMaxVec], g[kNormMaxVec];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < kNormMaxVec; ++i) {
-    const int j = lane + i * kWave;
-    if (j < nv) {
-      v[i] = __builtin_nontemporal_load(src + j);
-      g[i] = wv[j];
-      const half8_t x = as_half8(v[i]);
+    const int off = (lane + i * kWave) * 16;
+    v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(src, off, 0, 2));
+    g[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wsrc, off, 0, 0));
+  }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float f = (float)x[q];
-        ss = fmaf(f, f, ss);
-      }
+  for (int i = 0; i < kNormMaxVec; ++i) {
+    const half8_t x = as_half8(v[i]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float f = (float)x[q];
+      ss = fmaf(f, f, ss);
     }
   }
   const float total = wave_sum(ss);
   const float r = 1.f / sqrtf(total / (float)d + eps);
-  u32x4_t* __restrict__ dst = reinterpret_cast<u32x4_t*>(y + (size_t)row * d);
 #pragma unroll
   for (int i = 0; i < kNormMaxVec; ++i) {
-    const int j = lane + i * kWave;
-    if (j < nv) {
-      const half8_t x = as_half8(v[i]);
-      const half8_t gw = as_half8(g[i]);
-      half8_t o;
+    const half8_t x = as_half8(v[i]);
+    const half8_t gw = as_half8(g[i]);
+    half8_t o;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) o[q] = (_Float16)keep_f32(((float)x[q] * r) * (float)gw[q]);
-      dst[j] = as_u32x4(o);
-    }
+    for (int q = 0; q < 8; ++q) o[q] = (_Float16)keep_f32(((float)x[q] * r) * (float)gw[q]);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, as_u32x4(o)), dst,
+                                           (lane + i * kWave) * 16, 0, 0);
   }
 }
 
